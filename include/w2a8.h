@@ -1,0 +1,187 @@
+/*
+ * w2a8.h — C ABI of libw2a8.so, the MI355X (gfx950) W2A8 linear layer.
+ *
+ * The layer: ternary weights {-1, 0, 1} packed at 2 bits each, int8
+ * activations, exact int32 accumulation, and an fp32 scale epilogue.
+ *
+ * Sources (cited by page title and section):
+ *   [WIN]  "Windows 上跑通 BitNet b1.58：Flash Attention 与 CUDA sm_86 部署实录",
+ *          §3.1 "BitLinear 层的三元权重逻辑".
+ *   [CPU]  "微软BitNet：1-bit量化大模型CPU部署实践",
+ *          §2.1 "1.58-bit量化原理", §2.2 "CPU优化设计", §6.3 "模型微调".
+ *   [TEST] "如何编译 BitNet W2A8 CUDA 内核并用 test.py 运行 GEMV 加速测试？",
+ *          sections "编译 W2A8 CUDA 内核", "运行 test.py 做 GEMV 基准测试",
+ *          "如何判断结果", "限制与注意事项".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Return value: an int status, W2A8_OK (0) on success, otherwise one of
+ *   the W2A8_ERR_* codes below.  The library never prints and never aborts.
+ *   Arguments are validated on the host before any device work is enqueued;
+ *   on an error nothing is enqueued and no output is written (host
+ *   functions may have written part of their output when they return
+ *   W2A8_ERR_VALUE, see each function).
+ * - Ownership: every buffer is owned by the caller.  The library never
+ *   allocates, frees or synchronises device memory.  Device pointers are
+ *   plain device addresses (e.g. a torch tensor's data_ptr()).
+ * - Streams: `stream` is a hipStream_t passed as void*; NULL means the
+ *   legacy default stream.  Device entry points only enqueue work on that
+ *   stream and return; results are ready when the stream reaches them.
+ *   They may be recorded into a HIP graph (they enqueue kernels only, no
+ *   memset or copy).
+ * - Device: the current HIP device must be a gfx950 GPU (W2A8_ERR_ARCH
+ *   otherwise; W2A8_ERR_NODEVICE if there is none).  The library makes no
+ *   HIP call when it is loaded; the first device call queries the device.
+ * - Layouts: x is [M][K] row-major int8, y is [M][N] row-major.  N, K, M are
+ *   element counts (>= 1).  Device pointers to x, y and packed weights must
+ *   be 16-byte aligned (W2A8_ERR_ALIGN), scale pointers 4-byte aligned.
+ * - Thread safety: the library holds no mutable state besides a per-device
+ *   property cache; calls from several host threads are safe.  Two calls in
+ *   flight at once must not share a workspace.
+ */
+#ifndef W2A8_H
+#define W2A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w2a8_status {
+    W2A8_OK = 0,
+    W2A8_ERR_NULL = 1,      /* a required pointer is NULL                     */
+    W2A8_ERR_SHAPE = 2,     /* M, N or K < 1, or above the documented limits  */
+    W2A8_ERR_ALIGN = 3,     /* a pointer is not aligned as required           */
+    W2A8_ERR_VALUE = 4,     /* a weight outside {-1,0,1}, or a code 11        */
+    W2A8_ERR_BUFSIZE = 5,   /* a packed or workspace buffer is too small      */
+    W2A8_ERR_NODEVICE = 6,  /* no HIP device / device query failed            */
+    W2A8_ERR_ARCH = 7,      /* the current device is not gfx950               */
+    W2A8_ERR_LAUNCH = 8     /* the kernel launch was rejected by the runtime  */
+};
+
+/* Version of the packed weight layout below; stored packed weights are only
+ * valid for the same version. */
+#define W2A8_LAYOUT_VERSION 1
+
+/* Limits: 1 <= N <= 2^30, 1 <= K <= W2A8_MAX_K, 1 <= M <= 2^20.  The K bound
+ * keeps every int32 partial sum exact (|partial| <= 2048*K < 2^31). */
+#define W2A8_MAX_K 1048448
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *w2a8_status_str(int status);
+
+/* W2A8_LAYOUT_VERSION of the library (to check against the header). */
+int w2a8_layout_version(void);
+
+/* ------------------------------------------------------------------------
+ * Packed weight layout "T32x128", version 1.
+ *
+ * [CPU] §2.1 maps -1 -> 00, 0 -> 01, 1 -> 10 (code = w + 1; 11 never
+ * occurs) and [CPU] §2.2 stores 8 ternary weights in 2 bytes.  [TEST]
+ * "编译 W2A8 CUDA 内核" describes the reference GPU kernel's block reorder
+ * and 16-codes-per-32-bit-word interleave without giving the arrangement;
+ * this arrangement is this library's own, chosen so that one wave64 reads
+ * one 1 KiB tile with a single 16-byte load per lane:
+ *
+ *   Np = ceil(N/32)*32, Kp = ceil(K/128)*128, KT = Kp/128.
+ *   Size: Np*Kp/4 bytes (exactly N*K/4 when N%32 == 0 and K%128 == 0).
+ *   Tile (s, t) = rows 32s..32s+31, k 128t..128t+127, at byte (s*KT+t)*1024;
+ *   the tiles of a 32-row strip are contiguous, strips follow each other.
+ *   Inside a tile, lane slot l = 8*rg + kg (rg, kg in 0..7) is 16 bytes at
+ *   offset 16*l: four little-endian 32-bit words q = 0..3, word q holding
+ *   row 32s + 4rg + q at k = 128t + 16kg + i, i = 0..15.
+ *   Inside a word, the code of i = 4j + b sits at bits 8b+2j .. 8b+2j+1, so
+ *   (word >> 2j) & 0x03030303 holds the codes of k = 4j..4j+3 in bytes 0..3.
+ *   Positions with row >= N or k >= K hold code 01 (weight 0).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the packed matrix, or -1 if N or K is out of range. */
+int64_t w2a8_packed_bytes(int64_t N, int64_t K);
+
+/* Device workspace bytes that w2a8_gemv / w2a8_gemm need for (M, N, K),
+ * or -1 if out of range.  The workspace holds int32 partial sums and
+ * arrival counters of split-K row strips.  The caller allocates it, zeroes
+ * it ONCE before its first use, and may then reuse it for any call with the
+ * same or smaller (M, N, K): each call leaves it zeroed again. */
+int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------
+ * Offline host steps
+ * ------------------------------------------------------------------------ */
+
+/* Absmean ternarization, host memory to host memory.
+ * [WIN] §3.1 and [CPU] §6.3:  sw = mean(|W|);  wq = clamp(round(W/sw), -1, 1).
+ * W: fp32 [N][K] row-major (host).  wq: int8 [N][K] (host).  sw: one float.
+ * The mean is accumulated in fp64 in row-major order and rounded once to
+ * fp32; W/sw is an fp32 division rounded half to even.  An all-zero W
+ * gives sw = 0 and wq = 0.  Returns W2A8_ERR_NULL / W2A8_ERR_SHAPE. */
+int w2a8_ternarize_absmean(const float *W, int64_t N, int64_t K, int8_t *wq,
+                           float *sw);
+
+/* Pack ternary weights into the T32x128 layout, host memory to host memory.
+ * w: int8 [N][K] row-major with values in {-1, 0, 1}.  packed: at least
+ * w2a8_packed_bytes(N, K) bytes (packed_bytes is its capacity).
+ * Returns W2A8_ERR_VALUE if a weight is outside {-1, 0, 1} (packed is then
+ * partly written and must not be used), W2A8_ERR_BUFSIZE if packed_bytes is
+ * too small. */
+int pack_ternary(const int8_t *w, int64_t N, int64_t K, void *packed,
+                 int64_t packed_bytes);
+
+/* Inverse of pack_ternary (host), for tests and inspection.  Returns
+ * W2A8_ERR_VALUE if a code 11 is found at a position inside the matrix. */
+int unpack_ternary(const void *packed, int64_t packed_bytes, int64_t N,
+                   int64_t K, int8_t *w);
+
+/* ------------------------------------------------------------------------
+ * Device steps (enqueued on `stream`)
+ * ------------------------------------------------------------------------ */
+
+/* Per-token absmax quantization of bf16 activations to int8.
+ * [TEST] (introduction): the kernels consume 8-bit activations; the pages
+ * give no quantizer formula.  Per row m:
+ *   a = max_k |x[m][k]|;  inv = 127 / a  (fp32 division);
+ *   x_q[m][k] = clamp(round_half_even(x[m][k] * inv), -127, 127);
+ *   s_a[m] = a / 127  (fp32 division).   A zero row gives 0 and s_a = 0.
+ * x_bf16: device, [M][K] bf16 bit patterns (uint16), 16-byte aligned.
+ * x_q: device, int8 [M][K], 16-byte aligned.  s_a: device, fp32 [M].
+ * NaN and Inf inputs are outside the contract. */
+int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q,
+                   float *s_a, void *stream);
+
+/* W2A8 GEMV, M = 1 (decode).
+ * [TEST] "运行 test.py 做 GEMV 基准测试" / "如何判断结果": y must equal the
+ * integer product of the int8 activations and the weights exactly:
+ *   y_i32[n] = sum_k w[n][k] * x[k]
+ * [WIN] §3.1: the scale is multiplied back after the integer product:
+ *   y_f32[n] = ((float)y_i32[n] * s_a[0]) * s_w
+ * w_packed: device, T32x128 layout of W [N][K] (w2a8_packed_bytes(N, K)).
+ * x: device, int8 [K].  y_i32: device, int32 [N], or NULL.  y_f32: device,
+ * fp32 [N], or NULL; at least one of y_i32 / y_f32 must be given.  s_a:
+ * device, one float (required when y_f32 is given; may be NULL otherwise).
+ * s_w: the per-tensor weight scale, by value.  workspace: device, at least
+ * w2a8_workspace_bytes(1, N, K) bytes, zeroed before first use (see above).
+ * Unlike the reference kernel, which computes only a fixed list of shapes
+ * ([TEST] "限制与注意事项"), every N, K within the limits is computed. */
+int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K,
+              int32_t *y_i32, const float *s_a, float s_w, float *y_f32,
+              void *workspace, int64_t ws_bytes, void *stream);
+
+/* W2A8 batched product, M >= 1 (prefill).
+ * [TEST] "限制与注意事项": the reference handles only M == 1; this entry
+ * computes the same product for M token rows:
+ *   y_i32[m][n] = sum_k w[n][k] * x[m][k]
+ *   y_f32[m][n] = ((float)y_i32[m][n] * s_a[m]) * s_w
+ * x: device, int8 [M][K].  y_i32 / y_f32: device, [M][N] (at least one).
+ * s_a: device, fp32 [M] (required with y_f32).  workspace: at least
+ * w2a8_workspace_bytes(M, N, K) bytes, zeroed before first use. */
+int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N,
+              int64_t K, int32_t *y_i32, const float *s_a, float s_w,
+              float *y_f32, void *workspace, int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W2A8_H */

@@ -1,0 +1,250 @@
+"""CPU-only tests of libw2a8.so: it loads, exports what include/*.h declares,
+its size formulas and host steps agree with the oracle, and its argument
+validation rejects bad calls before any device work.
+
+No device computation is requested here: every device entry point is called
+with exactly one invalid argument, which the library rejects before it makes
+any HIP call (the fake pointers below are never dereferenced).
+"""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w2a8_gemv_amd as w2a8
+
+from conftest import ROOT
+
+ST = {"OK": 0, "NULL": 1, "SHAPE": 2, "ALIGN": 3, "VALUE": 4, "BUFSIZE": 5}
+F = ctypes.c_float
+FAKE = 0x10000          # 16-byte aligned stand-in, never dereferenced
+FAKE_ODD = 0x10004      # 4-byte aligned only
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_header_status_codes_match_library():
+    text = open(os.path.join(ROOT, "include", "w2a8.h")).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"W2A8_(?:ERR_)?(\w+)\s*=\s*(\d+)", text))
+    assert codes["OK"] == 0 and len(codes) == 9
+    L = w2a8.lib()
+    for v in codes.values():
+        assert L.w2a8_status_str(v) and L.w2a8_status_str(v) != b"unknown status"
+    assert L.w2a8_status_str(99) == b"unknown status"
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
+                "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
+                "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
+                "w2a8_tune_gemv", "w2a8_gemv_split"}
+    assert expected.issubset(set(names)), set(names) ^ expected
+    L = ctypes.CDLL(w2a8.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_layout_version():
+    assert w2a8.layout_version() == 1
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (31, 127), (32, 128), (33, 129), (2560, 2560),
+                                 (55296, 5120), (5120, 27648), (3200, 3200)])
+def test_packed_bytes_matches_oracle(N, K):
+    assert w2a8.packed_bytes(N, K) == oracle.packed_bytes(N, K)
+
+
+def test_packed_bytes_is_n_k_over_4_on_workload_shapes():
+    for N, K in synth.SWEEP_SHAPES + synth.LARGE_SHAPES + synth.GEMM_SHAPES:
+        assert w2a8.packed_bytes(N, K) == N * K // 4
+
+
+def test_size_queries_reject_bad_shapes():
+    L = w2a8.lib()
+    assert L.w2a8_packed_bytes(0, 5) == -1
+    assert L.w2a8_packed_bytes(5, 0) == -1
+    assert L.w2a8_packed_bytes(5, 1048448 + 1) == -1
+    assert L.w2a8_workspace_bytes(0, 5, 5) == -1
+    assert L.w2a8_workspace_bytes(1, 5, 5) > 0
+
+
+# ---------------------------------------------------------------------------
+# a2 parity: the library's packer is byte-identical to the oracle's
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,seed", [(1, 1, 0), (31, 127, 1), (33, 129, 2), (64, 384, 3),
+                                      (97, 300, 4), (5, 1000, 5), (2560, 2560, 6)])
+def test_pack_matches_oracle_bytes(N, K, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+    mine = w2a8.pack_ternary(torch.from_numpy(w)).numpy()
+    ref = oracle.pack(w)
+    np.testing.assert_array_equal(mine, ref)
+    back = w2a8.unpack_ternary(torch.from_numpy(ref), N, K).numpy()
+    np.testing.assert_array_equal(back, w)
+
+
+def test_pack_matches_oracle_on_sparse_workload_rows():
+    # first 4096 rows of the 55296 x 5120 workload (P(0) = 0.6)
+    x, w = synth.gemv_case(4096, 5120, synth.LARGE_SEEDS[1], sparse=True)
+    np.testing.assert_array_equal(w2a8.pack_ternary(torch.from_numpy(w)).numpy(), oracle.pack(w))
+
+
+def test_pack_rejects_non_ternary():
+    w = torch.zeros((4, 4), dtype=torch.int8)
+    w[2, 3] = 2
+    with pytest.raises(w2a8.W2A8Error) as e:
+        w2a8.pack_ternary(w)
+    assert e.value.status == ST["VALUE"]
+    w[2, 3] = -128
+    with pytest.raises(w2a8.W2A8Error):
+        w2a8.pack_ternary(w)
+
+
+def test_unpack_rejects_code_11():
+    p = w2a8.pack_ternary(torch.zeros((3, 3), dtype=torch.int8))
+    p[0] = 0xFF
+    with pytest.raises(w2a8.W2A8Error) as e:
+        w2a8.unpack_ternary(p, 3, 3)
+    assert e.value.status == ST["VALUE"]
+
+
+def test_pack_bufsize_and_null():
+    L = w2a8.lib()
+    w = np.zeros((32, 128), np.int8)
+    out = np.zeros(1024, np.uint8)
+    pw, po = w.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p)
+    assert L.pack_ternary(pw, 32, 128, po, 1023) == ST["BUFSIZE"]
+    assert L.pack_ternary(None, 32, 128, po, 1024) == ST["NULL"]
+    assert L.pack_ternary(pw, 32, 128, None, 1024) == ST["NULL"]
+    assert L.pack_ternary(pw, 0, 128, po, 1024) == ST["SHAPE"]
+    assert L.pack_ternary(pw, 32, 128, po, 1024) == ST["OK"]
+    assert L.unpack_ternary(po, 1023, 32, 128, pw) == ST["BUFSIZE"]
+
+
+# ---------------------------------------------------------------------------
+# a1 parity: the library's ternarizer is bit-identical to the oracle's
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,seed", [(1, 1, 0), (7, 300, 1), (64, 640, 2), (1024, 1024, 3)])
+def test_ternarize_matches_oracle(N, K, seed):
+    _, W = synth.linear_case(1, N, K, seed=seed)
+    wq, sw = w2a8.ternarize_absmean(torch.from_numpy(W))
+    owq, osw = oracle.ternarize_absmean(W)
+    assert np.float32(sw) == osw
+    np.testing.assert_array_equal(wq.numpy(), owq)
+
+
+def test_ternarize_matches_oracle_full_linear_shape():
+    _, W = synth.linear_case(1, 13824, 2560, seed=synth.LINEAR_SEEDS[1])
+    wq, sw = w2a8.ternarize_absmean(torch.from_numpy(W))
+    owq, osw = oracle.ternarize_absmean(W)
+    assert np.float32(sw) == osw
+    np.testing.assert_array_equal(wq.numpy(), owq)
+
+
+def test_ternarize_worked_examples_and_zero():
+    for W, sw_e, wq_e in [([[0.75, 0.25], [-0.25, -0.75]], 0.5, [[1, 0], [0, -1]]),
+                          ([[0.0, 0.0]], 0.0, [[0, 0]])]:
+        wq, sw = w2a8.ternarize_absmean(torch.tensor(W, dtype=torch.float32))
+        assert sw == sw_e
+        assert wq.tolist() == wq_e
+
+
+# ---------------------------------------------------------------------------
+# argument validation of the device entry points (rejected before any HIP call)
+# ---------------------------------------------------------------------------
+def _gemv(**kw):
+    a = dict(wp=FAKE, x=FAKE, N=64, K=256, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
+             wsb=1 << 20)
+    a.update(kw)
+    return w2a8.lib().w2a8_gemv(a["wp"], a["x"], a["N"], a["K"], a["y"], a["sa"], F(a["sw"]),
+                                a["yf"], a["ws"], a["wsb"], None)
+
+
+def test_gemv_validation():
+    assert _gemv(wp=None) == ST["NULL"]
+    assert _gemv(x=None) == ST["NULL"]
+    assert _gemv(ws=None) == ST["NULL"]
+    assert _gemv(y=None, yf=None) == ST["NULL"]
+    assert _gemv(sa=None) == ST["NULL"]            # y_f32 needs s_a
+    assert _gemv(N=0) == ST["SHAPE"]
+    assert _gemv(K=0) == ST["SHAPE"]
+    assert _gemv(K=1048448 + 128) == ST["SHAPE"]
+    assert _gemv(N=(1 << 30) + 1) == ST["SHAPE"]
+    assert _gemv(wp=FAKE + 8) == ST["ALIGN"]
+    assert _gemv(x=FAKE + 1) == ST["ALIGN"]
+    assert _gemv(y=FAKE_ODD) == ST["ALIGN"]
+    assert _gemv(yf=FAKE_ODD) == ST["ALIGN"]
+    assert _gemv(sa=FAKE + 2) == ST["ALIGN"]
+    assert _gemv(wsb=w2a8.workspace_bytes(1, 64, 256) - 1) == ST["BUFSIZE"]
+
+
+def _gemm(**kw):
+    a = dict(wp=FAKE, x=FAKE, M=8, N=64, K=256, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
+             wsb=1 << 24)
+    a.update(kw)
+    return w2a8.lib().w2a8_gemm(a["wp"], a["x"], a["M"], a["N"], a["K"], a["y"], a["sa"],
+                                F(a["sw"]), a["yf"], a["ws"], a["wsb"], None)
+
+
+def test_gemm_validation():
+    assert _gemm(wp=None) == ST["NULL"]
+    assert _gemm(x=None) == ST["NULL"]
+    assert _gemm(y=None, yf=None) == ST["NULL"]
+    assert _gemm(sa=None) == ST["NULL"]
+    assert _gemm(ws=None) == ST["NULL"]            # this shape needs split-K scratch
+    assert _gemm(M=0) == ST["SHAPE"]
+    assert _gemm(M=(1 << 20) + 1) == ST["SHAPE"]
+    assert _gemm(N=0) == ST["SHAPE"]
+    assert _gemm(x=FAKE + 4) == ST["ALIGN"]
+    assert _gemm(y=FAKE_ODD) == ST["ALIGN"]
+    assert _gemm(wsb=w2a8.workspace_bytes(8, 64, 256) - 1) == ST["BUFSIZE"]
+
+
+def test_quant_validation():
+    L = w2a8.lib()
+    assert L.quant_act_int8(None, 1, 16, FAKE, FAKE, None) == ST["NULL"]
+    assert L.quant_act_int8(FAKE, 1, 16, None, FAKE, None) == ST["NULL"]
+    assert L.quant_act_int8(FAKE, 1, 16, FAKE, None, None) == ST["NULL"]
+    assert L.quant_act_int8(FAKE, 0, 16, FAKE, FAKE, None) == ST["SHAPE"]
+    assert L.quant_act_int8(FAKE, 1, 0, FAKE, FAKE, None) == ST["SHAPE"]
+    assert L.quant_act_int8(FAKE + 2, 1, 16, FAKE, FAKE, None) == ST["ALIGN"]
+    assert L.quant_act_int8(FAKE, 1, 16, FAKE + 8, FAKE, None) == ST["ALIGN"]
+    assert L.quant_act_int8(FAKE, 1, 16, FAKE, FAKE + 1, None) == ST["ALIGN"]
+
+
+def test_workspace_formula():
+    # GEMV: 4*Np + 4*NS bytes rounded up to 256
+    for N in (1, 31, 32, 2560, 55296):
+        Np = -(-N // 32) * 32
+        assert w2a8.workspace_bytes(1, N, 1000) == -(-(4 * Np + 4 * (Np // 32)) // 256) * 256
+    # large batched outputs never split K: no workspace needed
+    assert w2a8.workspace_bytes(512, 13824, 2560) == 0
+
+
+def test_tuning_knobs_validate():
+    with pytest.raises(w2a8.W2A8Error):
+        w2a8.tune_gemv(0, 8, 4)
+    with pytest.raises(w2a8.W2A8Error):
+        w2a8.tune_gemv(16, 8, 3)
+    assert w2a8.gemv_split(2560, 2560, 256) >= 1
+    assert w2a8.gemv_split(0, 2560, 256) == -1
+
+
+def test_binding_refuses_host_tensors_for_device_calls():
+    with pytest.raises(ValueError):
+        w2a8.quant_act_int8(torch.zeros((1, 16), dtype=torch.bfloat16))

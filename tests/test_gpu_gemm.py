@@ -1,0 +1,111 @@
+"""GPU parity of the batched W2A8 product (M > 1, int8 MFMA): bit-exact int32.
+
+Small and ragged shapes are compared in full; the prefill workload shapes
+(M in {8, 128, 512} at 13824x2560 and 2560x6912) are compared in full for
+M <= 128 and on sampled rows for M = 512 (each sampled row in full).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w2a8_gemv_amd as w2a8
+
+from gpu_util import CANARY_I32, GUARD, check_guard, dev, packed_on_device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm_dev(wp, xd, M, N, K, sa=None, sw=1.0, want_f32=False):
+    y = torch.full((M * N + GUARD,), CANARY_I32, dtype=torch.int32, device=dev())
+    yf = None
+    if want_f32:
+        yf = torch.full((M * N + GUARD,), float("nan"), dtype=torch.float32, device=dev())
+    w2a8.w2a8_gemm(wp, xd, M, N, K, y_i32=y[:M * N], s_a=sa, s_w=sw,
+                   y_f32=None if yf is None else yf[:M * N])
+    torch.cuda.synchronize()
+    check_guard(y, M * N)
+    out = y[:M * N].cpu().numpy().reshape(M, N)
+    if yf is None:
+        return out
+    check_guard(yf, M * N)
+    return out, yf[:M * N].cpu().numpy().reshape(M, N)
+
+
+SMALL = [(2, 1, 1), (2, 32, 128), (3, 33, 129), (16, 64, 256), (17, 100, 300),
+         (31, 97, 97), (33, 128, 512), (64, 256, 1000), (65, 130, 2560), (128, 160, 640),
+         (129, 64, 384), (200, 96, 1024), (8, 2560, 6912), (300, 33, 16)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_gemm_small_ragged(M, N, K):
+    x, w = synth.gemm_case(M, N, K, seed=M + 10 * N + 100 * K)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+
+
+@pytest.mark.parametrize("key", list(synth.GEMM_SEEDS.keys()),
+                         ids=[f"{n}x{k}_M{m}" for (n, k), m in synth.GEMM_SEEDS.keys()])
+def test_gemm_prefill_shapes(key):
+    (N, K), M = key
+    x, w = synth.gemm_case(M, N, K, seed=synth.GEMM_SEEDS[key])
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    if M <= 128:
+        np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+    else:
+        rng = np.random.default_rng(0)
+        rows = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, M - 1],
+                                         rng.choice(M, 17, replace=False)]))
+        np.testing.assert_array_equal(y[rows], oracle.gemm_i32(x[rows], w))
+
+
+def test_gemm_extremes():
+    M, N, K = 20, 64, 27648
+    x = np.full((M, K), -128, np.int8)
+    x[1::2] = 127
+    w = -np.ones((N, K), np.int8)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    assert np.all(y[0::2] == 128 * K) and np.all(y[1::2] == -127 * K)
+
+
+def test_gemm_fp32_epilogue_per_row_scales():
+    M, N, K = 40, 2560, 2560
+    x, w = synth.gemm_case(M, N, K, seed=3)
+    rng = np.random.default_rng(4)
+    sa = rng.uniform(0.001, 0.1, size=M).astype(np.float32)
+    sw = np.float32(0.0159)
+    yi, yf = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K, sa=to_dev(sa), sw=float(sw),
+                       want_f32=True)
+    acc = oracle.gemm_i32(x, w)
+    np.testing.assert_array_equal(yi, acc)
+    np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw))
+
+
+def test_gemm_rows_match_gemv():
+    """Row m of the batched product equals the GEMV of row m."""
+    M, N, K = 24, 2560, 2560
+    x, w = synth.gemm_case(M, N, K, seed=12)
+    wp = packed_on_device(w)
+    y = _gemm_dev(wp, to_dev(x), M, N, K)
+    for m in (0, 7, 23):
+        yv = torch.empty(N, dtype=torch.int32, device=dev())
+        w2a8.w2a8_gemv(wp, to_dev(x[m]), N, K, y_i32=yv)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y[m], yv.cpu().numpy())
+
+
+def test_gemm_repeat_deterministic_and_workspace_reset():
+    M, N, K = 8, 2560, 6912
+    x, w = synth.gemm_case(M, N, K, seed=41)
+    wp, xd = packed_on_device(w), to_dev(x)
+    nb = w2a8.workspace_bytes(M, N, K)
+    assert nb > 0
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev())
+    ref = oracle.gemm_i32(x, w)
+    for _ in range(4):
+        y = torch.empty((M, N), dtype=torch.int32, device=dev())
+        w2a8.w2a8_gemm(wp, xd, M, N, K, y_i32=y, workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref)
+        assert int(ws.count_nonzero()) == 0

@@ -1,0 +1,311 @@
+"""Thin Python binding of libw2a8.so (the MI355X W2A8 linear layer).
+
+Every function marshals arguments (dtype, shape, device, contiguity checks;
+pointers and the current HIP stream) and calls the C ABI of the same name in
+``include/w2a8.h``; all computation happens in the library.  PyTorch supplies
+device memory and streams only.  If the library has not been built, importing
+the binding's functions raises; there is no fallback path.
+
+Host functions take/return CPU tensors; device functions take CUDA (HIP)
+tensors on the current device and enqueue work on the current stream (or on
+``stream=`` if given).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
+    "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
+    "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
+    "tune_gemv", "gemv_split",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw2a8.so")
+LAYOUT_VERSION = 1
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class W2A8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().w2a8_status_str(status).decode()} (status {status})")
+
+
+def lib():
+    """The loaded library (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python w2a8_gemv_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.w2a8_status_str.argtypes = [I32]
+        L.w2a8_status_str.restype = ctypes.c_char_p
+        L.w2a8_layout_version.argtypes = []
+        L.w2a8_layout_version.restype = I32
+        L.w2a8_packed_bytes.argtypes = [I64, I64]
+        L.w2a8_packed_bytes.restype = I64
+        L.w2a8_workspace_bytes.argtypes = [I64, I64, I64]
+        L.w2a8_workspace_bytes.restype = I64
+        L.w2a8_ternarize_absmean.argtypes = [P, I64, I64, P, P]
+        L.w2a8_ternarize_absmean.restype = I32
+        L.pack_ternary.argtypes = [P, I64, I64, P, I64]
+        L.pack_ternary.restype = I32
+        L.unpack_ternary.argtypes = [P, I64, I64, I64, P]
+        L.unpack_ternary.restype = I32
+        L.quant_act_int8.argtypes = [P, I64, I64, P, P, P]
+        L.quant_act_int8.restype = I32
+        L.w2a8_gemv.argtypes = [P, P, I64, I64, P, P, F32, P, P, I64, P]
+        L.w2a8_gemv.restype = I32
+        L.w2a8_gemm.argtypes = [P, P, I64, I64, I64, P, P, F32, P, P, I64, P]
+        L.w2a8_gemm.restype = I32
+        L.w2a8_tune_gemv.argtypes = [I32, I32, I32]
+        L.w2a8_tune_gemv.restype = I32
+        L.w2a8_gemv_split.argtypes = [I64, I64, I32]
+        L.w2a8_gemv_split.restype = I32
+        if L.w2a8_layout_version() != LAYOUT_VERSION:
+            raise RuntimeError("libw2a8.so layout version does not match the binding")
+        _lib = L
+        return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise W2A8Error(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device == "cuda" and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device == "cpu" and t.is_cuda:
+        raise ValueError(f"{name} must be a host tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------------------
+# sizes
+# ---------------------------------------------------------------------------
+def layout_version() -> int:
+    return int(lib().w2a8_layout_version())
+
+
+def packed_bytes(N: int, K: int) -> int:
+    n = int(lib().w2a8_packed_bytes(N, K))
+    if n < 0:
+        raise W2A8Error(2, "w2a8_packed_bytes")
+    return n
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    n = int(lib().w2a8_workspace_bytes(M, N, K))
+    if n < 0:
+        raise W2A8Error(2, "w2a8_workspace_bytes")
+    return n
+
+
+# ---------------------------------------------------------------------------
+# offline host steps
+# ---------------------------------------------------------------------------
+def ternarize_absmean(W: torch.Tensor):
+    """W fp32 [N, K] (CPU) -> (wq int8 [N, K] CPU, sw float)."""
+    _need(W, "W", torch.float32, "cpu")
+    N, K = W.shape
+    wq = torch.empty((N, K), dtype=torch.int8)
+    sw = torch.zeros(1, dtype=torch.float32)
+    _check(lib().w2a8_ternarize_absmean(_ptr(W), N, K, _ptr(wq), _ptr(sw)),
+           "w2a8_ternarize_absmean")
+    return wq, float(sw[0])
+
+
+def pack_ternary(w: torch.Tensor) -> torch.Tensor:
+    """w int8 [N, K] in {-1,0,1} (CPU) -> packed uint8 [packed_bytes(N, K)] (CPU)."""
+    _need(w, "w", torch.int8, "cpu")
+    N, K = w.shape
+    nb = packed_bytes(N, K)
+    out = torch.empty(nb, dtype=torch.uint8)
+    _check(lib().pack_ternary(_ptr(w), N, K, _ptr(out), nb), "pack_ternary")
+    return out
+
+
+def unpack_ternary(p: torch.Tensor, N: int, K: int) -> torch.Tensor:
+    _need(p, "packed", torch.uint8, "cpu")
+    w = torch.empty((N, K), dtype=torch.int8)
+    _check(lib().unpack_ternary(_ptr(p), p.numel(), N, K, _ptr(w)), "unpack_ternary")
+    return w
+
+
+# ---------------------------------------------------------------------------
+# workspace cache (one zeroed buffer per device and stream)
+# ---------------------------------------------------------------------------
+class Workspace:
+    """Zero-initialised device workspace; each library call leaves it zeroed."""
+
+    _cache = {}
+    _lock = threading.Lock()
+
+    @classmethod
+    def get(cls, nbytes: int, device: torch.device, stream) -> torch.Tensor | None:
+        if nbytes <= 0:
+            return None
+        key = (device.index, stream.cuda_stream)
+        with cls._lock:
+            buf = cls._cache.get(key)
+            if buf is None or buf.numel() < nbytes:
+                with torch.cuda.stream(stream):
+                    buf = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+                cls._cache[key] = buf
+            return buf
+
+
+def _ws(nbytes, device, stream, workspace):
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, "cuda")
+        return workspace
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return Workspace.get(nbytes, device, s)
+
+
+# ---------------------------------------------------------------------------
+# device steps
+# ---------------------------------------------------------------------------
+def quant_act_int8(x_bf16: torch.Tensor, x_q=None, s_a=None, stream=None):
+    """x bf16 [M, K] (device) -> (x_q int8 [M, K], s_a fp32 [M])."""
+    _need(x_bf16, "x_bf16", torch.bfloat16, "cuda")
+    if x_bf16.dim() == 1:
+        x_bf16 = x_bf16.view(1, -1)
+    M, K = x_bf16.shape
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x_bf16.device)
+    if s_a is None:
+        s_a = torch.empty(M, dtype=torch.float32, device=x_bf16.device)
+    _need(x_q, "x_q", torch.int8, "cuda")
+    _need(s_a, "s_a", torch.float32, "cuda")
+    if x_q.numel() != M * K or s_a.numel() != M:
+        raise ValueError("x_q / s_a have the wrong size")
+    _check(lib().quant_act_int8(_ptr(x_bf16), M, K, _ptr(x_q), _ptr(s_a), _stream_handle(stream)),
+           "quant_act_int8")
+    return x_q, s_a
+
+
+def w2a8_gemv(w_packed, x, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
+              workspace=None, stream=None):
+    """Raw C-ABI call (outputs must be given); returns nothing."""
+    _need(w_packed, "w_packed", torch.uint8, "cuda")
+    _need(x, "x", torch.int8, "cuda")
+    if x.numel() != K:
+        raise ValueError("x must have K elements")
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than packed_bytes(N, K)")
+    for t, nm, dt in ((y_i32, "y_i32", torch.int32), (y_f32, "y_f32", torch.float32)):
+        if t is not None:
+            _need(t, nm, dt, "cuda")
+            if t.numel() != N:
+                raise ValueError(f"{nm} must have N elements")
+    if s_a is not None:
+        _need(s_a, "s_a", torch.float32, "cuda")
+    need = workspace_bytes(1, N, K)
+    ws = _ws(need, x.device, stream, workspace)
+    _check(lib().w2a8_gemv(_ptr(w_packed), _ptr(x), N, K, _ptr(y_i32), _ptr(s_a),
+                           ctypes.c_float(s_w), _ptr(y_f32), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream_handle(stream)),
+           "w2a8_gemv")
+
+
+def w2a8_gemm(w_packed, x, M, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
+              workspace=None, stream=None):
+    """Raw C-ABI call (outputs must be given); returns nothing."""
+    _need(w_packed, "w_packed", torch.uint8, "cuda")
+    _need(x, "x", torch.int8, "cuda")
+    if x.numel() != M * K:
+        raise ValueError("x must have M*K elements")
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than packed_bytes(N, K)")
+    for t, nm, dt in ((y_i32, "y_i32", torch.int32), (y_f32, "y_f32", torch.float32)):
+        if t is not None:
+            _need(t, nm, dt, "cuda")
+            if t.numel() != M * N:
+                raise ValueError(f"{nm} must have M*N elements")
+    if s_a is not None:
+        _need(s_a, "s_a", torch.float32, "cuda")
+        if s_a.numel() != M:
+            raise ValueError("s_a must have M elements")
+    need = workspace_bytes(M, N, K)
+    ws = _ws(need, x.device, stream, workspace)
+    _check(lib().w2a8_gemm(_ptr(w_packed), _ptr(x), M, N, K, _ptr(y_i32), _ptr(s_a),
+                           ctypes.c_float(s_w), _ptr(y_f32), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream_handle(stream)),
+           "w2a8_gemm")
+
+
+def gemv(w_packed, x, N, K, *, out_i32=True, s_a=None, s_w=1.0, stream=None):
+    """y_i32 [N] (and y_f32 [N] when s_a is given) for one int8 activation row."""
+    y_i32 = torch.empty(N, dtype=torch.int32, device=x.device) if out_i32 else None
+    y_f32 = torch.empty(N, dtype=torch.float32, device=x.device) if s_a is not None else None
+    w2a8_gemv(w_packed, x, N, K, y_i32=y_i32, s_a=s_a, s_w=s_w, y_f32=y_f32, stream=stream)
+    return y_i32 if y_f32 is None else (y_i32, y_f32)
+
+
+def gemm(w_packed, x, N, K, *, out_i32=True, s_a=None, s_w=1.0, stream=None):
+    """Y_i32 [M, N] (and Y_f32 when s_a is given) for int8 activations [M, K]."""
+    M = x.shape[0]
+    y_i32 = torch.empty((M, N), dtype=torch.int32, device=x.device) if out_i32 else None
+    y_f32 = torch.empty((M, N), dtype=torch.float32, device=x.device) if s_a is not None else None
+    w2a8_gemm(w_packed, x, M, N, K, y_i32=y_i32, s_a=s_a, s_w=s_w, y_f32=y_f32, stream=stream)
+    return y_i32 if y_f32 is None else (y_i32, y_f32)
+
+
+def linear(x_bf16, w_packed, s_w, N, K, stream=None):
+    """Full W2A8 linear layer: bf16 activations [M, K] -> fp32 [M, N].
+
+    quant_act_int8, then w2a8_gemv (M == 1) or w2a8_gemm (M > 1) with the
+    fp32 epilogue, all enqueued on one stream with no host synchronisation.
+    """
+    x2 = x_bf16.view(1, -1) if x_bf16.dim() == 1 else x_bf16
+    M = x2.shape[0]
+    xq, sa = quant_act_int8(x2, stream=stream)
+    y = torch.empty((M, N), dtype=torch.float32, device=x2.device)
+    if M == 1:
+        w2a8_gemv(w_packed, xq.view(-1), N, K, s_a=sa, s_w=s_w, y_f32=y.view(-1), stream=stream)
+    else:
+        w2a8_gemm(w_packed, xq, M, N, K, s_a=sa, s_w=s_w, y_f32=y, stream=stream)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# tuning knobs (w2a8_tuning.h)
+# ---------------------------------------------------------------------------
+def tune_gemv(waves_per_cu: int, min_tiles: int, unroll: int):
+    _check(lib().w2a8_tune_gemv(waves_per_cu, min_tiles, unroll), "w2a8_tune_gemv")
+
+
+def gemv_split(N: int, K: int, cus: int) -> int:
+    return int(lib().w2a8_gemv_split(N, K, cus))

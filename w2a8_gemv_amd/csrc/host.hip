@@ -1,0 +1,315 @@
+// Host side of libw2a8.so: argument validation, the offline steps
+// (ternarization and packing) and the device entry points' dispatch.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "common.h"
+#include "w2a8_tuning.h"
+
+namespace w2a8 {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+bool g_dev_known[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+int g_dev_status[kMaxDevices];
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool nk_ok(int64_t N, int64_t K) {
+    return N >= 1 && K >= 1 && N <= kMaxN && K <= W2A8_MAX_K;
+}
+
+}  // namespace
+
+int current_device(DeviceInfo *out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return W2A8_ERR_NODEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    if (!g_dev_known[dev]) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return W2A8_ERR_NODEVICE;
+        DeviceInfo info;
+        info.id = dev;
+        info.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+        info.xcds = 8;
+        g_dev[dev] = info;
+        g_dev_status[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? W2A8_OK : W2A8_ERR_ARCH;
+        g_dev_known[dev] = true;
+    }
+    *out = g_dev[dev];
+    return g_dev_status[dev];
+}
+
+GemvPolicy &gemv_policy() {
+    static GemvPolicy p = {16, 8, 4};
+    return p;
+}
+
+// Split of a GEMV into work-waves: each 32-row strip is cut into S k-parts
+// of at least `min_tiles` tiles, S chosen so that NS*S waves cover the
+// device about `waves_per_cu` deep.  S == 1 needs no cross-wave reduction.
+static int gemv_parts(int64_t NS, int64_t KT, int cus) {
+    const GemvPolicy &p = gemv_policy();
+    int64_t target = int64_t(cus) * std::max(1, p.waves_per_cu);
+    int64_t s = ceil_div(target, NS);
+    int64_t smax = std::max<int64_t>(1, KT / std::max(1, p.min_tiles));
+    s = std::min(s, smax);
+    s = std::max<int64_t>(1, std::min(s, KT));
+    return int(s);
+}
+
+}  // namespace w2a8
+
+using namespace w2a8;
+
+extern "C" {
+
+const char *w2a8_status_str(int status) {
+    switch (status) {
+    case W2A8_OK: return "ok";
+    case W2A8_ERR_NULL: return "a required pointer is NULL";
+    case W2A8_ERR_SHAPE: return "M, N or K out of range";
+    case W2A8_ERR_ALIGN: return "a pointer is not aligned as required";
+    case W2A8_ERR_VALUE: return "weight outside {-1,0,1} or invalid 2-bit code";
+    case W2A8_ERR_BUFSIZE: return "packed or workspace buffer too small";
+    case W2A8_ERR_NODEVICE: return "no HIP device available";
+    case W2A8_ERR_ARCH: return "current device is not gfx950";
+    case W2A8_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int w2a8_layout_version(void) { return W2A8_LAYOUT_VERSION; }
+
+int64_t w2a8_packed_bytes(int64_t N, int64_t K) {
+    if (!nk_ok(N, K)) return -1;
+    return round_up(N, kTileRows) * round_up(K, kTileK) / 4;
+}
+
+int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!nk_ok(N, K) || M < 1 || M > kMaxM) return -1;
+    const int64_t Np = round_up(N, kTileRows);
+    const int64_t NS = Np / kTileRows;
+    int64_t bytes = 0;
+    if (M == 1) {
+        // GEMV: int32 partial per padded row + one arrival counter per strip.
+        bytes = 4 * Np + 4 * NS;
+    } else if (M * Np <= kGemmSplitMaxOut) {
+        // GEMM split-K: int32 partial per output + one counter per
+        // (m-block of >= 16 rows, n-block of 4 strips).
+        bytes = 4 * M * Np + 4 * ceil_div(M, 16) * ceil_div(NS, 4);
+    }
+    return round_up(bytes, 256);
+}
+
+// ---------------------------------------------------------------------------
+// a1: absmean ternarization (host)
+// ---------------------------------------------------------------------------
+int w2a8_ternarize_absmean(const float *W, int64_t N, int64_t K, int8_t *wq, float *sw) {
+    if (!W || !wq || !sw) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    const int64_t total = N * K;
+    // fp64 sum of |W| in row-major order, rounded once to fp32.
+    double s = 0.0;
+    for (int64_t i = 0; i < total; ++i) s += fabs(double(W[i]));
+    const float scale = float(s / double(total));
+    *sw = scale;
+    if (scale == 0.0f) {
+        memset(wq, 0, size_t(total));
+        return W2A8_OK;
+    }
+    for (int64_t i = 0; i < total; ++i) {
+        const float q = W[i] / scale;  // fp32 division
+        float r = rintf(q);            // nearest, ties to even
+        r = r > 1.0f ? 1.0f : (r < -1.0f ? -1.0f : r);
+        wq[i] = int8_t(r);
+    }
+    return W2A8_OK;
+}
+
+// ---------------------------------------------------------------------------
+// a2: packing (host).  One 32-bit word = 16 codes of one row.
+// ---------------------------------------------------------------------------
+int pack_ternary(const int8_t *w, int64_t N, int64_t K, void *packed, int64_t packed_bytes) {
+    if (!w || !packed) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    const int64_t need = w2a8_packed_bytes(N, K);
+    if (packed_bytes < need) return W2A8_ERR_BUFSIZE;
+    const int64_t Np = round_up(N, kTileRows), KT = round_up(K, kTileK) / kTileK;
+    uint32_t *out = static_cast<uint32_t *>(packed);
+    for (int64_t n = 0; n < Np; ++n) {
+        const int64_t s = n / kTileRows, r = n % kTileRows, rg = r / 4, q = r % 4;
+        const int8_t *row = n < N ? w + n * K : nullptr;
+        for (int64_t t = 0; t < KT; ++t) {
+            uint32_t *tile = out + (s * KT + t) * kTileWords;
+            for (int kg = 0; kg < 8; ++kg) {
+                const int64_t k0 = t * kTileK + 16 * kg;
+                uint32_t word = 0;
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t k = k0 + i;
+                    int v = 0;
+                    if (row && k < K) {
+                        v = row[k];
+                        if (v < -1 || v > 1) return W2A8_ERR_VALUE;
+                    }
+                    const uint32_t code = uint32_t(v + 1);
+                    word |= code << (8 * (i & 3) + 2 * (i >> 2));
+                }
+                tile[(8 * rg + kg) * 4 + q] = word;
+            }
+        }
+    }
+    return W2A8_OK;
+}
+
+int unpack_ternary(const void *packed, int64_t packed_bytes, int64_t N, int64_t K, int8_t *w) {
+    if (!packed || !w) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    if (packed_bytes < w2a8_packed_bytes(N, K)) return W2A8_ERR_BUFSIZE;
+    const int64_t KT = round_up(K, kTileK) / kTileK;
+    const uint32_t *in = static_cast<const uint32_t *>(packed);
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t s = n / kTileRows, r = n % kTileRows, rg = r / 4, q = r % 4;
+        for (int64_t t = 0; t < KT; ++t) {
+            const uint32_t *tile = in + (s * KT + t) * kTileWords;
+            for (int kg = 0; kg < 8; ++kg) {
+                const uint32_t word = tile[(8 * rg + kg) * 4 + q];
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t k = t * kTileK + 16 * kg + i;
+                    if (k >= K) break;
+                    const uint32_t code = (word >> (8 * (i & 3) + 2 * (i >> 2))) & 3u;
+                    if (code == 3u) return W2A8_ERR_VALUE;
+                    w[n * K + k] = int8_t(int(code) - 1);
+                }
+            }
+        }
+    }
+    return W2A8_OK;
+}
+
+// ---------------------------------------------------------------------------
+// a3: activation quantization (device)
+// ---------------------------------------------------------------------------
+int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q, float *s_a,
+                   void *stream) {
+    if (!x_bf16 || !x_q || !s_a) return W2A8_ERR_NULL;
+    if (M < 1 || M > kMaxM || K < 1 || K > W2A8_MAX_K) return W2A8_ERR_SHAPE;
+    if (!aligned(x_bf16, 16) || !aligned(x_q, 16) || !aligned(s_a, 4)) return W2A8_ERR_ALIGN;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+    hipError_t e = launch_quant(x_bf16, int(M), int(K), x_q, s_a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// a4..a7: GEMV (device)
+// ---------------------------------------------------------------------------
+int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32_t *y_i32,
+              const float *s_a, float s_w, float *y_f32, void *workspace, int64_t ws_bytes,
+              void *stream) {
+    if (!w_packed || !x || !workspace) return W2A8_ERR_NULL;
+    if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
+    if (y_f32 && !s_a) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    if (!aligned(w_packed, 16) || !aligned(x, 16) || (y_i32 && !aligned(y_i32, 16)) ||
+        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)) || !aligned(workspace, 16))
+        return W2A8_ERR_ALIGN;
+    if (ws_bytes < w2a8_workspace_bytes(1, N, K)) return W2A8_ERR_BUFSIZE;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+
+    const int64_t Np = round_up(N, kTileRows);
+    GemvLaunch a;
+    a.wp = static_cast<const uint32_t *>(w_packed);
+    a.x = x;
+    a.y_i32 = y_i32;
+    a.y_f32 = y_f32;
+    a.sa = s_a;
+    a.sw = s_w;
+    a.ws_acc = static_cast<int32_t *>(workspace);
+    a.ws_cnt = reinterpret_cast<uint32_t *>(a.ws_acc + Np);
+    a.N = int(N);
+    a.K = int(K);
+    a.KT = int(round_up(K, kTileK) / kTileK);
+    a.NS = int(Np / kTileRows);
+    a.S = gemv_parts(a.NS, a.KT, dev.cus);
+    a.unroll = gemv_policy().unroll;
+    hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// a8: batched product (device)
+// ---------------------------------------------------------------------------
+int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64_t K,
+              int32_t *y_i32, const float *s_a, float s_w, float *y_f32, void *workspace,
+              int64_t ws_bytes, void *stream) {
+    if (!w_packed || !x) return W2A8_ERR_NULL;
+    if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
+    if (y_f32 && !s_a) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K) || M < 1 || M > kMaxM) return W2A8_ERR_SHAPE;
+    const int64_t need = w2a8_workspace_bytes(M, N, K);
+    if (need > 0 && !workspace) return W2A8_ERR_NULL;
+    if (!aligned(w_packed, 16) || !aligned(x, 16) || (y_i32 && !aligned(y_i32, 16)) ||
+        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)) ||
+        (workspace && !aligned(workspace, 16)))
+        return W2A8_ERR_ALIGN;
+    if (ws_bytes < need) return W2A8_ERR_BUFSIZE;
+    if (M * round_up(N, kTileRows) > (int64_t(1) << 40)) return W2A8_ERR_SHAPE;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+    const int64_t Np = round_up(N, kTileRows);
+    GemmLaunch a;
+    a.wp = static_cast<const uint32_t *>(w_packed);
+    a.x = x;
+    a.y_i32 = y_i32;
+    a.y_f32 = y_f32;
+    a.sa = s_a;
+    a.sw = s_w;
+    a.ws_acc = static_cast<int32_t *>(workspace);
+    a.ws_cnt = need > 0 ? reinterpret_cast<uint32_t *>(a.ws_acc + M * Np) : nullptr;
+    a.M = int(M);
+    a.N = int(N);
+    a.K = int(K);
+    a.KT = int(round_up(K, kTileK) / kTileK);
+    a.NS = int(Np / kTileRows);
+    a.shape = gemm_shape(M, N, K, dev.cus, need > 0);
+    if (int64_t(a.shape.tiles) + 8 > int64_t(INT32_MAX)) return W2A8_ERR_SHAPE;
+    hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// Tuning knobs (w2a8_tuning.h)
+// ---------------------------------------------------------------------------
+int w2a8_tune_gemv(int waves_per_cu, int min_tiles, int unroll) {
+    if (waves_per_cu < 1 || waves_per_cu > 64 || min_tiles < 1 ||
+        !(unroll == 2 || unroll == 4 || unroll == 8))
+        return W2A8_ERR_VALUE;
+    GemvPolicy &p = gemv_policy();
+    p.waves_per_cu = waves_per_cu;
+    p.min_tiles = min_tiles;
+    p.unroll = unroll;
+    return W2A8_OK;
+}
+
+int w2a8_gemv_split(int64_t N, int64_t K, int cus) {
+    if (!nk_ok(N, K) || cus < 1) return -1;
+    const int64_t NS = round_up(N, kTileRows) / kTileRows;
+    const int64_t KT = round_up(K, kTileK) / kTileK;
+    return gemv_parts(NS, KT, cus);
+}
+
+}  // extern "C"

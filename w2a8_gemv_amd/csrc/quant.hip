@@ -1,0 +1,93 @@
+// Per-token absmax quantization of bf16 activations to int8 (gfx950).
+//
+// The pages fix 8-bit activations ("如何编译 BitNet W2A8 CUDA 内核并用 test.py
+// 运行 GEMV 加速测试？", introduction) but give no quantizer.  Per row m:
+//   a = max|x|;  inv = 127/a;  q = clamp(round_half_even(x*inv), -127, 127);
+//   s_a = a/127;  a zero row gives q = 0, s_a = 0.
+// Every step is a single correctly rounded fp32 operation (the division is
+// IEEE, the product is not contracted, v_rndne_f32 rounds half to even), so
+// the result is bit-identical to any IEEE implementation of the same steps.
+//
+// One 256-thread workgroup per row: a vectorised max pass, a block max, then
+// a quantize pass that re-reads the row from L2.
+#include "common.h"
+
+namespace w2a8 {
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t q8(float x, float inv) {
+    float r = __builtin_rintf(x * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return uint32_t(uint8_t(int8_t(int(r))));
+}
+
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t *xb, int M, int K, int8_t *xq,
+                                                    float *sa) {
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t *row = xb + int64_t(m) * K;
+    int8_t *out = xq + int64_t(m) * K;
+    // Rows are 16-byte aligned (input) and 8-byte aligned (output) when K%8 == 0.
+    const bool vec = (K & 7) == 0;
+
+    float amax = 0.0f;
+    if (vec) {
+        const v4u *r8 = reinterpret_cast<const v4u *>(row);
+        for (int c = tid; c < K / 8; c += 256) {
+            const v4u v = r8[c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(v[j])), fabsf(hi_bf16(v[j]))));
+        }
+    } else {
+        for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf(lo_bf16(row[k])));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    __shared__ float red[4];
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+    if (amax == 0.0f) {
+        for (int k = tid; k < K; k += 256) out[k] = 0;
+        if (tid == 0) sa[m] = 0.0f;
+        return;
+    }
+    const float inv = 127.0f / amax;
+    if (vec) {
+        const v4u *r8 = reinterpret_cast<const v4u *>(row);
+        v2u *o8 = reinterpret_cast<v2u *>(out);
+        for (int c = tid; c < K / 8; c += 256) {
+            const v4u v = r8[c];
+            uint32_t o[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t a = v[2 * h], b = v[2 * h + 1];
+                o[h] = q8(lo_bf16(a), inv) | (q8(hi_bf16(a), inv) << 8) |
+                       (q8(lo_bf16(b), inv) << 16) | (q8(hi_bf16(b), inv) << 24);
+            }
+            o8[c] = v2u{o[0], o[1]};
+        }
+    } else {
+        for (int k = tid; k < K; k += 256) out[k] = int8_t(q8(lo_bf16(row[k]), inv));
+    }
+    if (tid == 0) sa[m] = amax / 127.0f;
+}
+
+}  // namespace
+
+hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
+                        hipStream_t stream) {
+    void *args[] = {const_cast<uint16_t **>(&xb), &M, &K, &xq, &sa};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&quant_kernel), dim3(unsigned(M)),
+                           dim3(256), args, 0, stream);
+}
+
+}  // namespace w2a8

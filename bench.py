@@ -1,0 +1,468 @@
+#!/usr/bin/env python3
+"""Benchmark of the W2A8 GEMV (M = 1) on one MI355X.
+
+Workload: the eight (N, K) shapes of the benchmark page's test script
+("如何编译 BitNet W2A8 CUDA 内核并用 test.py 运行 GEMV 加速测试？", section
+"运行 test.py 做 GEMV 基准测试"), random int8 activations and ternary weights
+(1/3 each), int32 output.  One step = one GEMV per shape (the whole sweep),
+with the packed weights read cold: each step uses its own copy of every
+matrix, rotating over enough copies (16 x 46 MB) that the 256 MB Infinity
+Cache and the L2s never hold a copy when it is read again.  Inputs are
+resident in HBM before timing starts.
+
+Each step is one HIP graph of the eight launches.  Two events on the launch
+stream bracket the K timed steps; their device time divided by the 8*K
+launches is the average launch duration, so the roofline's `achieved` is the
+algorithmic bytes of all launches over that device time (it includes the
+short dispatch gaps between graph nodes).  The host clock around the K steps
+gives the whole-job rate (`value`).  Algorithmic bytes per launch: N*K/4
+(packed weights) + K (activations) + 4N (int32 output).  Events are not put
+around single launches: a marker costs about as much as a small GEMV, and
+markers captured inside a graph do not wait for the preceding kernel node.
+
+Per-shape times ("detail") are measured the same way: one graph of 24
+launches of one shape (rotating copies when cold), bracketed by two events.
+
+Extras reported under "detail": per-shape times, the host-call latency of
+one synchronised call (mean of 50, like the page's timeit(50)), the two
+large shapes (5120x27648, 55296x5120; 60% zero weights) cold and warm, and a
+device copy-bandwidth calibration.  The CPU baseline times the plain-C oracle
+on the same eight GEMVs (single thread) and spot-checks the GPU outputs.
+
+  python bench.py [--steps K] [--warmup W] [--mode cold|warm] [--no-cpu-baseline]
+                  [--no-extra] [--eager]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W2A8 GEMV us/call and cold-cache HBM GB/s (% of peak) per (N,K), M=1"
+PEAK_HBM_GBPS = 8000.0
+ROTATE_BYTES = 700e6          # > 256 MB Infinity Cache + 8 x 4 MB L2, with margin
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
+GEMV_SRC = os.path.join(ROOT, "w2a8_gemv_amd", "csrc", "gemv.hip")
+
+# The page's A100 40GB numbers for the same shapes (host-timed mean of 50
+# calls; another machine): context only.
+A100_US = {(2560, 2560): 13.32, (3840, 2560): 14.90, (13824, 2560): 18.75, (2560, 6912): 14.49,
+           (3200, 3200): 14.61, (4800, 3200): 13.09, (3200, 10240): 19.64,
+           (20480, 3200): 30.99}
+
+
+def algo_bytes(n, k):
+    return n * k // 4 + k + 4 * n
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each GEMV from the host instead of replaying graphs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device copy (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --steps 4 --warmup 1 --no-extra --no-cpu-baseline "
+                         "--calibrate-copy` into " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    return ap.parse_args()
+
+
+CALIB_BYTES = 256 << 20
+
+
+def write_traffic_summary(fetch_csv, write_csv, cus=256):
+    """Per-launch HBM traffic of the GEMV from two counter runs.
+
+    Counter values are KiB per dispatch.  Each counter is scaled by what it
+    reads for the 256 MiB calibration copy (the largest copy dispatch of the
+    run), whose true read and write sizes are known."""
+    import csv
+
+    import synth
+    import w2a8_gemv_amd as w2a8
+
+    def load(path):
+        rows = list(csv.DictReader(open(path)))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        factor = CALIB_BYTES / (max(copies) * 1024.0)
+        per = {}
+        for r in rows:
+            if "gemv_kernel" in r["Kernel_Name"]:
+                per.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]) * 1024.0)
+        return factor, per
+
+    ff, fetch = load(fetch_csv)
+    wf, write = load(write_csv)
+    shapes = []
+    for n, k in synth.SWEEP_SHAPES:
+        wk, sg, _ = w2a8.gemv_plan(n, k, cus)
+        grid = (-(-n // 32)) * sg * 64 * wk
+        f = sum(fetch[grid]) / len(fetch[grid]) * ff
+        w = sum(write[grid]) / len(write[grid]) * wf
+        shapes.append({"n": n, "k": k, "algorithmic_bytes": algo_bytes(n, k),
+                       "fetch_bytes": round(f), "write_bytes": round(w),
+                       "ratio": round((f + w) / algo_bytes(n, k), 4)})
+    with open(GEMV_SRC, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    per_launch = sum(x["fetch_bytes"] + x["write_bytes"] for x in shapes) / len(shapes)
+    algo = sum(x["algorithmic_bytes"] for x in shapes) / len(shapes)
+    out = {"gemv_hip_sha256": sha, "bytes_per_launch": round(per_launch),
+           "algorithmic_bytes_per_launch": round(algo),
+           "ratio": round(per_launch / algo, 4),
+           "fetch_scale": round(ff, 5), "write_scale": round(wf, 5),
+           "calibration": "one 256 MiB device copy per run; scale = 256 MiB / counter",
+           "per_shape": shapes,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python -u "
+               "bench.py --steps 4 --warmup 1 --no-extra --no-cpu-baseline --calibrate-copy",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python -u "
+               "bench.py --steps 4 --warmup 1 --no-extra --no-cpu-baseline --calibrate-copy",
+               "python bench.py --traffic-summary <fetch_counter_collection.csv> "
+               "<write_counter_collection.csv>"]}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
+class Shape:
+    """Device buffers of one GEMV shape (rotating weight copies)."""
+
+    def __init__(self, torch, w2a8, n, k, x, w, slots, dev):
+        self.n, self.k = n, k
+        self.nbytes = algo_bytes(n, k)
+        wp = w2a8.pack_ternary(torch.from_numpy(w)).to(dev)
+        self.copies = [wp] + [wp.clone() for _ in range(slots - 1)]
+        self.x = torch.from_numpy(x).to(dev)
+        self.y = torch.empty(n, dtype=torch.int32, device=dev)
+        self.ws = torch.zeros(max(256, w2a8.workspace_bytes(1, n, k)), dtype=torch.uint8,
+                              device=dev)
+        self.x_host = x
+
+    def launcher(self, lib, stream):
+        """A closure that enqueues the C-ABI GEMV on `stream` for copy `slot`."""
+        xp, yp, wsp = (ctypes.c_void_p(self.x.data_ptr()), ctypes.c_void_p(self.y.data_ptr()),
+                       ctypes.c_void_p(self.ws.data_ptr()))
+        ptrs = [ctypes.c_void_p(c.data_ptr()) for c in self.copies]
+        n, k, nws = self.n, self.k, self.ws.numel()
+        one = ctypes.c_float(1.0)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        fn = lib.w2a8_gemv
+
+        def launch(slot):
+            rc = fn(ptrs[slot % len(ptrs)], xp, n, k, yp, None, one, None, wsp, nws, sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a8_gemv failed with status {rc}")
+        return launch
+
+
+def make_shapes(torch, w2a8, synth, specs, mode, dev):
+    total = sum(algo_bytes(n, k) for n, k, _, _ in specs)
+    slots = 1 if mode == "warm" else max(2, int(-(-ROTATE_BYTES // total)) + 1)
+    shapes = []
+    for n, k, seed, sparse in specs:
+        x, w = synth.gemv_case(n, k, seed, sparse=sparse)
+        shapes.append(Shape(torch, w2a8, n, k, x, w, slots, dev))
+        del w
+    torch.cuda.synchronize()
+    return shapes, slots
+
+
+def build_graphs(torch, shapes, lib, count, stream):
+    """One graph per step; step j reads copy j of every matrix."""
+    launchers = [s.launcher(lib, stream) for s in shapes]
+    graphs = []
+    with torch.cuda.stream(stream):
+        for l in launchers:       # eager warm-up (device query, code object load)
+            l(0)
+    torch.cuda.synchronize()
+    for j in range(count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for l in launchers:
+                l(j)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs, launchers
+
+
+def timed_steps(torch, graphs, launchers, steps, warmup, eager, stream):
+    """Warmup + timed steps.  Returns (host seconds, device us of the timed steps)."""
+    with torch.cuda.stream(stream):
+        for j in range(warmup):
+            if eager:
+                for l in launchers:
+                    l(j)
+            else:
+                graphs[j % len(graphs)].replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()                      # barrier (one rank)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for j in range(steps):
+            if eager:
+                for l in launchers:
+                    l(warmup + j)
+            else:
+                graphs[j].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, e0.elapsed_time(e1) * 1e3
+
+
+def kernel_times(torch, lib, shape, reps, stream, rounds=5):
+    """Device time per launch (us) of one shape: a graph of `reps` launches
+    (launch j reads copy j), replayed `rounds` times, two events per replay."""
+    l = shape.launcher(lib, stream)
+    with torch.cuda.stream(stream):
+        l(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for j in range(reps):
+            l(j)
+    out = []
+    for r in range(rounds + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        if r:                                      # first replay is a warm-up
+            out.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return out
+
+
+def host_call_us(torch, launcher, reps=50):
+    """Mean latency of one synchronised call (the page's timeit(50) style)."""
+    launcher(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(reps):
+        launcher(j)
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30):
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    ts.sort()
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / ts[len(ts) // 2] / 1e9
+
+
+def traffic_summary():
+    """Measured HBM bytes per launch from the committed counter summary, if the
+    GEMV kernel source is unchanged since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(GEMV_SRC, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("gemv_hip_sha256") != h:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(shapes, seconds=10.0):
+    """The oracle (plain C, one thread) on the same eight GEMVs, repeated for
+    about `seconds`; also checks the GPU's last outputs on sampled rows."""
+    import numpy as np
+
+    import oracle
+    import synth
+    import w2a8_gemv_amd as w2a8
+
+    ws = []
+    for s in shapes:
+        _, w = synth.gemv_case(s.n, s.k, s.seed, sparse=s.sparse)
+        ws.append(w)
+    # spot check: a sample of rows of every shape against the GPU result
+    ok = True
+    rng = np.random.default_rng(0)
+    for s, w in zip(shapes, ws):
+        rows = rng.choice(s.n, size=min(64, s.n), replace=False)
+        ref = oracle.gemm_i32(s.x_host, w[rows])
+        got = s.y.cpu().numpy()[rows]
+        ok = ok and bool(np.array_equal(ref, got))
+    del w2a8
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for s, w in zip(shapes, ws):
+            oracle.gemm_i32(s.x_host, w)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    total = sum(s.nbytes for s in shapes) * reps
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the 8 sweep GEMVs in full (int8 weights unpacked), repeated {reps} times "
+                      f"({dt:.1f} s), single thread; GB/s counts the same algorithmic bytes "
+                      f"N*K/4+K+4N per GEMV", "ms_per_sweep": round(dt / reps * 1e3, 3),
+            "gpu_rows_match": ok}
+
+
+def summarize_times(s, d):
+    import numpy as np
+    d = np.asarray(d, dtype=np.float64)
+    return {"n": s.n, "k": s.k, "bytes": s.nbytes, "mean_us": round(float(d.mean()), 3),
+            "median_us": round(float(np.median(d)), 3),
+            "p10_us": round(float(np.percentile(d, 10)), 3),
+            "p90_us": round(float(np.percentile(d, 90)), 3),
+            "GBps": round(s.nbytes / float(d.mean()) / 1e3, 1),
+            "pct_peak": round(100 * s.nbytes / float(d.mean()) / 1e3 / PEAK_HBM_GBPS, 1)}
+
+
+def main():
+    args = parse_args()
+    if args.traffic_summary:
+        print(json.dumps(write_traffic_summary(*args.traffic_summary), indent=1))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the W2A8 GEMV runs on a single MI355X and has no "
+              "multi-GPU path (row-sharding across GPUs is a design note only). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w2a8_gemv_amd as w2a8
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    lib = w2a8.lib()
+    stream = torch.cuda.Stream()
+
+    specs = [(n, k, seed, False) for (n, k), seed in zip(synth.SWEEP_SHAPES, synth.SWEEP_SEEDS)]
+    shapes, slots = make_shapes(torch, w2a8, synth, specs, args.mode, dev)
+    for s, (_, _, seed, sparse) in zip(shapes, specs):
+        s.seed, s.sparse = seed, sparse
+    graphs, launchers = [], [s.launcher(lib, stream) for s in shapes]
+    if not args.eager:
+        graphs, launchers = build_graphs(torch, shapes, lib, max(args.steps, 1), stream)
+    secs, region_us = timed_steps(torch, graphs, launchers, args.steps, args.warmup, args.eager,
+                                  stream)
+    step_bytes = sum(s.nbytes for s in shapes)
+    ms_per_step = secs * 1e3 / args.steps
+    value = step_bytes / (secs / args.steps) / 1e9
+    dev_us = region_us / args.steps                      # device time of one step
+    achieved = step_bytes / dev_us / 1e3                 # GB/s over all launches
+    traffic = traffic_summary()
+    per = [summarize_times(s, kernel_times(torch, lib, s, 24, stream)) for s in shapes]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "W2A8 GEMV M=1 over the 8 (N,K) shapes of the page's test script, "
+                        + ("cold weights (rotating copies)" if args.mode == "cold" else "warm"),
+            "shapes_nk": [[s.n, s.k] for s in shapes],
+            "weights": "ternary, P(-1)=P(0)=P(1)=1/3, 2-bit packed",
+            "activations": "int8 uniform [-127,127]",
+            "rotation_copies": slots,
+            "launch": "eager" if args.eager else "one hipGraph per step",
+            "bytes_per_step": step_bytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "w2a8::gemv_kernel (all launches of the timed region)",
+            "avg_launch_us": round(dev_us / len(shapes), 3),
+            "step_device_us": round(dev_us, 3),
+        },
+        "detail": {
+            "device": f"{props.name} {props.gcnArchName} {cus} CUs",
+            "per_shape_kernel_times": per,
+            "per_shape_method": "graph of 24 launches of one shape (rotating copies), "
+                                "device time / 24, 5 replays",
+            "plans": {f"{s.n}x{s.k}": list(w2a8.gemv_plan(s.n, s.k, cus)) for s in shapes},
+            "a100_page_us_context": {f"{n}x{k}": v for (n, k), v in A100_US.items()},
+        },
+    }
+
+    if not args.no_extra:
+        out["detail"]["host_call_us_mean50"] = {
+            f"{s.n}x{s.k}": round(host_call_us(torch, l), 2) for s, l in zip(shapes, launchers)}
+        # the two large shapes, cold then warm
+        large = []
+        lspecs = [(n, k, seed, True) for (n, k), seed in zip(synth.LARGE_SHAPES, synth.LARGE_SEEDS)]
+        for spec in lspecs:
+            for mode in ("cold", "warm"):
+                shp, sl = make_shapes(torch, w2a8, synth, [spec], mode, dev)
+                p = summarize_times(shp[0], kernel_times(torch, lib, shp[0], 24, stream))
+                p.update({"mode": mode, "rotation_copies": sl,
+                          "plan": list(w2a8.gemv_plan(spec[0], spec[1], cus))})
+                large.append(p)
+                del shp
+                torch.cuda.empty_cache()
+        out["detail"]["large_shapes"] = large
+        out["detail"]["device_copy_GBps_read_plus_write"] = round(copy_bandwidth(torch, dev), 1)
+
+    if args.calibrate_copy:
+        a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shapes)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

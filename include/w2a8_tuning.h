@@ -14,17 +14,24 @@
 extern "C" {
 #endif
 
-/* GEMV work split (w2a8_gemv).  Each 32-row strip of the packed matrix is
- * cut into S contiguous k-parts, one wave each, with S the smallest count
- * that gives about `waves_per_cu` waves per compute unit but no part
- * shorter than `min_tiles` 1 KiB tiles.  `unroll` (2, 4 or 8) is the number
- * of 16-byte loads each lane keeps in flight.  Returns W2A8_OK or
- * W2A8_ERR_VALUE for out-of-range knobs (1..64, >= 1, {2,4,8}). */
-int w2a8_tune_gemv(int waves_per_cu, int min_tiles, int unroll);
+/* GEMV launch plan (w2a8_gemv).  A 32-row strip with at least
+ * `split_min_tiles` k-tiles (1 KiB each) is split over workgroups, aiming at
+ * `wg_per_cu` workgroups per compute unit (1..64), never below
+ * `tiles_per_wave` tiles per workgroup, and never above `krange_tiles`
+ * (1..256) tiles per workgroup; split strips combine their partial sums
+ * through the workspace.  A workgroup splits its k-range over up to 16 waves
+ * with runs of about `tiles_per_wave` tiles (1..32).  Each wave keeps two
+ * load batches in flight; a batch is the smallest of 2, 4, 8 tiles whose two
+ * batches cover the run, but at most `unroll` (2, 4 or 8).  Returns W2A8_OK
+ * or W2A8_ERR_VALUE for out-of-range knobs. */
+int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_tiles,
+                   int split_min_tiles);
 
-/* The k-parts per strip S that w2a8_gemv would use for (N, K) on a device
- * with `cus` compute units under the current knobs (-1 if out of range). */
-int w2a8_gemv_split(int64_t N, int64_t K, int cus);
+/* The plan w2a8_gemv would use for (N, K) on a device with `cus` compute
+ * units under the current knobs: waves per workgroup, workgroups per strip
+ * and load batch.  Returns W2A8_OK, W2A8_ERR_NULL or W2A8_ERR_SHAPE. */
+int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
+                   int *unroll);
 
 #ifdef __cplusplus
 }

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol():
     expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
-                "w2a8_tune_gemv", "w2a8_gemv_split"}
+                "w2a8_tune_gemv", "w2a8_gemv_plan"}
     assert expected.issubset(set(names)), set(names) ^ expected
     L = ctypes.CDLL(w2a8.LIB_PATH)
     for n in names:
@@ -237,12 +237,37 @@ def test_workspace_formula():
 
 
 def test_tuning_knobs_validate():
+    for bad in [(0, 8, 4, 256, 64), (4, 0, 4, 256, 64), (4, 33, 4, 256, 64), (4, 8, 3, 256, 64),
+                (4, 8, 4, 257, 64), (4, 8, 4, 0, 64), (4, 8, 4, 256, 0), (65, 8, 4, 256, 64)]:
+        with pytest.raises(w2a8.W2A8Error):
+            w2a8.tune_gemv(*bad)
     with pytest.raises(w2a8.W2A8Error):
-        w2a8.tune_gemv(0, 8, 4)
-    with pytest.raises(w2a8.W2A8Error):
-        w2a8.tune_gemv(16, 8, 3)
-    assert w2a8.gemv_split(2560, 2560, 256) >= 1
-    assert w2a8.gemv_split(0, 2560, 256) == -1
+        w2a8.gemv_plan(0, 2560, 256)
+
+
+def test_gemv_plan_properties():
+    """The launch plan keeps every wave/workgroup within its documented bounds."""
+    pols = [w2a8.DEFAULT_GEMV_POLICY, (1, 32, 8, 256, 10 ** 6), (1, 1, 4, 256, 10 ** 6),
+            (64, 1, 8, 256, 1), (4, 4, 4, 3, 1), (16, 32, 2, 1, 1)]
+    try:
+        for pol in pols:
+            w2a8.tune_gemv(*pol)
+            for N in (1, 31, 2560, 55296):
+                for K in (1, 127, 128, 2560, 27648, 100000, 1048448):
+                    for cus in (1, 80, 256):
+                        wk, sg, u = w2a8.gemv_plan(N, K, cus)
+                        kt = -(-K // 128)
+                        ktw = -(-kt // sg)
+                        run = -(-ktw // wk)
+                        assert 1 <= sg <= kt and ktw <= pol[3]
+                        assert 1 <= wk <= 16 and wk <= ktw
+                        assert run <= 32                              # <= 4 staged chunks per lane
+                        assert wk * run * 128 + wk * 128 + 16 <= 64 * 1024  # LDS per workgroup
+                        assert u in (2, 4, 8) and u <= pol[2]
+                        if kt < pol[4] and kt <= pol[3]:
+                            assert sg == 1
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
 
 
 def test_binding_refuses_host_tensors_for_device_calls():

@@ -18,7 +18,7 @@ from gpu_util import dev, gemv_dev, packed_on_device, to_dev
 
 pytestmark = pytest.mark.gpu
 
-DEFAULT_POLICY = (16, 8, 4)
+DEFAULT_POLICY = w2a8.DEFAULT_GEMV_POLICY
 
 
 @pytest.fixture(autouse=True)
@@ -42,10 +42,19 @@ def test_gemv_small_ragged(N, K):
     np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
 
 
-@pytest.mark.parametrize("policy", [(1, 1, 2), (64, 1, 2), (64, 1, 8), (8, 4, 8), (4, 64, 4)])
+# (wg_per_cu, tiles_per_wave, unroll, krange_tiles, split_min_tiles): one
+# workgroup per strip with long multi-batch runs, one tile per wave, the
+# default, and strips split over 2..KT workgroups (the atomic path).
+NOSPLIT = 10 ** 6
+POLICIES = [(1, 32, 8, 256, NOSPLIT), (1, 32, 2, 256, NOSPLIT), (1, 1, 4, 256, NOSPLIT),
+            w2a8.DEFAULT_GEMV_POLICY, (64, 1, 8, 256, 1), (4, 4, 4, 3, NOSPLIT),
+            (2, 2, 8, 7, 1), (16, 32, 4, 1, 1), (8, 16, 8, 256, 1)]
+
+
+@pytest.mark.parametrize("policy", POLICIES)
 @pytest.mark.parametrize("N,K", [(33, 1000), (64, 2560), (200, 3200), (96, 27648)])
 def test_gemv_forced_splits(policy, N, K):
-    """Every split of the k-range (1 part up to 1 tile per part) and unroll."""
+    """Every way of splitting a strip's k-range over waves and workgroups."""
     w2a8.tune_gemv(*policy)
     x, w, wp, xd = _case(N, K, seed=7 + N + K)
     np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
@@ -149,8 +158,8 @@ def test_gemv_f32_only_output():
 
 def test_gemv_repeat_deterministic_and_workspace_reset():
     N, K = 2560, 6912
-    w2a8.tune_gemv(64, 1, 4)   # many k-parts per strip: exercises the atomics
-    assert w2a8.gemv_split(N, K, torch.cuda.get_device_properties(0).multi_processor_count) > 1
+    w2a8.tune_gemv(8, 4, 4, 256, 1)   # strips split over workgroups: exercises the atomics
+    assert w2a8.gemv_plan(N, K, torch.cuda.get_device_properties(0).multi_processor_count)[1] > 1
     x, w, wp, xd = _case(N, K, seed=31)
     ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
     ref = oracle.gemm_i32(x, w)
@@ -175,7 +184,7 @@ def test_gemv_graph_replays_match_eager():
     x, w, wp, xd = _case(N, K, seed=55)
     ref = oracle.gemm_i32(x, w)
     y = torch.empty(N, dtype=torch.int32, device=dev())
-    w2a8.tune_gemv(64, 1, 4)   # split path: workspace must be reset between replays
+    w2a8.tune_gemv(8, 4, 4, 256, 1)   # split path: workspace must be reset between replays
     s = torch.cuda.Stream()
     ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
     torch.cuda.synchronize()

@@ -32,9 +32,11 @@ int current_device(DeviceInfo *out);
 
 // Launch-shape knobs, settable through w2a8_tuning.h for measurements.
 struct GemvPolicy {
-    int waves_per_cu;    // target resident work-waves per CU
-    int min_tiles;       // smallest k-range (in 1 KiB tiles) of one wave
-    int unroll;          // tiles in flight per wave: 2, 4 or 8
+    int wg_per_cu;        // workgroups per CU to aim for when strips are split
+    int tiles_per_wave;   // target run of 1 KiB tiles per wave
+    int unroll;           // largest load batch in tiles (two in flight): 2, 4 or 8
+    int krange_tiles;     // at most this many k-tiles per workgroup
+    int split_min_tiles;  // split a strip over workgroups only if KT >= this
 };
 GemvPolicy &gemv_policy();
 
@@ -49,9 +51,14 @@ struct GemvLaunch {
     int32_t *ws_acc;
     uint32_t *ws_cnt;
     int N, K, KT, NS;
-    int S;        // k-parts per row strip
+    int WK;       // waves per workgroup, splitting its k-range
+    int SG;       // workgroups (k-ranges) per row strip
+    int RUN;      // longest run of tiles of one wave (<= 32)
     int unroll;
 };
+// Launch plan for (N, K) on `cus` compute units under the current policy.
+void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll);
+size_t gemv_lds_bytes(const GemvLaunch &a);
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,

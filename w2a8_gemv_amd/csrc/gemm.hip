@@ -222,15 +222,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // All exchanges are device-scope read-modify-write atomics (coherent
+    // across the XCDs' L2s); each wave waits for its own to complete before
+    // the barrier, so the ticket is taken after every partial sum has landed
+    // and no L2 writeback/invalidate fence is needed.
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int cidx = mb * a.NBLK + nb;
     if (tid == 0)
-        s_ticket = __hip_atomic_fetch_add(a.ws_cnt + cidx, 1u, __ATOMIC_ACQ_REL,
+        s_ticket = __hip_atomic_fetch_add(a.ws_cnt + cidx, 1u, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (s_ticket != uint32_t(a.S - 1)) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (active) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 }
     }
     if (tid == 0)
-        __hip_atomic_store(a.ws_cnt + cidx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_exchange(a.ws_cnt + cidx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

@@ -7,33 +7,43 @@
 // (the scale is multiplied back after the integer product).
 //
 // Design (gfx950, wave64):
-//  * Work unit = one wave.  The packed matrix is a sequence of 32-row strips,
-//    each a contiguous run of KT 1 KiB tiles.  Strip s is cut into S k-parts;
-//    wave (s, p) streams tiles [p*KT/S, (p+1)*KT/S) of strip s, so every wave
-//    reads one contiguous byte range with one 16-byte non-temporal load per
-//    lane per tile (a whole 1 KiB tile per wave instruction).
-//  * Lane l = 8*rg + kg holds rows 4rg..4rg+3 at k = 16kg..16kg+15 of a tile;
-//    it loads the matching 16 activation bytes (L1/L2 resident) once and uses
-//    them for its four rows.
+//  * A workgroup owns one 32-row strip (or, for very long K, one k-range of
+//    it) and splits its 1 KiB tiles over WK waves.  Each wave streams a
+//    contiguous run of tiles with one 16-byte non-temporal load per lane per
+//    tile and keeps up to 2*U tiles in flight; the loads are clamped rather
+//    than skipped at the end of the run so the steady state never waits for
+//    more than the batch it multiplies.
+//  * Each wave stages the activations of its own run into a private LDS
+//    region (zero-padded past K, so the ragged last tile needs no special
+//    case) and sums them on the way (sum_k x, used below); LDS accesses of one
+//    wave are ordered, so this needs no workgroup barrier.  The activation
+//    loads are issued before the weight loads, so staging waits only for
+//    them.
+//  * Lane l = 8*rg + kg holds rows 4rg..4rg+3 at k = 16kg..16kg+15 of a tile
+//    and reads the matching 16 activation bytes from LDS (a broadcast read).
 //  * Decode without sign handling: code c = w + 1 in {0,1,2}.  For a word,
 //    the masks 0x03030303, 0x0C0C0C0C, 0x30303030 and (word>>2)&0x30303030
 //    leave c, 4c, 16c, 16c in the four bytes, which v_dot4 multiplies with
 //    the four activation words; three accumulators (scales 1, 4, 16) are
-//    divided back exactly (every partial is a multiple of its scale).  Then
-//    sum_k w*x = sum_k c*x - sum_k x, with sum_k x taken once per wave over
-//    its k-range.
-//  * Reduction: the 8 lanes of a row group are summed with lane shuffles.
-//    S == 1: the wave owns the strip and stores y.  S > 1: int32 partials
-//    are added atomically into the workspace; the last wave of the strip (an
-//    arrival counter) reads the totals, resets workspace and counter, and
-//    applies the epilogue.  Integer addition makes the result independent of
-//    arrival order, so it is exact and deterministic.
+//    divided back exactly (each partial is a multiple of its scale), and
+//    sum_k w*x = sum_k c*x - sum_k x.
+//  * Reduction: DPP sums over the 8 lanes of a row group, then the WK waves
+//    combine through LDS (one barrier).  Only when a strip's k-range is split over several
+//    workgroups are int32 partials added atomically into the workspace; the
+//    last workgroup of the strip (an arrival counter) reads the totals,
+//    resets workspace and counter, and applies the epilogue.  Integer
+//    addition makes the result independent of arrival order: exact and
+//    deterministic.
 #include "common.h"
 
 namespace w2a8 {
 namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Activation chunks (16 bytes) staged per lane: a wave's run is at most
+// kXChunks * 64 / 8 = 32 tiles (the launch plan keeps RUN <= 32).
+constexpr int kXChunks = 4;
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4(int(a), int(b), c, false);
@@ -55,30 +65,13 @@ __device__ __forceinline__ void mac(const v4u w, const v4u xv, Acc &acc) {
     }
 }
 
-// 16 activation bytes at k0..k0+15; bytes at k >= kend read as 0.
-__device__ __forceinline__ v4u load_x16(const int8_t *x, int k0, int kend) {
-    if (k0 + 16 <= kend) return *reinterpret_cast<const v4u *>(x + k0);
-    uint32_t b[4] = {0u, 0u, 0u, 0u};
-    for (int i = 0; i < 16; ++i) {
-        const int k = k0 + i;
-        if (k < kend) b[i >> 2] |= uint32_t(uint8_t(x[k])) << (8 * (i & 3));
-    }
-    return v4u{b[0], b[1], b[2], b[3]};
-}
-
-// sum of x[k0..k1) over the wave (every lane gets the total).
-__device__ __forceinline__ int xsum_range(const int8_t *x, int k0, int k1, int lane) {
-    int s = 0;
-    for (int c = k0 + 16 * lane; c < k1; c += 1024) {
-        const v4u v = load_x16(x, c, k1);
-        s = dot4(v[0], 0x01010101u, s);
-        s = dot4(v[1], 0x01010101u, s);
-        s = dot4(v[2], 0x01010101u, s);
-        s = dot4(v[3], 0x01010101u, s);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    return s;
+// Sum over the 8 lanes of a row group (lanes 8j..8j+7) with DPP moves:
+// xor 1 and xor 2 inside quads, then the mirrored half-row (lane i <-> 7-i).
+__device__ __forceinline__ int sum8(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    return v;
 }
 
 __device__ __forceinline__ void store_out(const GemvLaunch &a, int row, int v) {
@@ -86,108 +79,192 @@ __device__ __forceinline__ void store_out(const GemvLaunch &a, int row, int v) {
     if (a.y_f32) a.y_f32[row] = (float(v) * a.sa[0]) * a.sw;
 }
 
+// Loads of batch b (tiles w0 + b*U + u, clamped to the run's last tile).
 template <int U>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvLaunch a) {
-    const int lane = threadIdx.x & 63;
-    // Wave-uniform values live in scalar registers.
-    const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 4 + (int(threadIdx.x) >> 6));
-    if (wave >= a.NS * a.S) return;
-    const int s = wave / a.S;
-    const int p = wave - s * a.S;
-    const int t0 = int((int64_t(p) * a.KT) / a.S);
-    const int t1 = int((int64_t(p + 1) * a.KT) / a.S);
+__device__ __forceinline__ void load_batch(const v4u *wt, int w0, int last, int b, v4u (&w)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        w[u] = __builtin_nontemporal_load(wt + min(w0 + b * U + u, last) * (kTileBytes / 16));
+    // Keep the loads here: the scheduler would otherwise sink them towards
+    // their uses and shorten the prefetch distance.
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Multiply batch b (only tiles inside the run) against the staged activations.
+template <int U>
+__device__ __forceinline__ void mac_batch(const v4u (&w)[U], const uint8_t *xl, int w0, int kt0,
+                                          int n, int b, int kg, Acc &acc) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (b * U + u < n) {
+            const int t = w0 + b * U + u;
+            const v4u xv = *reinterpret_cast<const v4u *>(xl + (t - kt0) * kTileK + 16 * kg);
+            mac(w[u], xv, acc);
+        }
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = int(blockIdx.x) / a.SG;             // row strip
+    const int g = int(blockIdx.x) - s * a.SG;         // k-range of the strip
+    const int kt0 = int(int64_t(g) * a.KT / a.SG);
+    const int kt1 = int(int64_t(g + 1) * a.KT / a.SG);
+    const int ntile = kt1 - kt0;
+    // this wave's run of tiles
+    const int w0 = kt0 + int(int64_t(wv) * ntile / a.WK);
+    const int w1 = kt0 + int(int64_t(wv + 1) * ntile / a.WK);
+    const int n = w1 - w0;
+    const int nb = (n + U - 1) / U;
     const int kg = lane & 7, rg = lane >> 3;
 
-    const uint32_t *wb = a.wp + int64_t(s) * a.KT * kTileWords + lane * 4;
-    const int8_t *xb = a.x + kg * 16;
+    // LDS: per-wave activation regions of RUN tiles, then the row partials.
+    uint8_t *xl = smem + wv * (a.RUN * kTileK);
+    int *red = reinterpret_cast<int *>(smem + a.WK * a.RUN * kTileK);   // WK*32 ints
+    uint32_t *ticket = reinterpret_cast<uint32_t *>(red + a.WK * kTileRows);
 
+    const v4u *wt = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords) + lane;
+    // Last tile a load may touch: the run's last tile, or (for an empty run)
+    // a tile of this strip, never past it.
+    const int last = min(max(w0, w1 - 1), a.KT - 1);
+
+    // 1. This wave's activation chunks (k in [w0*128, w1*128)) that lie
+    //    entirely below K, at most kXChunks per lane, loaded before the
+    //    weights so that staging waits only for them.  The one chunk that
+    //    straddles K (only when K % 16 != 0) is assembled byte by byte.
+    const int kbase = w0 * kTileK;
+    const int nchunk = n * (kTileK / 16);
+    v4u xr[kXChunks];
+#pragma unroll
+    for (int j = 0; j < kXChunks; ++j) {
+        const int c = lane + 64 * j;
+        xr[j] = v4u{0u, 0u, 0u, 0u};
+        if (c < nchunk && kbase + 16 * c + 16 <= a.K)
+            xr[j] = *reinterpret_cast<const v4u *>(a.x + kbase + 16 * c);
+    }
+    if ((a.K & 15) != 0) {
+#pragma unroll
+        for (int j = 0; j < kXChunks; ++j) {
+            const int c = lane + 64 * j;
+            const int k0 = kbase + 16 * c;
+            if (c < nchunk && k0 < a.K && k0 + 16 > a.K) {
+                uint32_t b4[4] = {0u, 0u, 0u, 0u};
+                for (int i = 0; i < 16; ++i)
+                    if (k0 + i < a.K)
+                        b4[i >> 2] |= uint32_t(uint8_t(a.x[k0 + i])) << (8 * (i & 3));
+                xr[j] = v4u{b4[0], b4[1], b4[2], b4[3]};
+            }
+        }
+    }
+
+    // 2. Two batches of weight loads in flight (clamped to the run, so the
+    //    count of outstanding loads is the same in every wave).
+    v4u wa[U], wb[U];
+    load_batch<U>(wt, w0, last, 0, wa);
+    load_batch<U>(wt, w0, last, 1, wb);
+
+    // 3. Stage the run's activations into the wave's LDS region and sum them.
+    int sx = 0;
+#pragma unroll
+    for (int j = 0; j < kXChunks; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunk) *reinterpret_cast<v4u *>(xl + 16 * c) = xr[j];
+        sx = dot4(xr[j][0], 0x01010101u, sx);
+        sx = dot4(xr[j][1], 0x01010101u, sx);
+        sx = dot4(xr[j][2], 0x01010101u, sx);
+        sx = dot4(xr[j][3], 0x01010101u, sx);
+    }
+    sx = sum8(sx);
+    sx += __shfl_xor(sx, 8);
+    sx += __shfl_xor(sx, 16);
+    sx += __shfl_xor(sx, 32);
+
+    // 4. Stream the run: multiply one batch while the next is in flight.
     Acc acc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc.a1[q] = acc.a4[q] = acc.a16[q] = 0;
-
-    // Tiles entirely below K need no activation bounds check.
-    const int tfull = min(t1, a.K / kTileK);
-    int t = t0;
-    for (; t + U <= tfull; t += U) {
-        v4u w[U], xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            w[u] = __builtin_nontemporal_load(
-                reinterpret_cast<const v4u *>(wb + int64_t(t + u) * kTileWords));
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            xv[u] = *reinterpret_cast<const v4u *>(xb + (t + u) * kTileK);
-#pragma unroll
-        for (int u = 0; u < U; ++u) mac(w[u], xv[u], acc);
-    }
-    for (; t < tfull; ++t) {
-        const v4u w = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u *>(wb + int64_t(t) * kTileWords));
-        const v4u xv = *reinterpret_cast<const v4u *>(xb + t * kTileK);
-        mac(w, xv, acc);
-    }
-    // The last tile of a strip may cross K: activations at k >= K read as 0
-    // (the packed codes there are 01, weight 0, and do not matter).
-    for (; t < t1; ++t) {
-        const v4u w = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u *>(wb + int64_t(t) * kTileWords));
-        const v4u xv = load_x16(a.x, t * kTileK + 16 * kg, a.K);
-        mac(w, xv, acc);
+    if (n > 0) {
+        int b = 0;
+        for (; b + 2 < nb; b += 2) {
+            mac_batch<U>(wa, xl, w0, w0, n, b, kg, acc);
+            load_batch<U>(wt, w0, last, b + 2, wa);
+            mac_batch<U>(wb, xl, w0, w0, n, b + 1, kg, acc);
+            load_batch<U>(wt, w0, last, b + 3, wb);
+        }
+        mac_batch<U>(wa, xl, w0, w0, n, b, kg, acc);
+        if (b + 1 < nb) mac_batch<U>(wb, xl, w0, w0, n, b + 1, kg, acc);
     }
 
+    // 5. Reduce: 8 lanes per row group (DPP); sum_k w*x = sum_k c*x - sum_k x
+    //    over the wave's run; then the WK waves via LDS.
     int r[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        int v = acc.a1[q] + (acc.a4[q] >> 2) + (acc.a16[q] >> 4);
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        r[q] = v;
-    }
-    const int sx = xsum_range(a.x, t0 * kTileK, min(t1 * kTileK, a.K), lane);
-
+    for (int q = 0; q < 4; ++q) r[q] = sum8(acc.a1[q] + (acc.a4[q] >> 2) + (acc.a16[q] >> 4));
     // Lane (rg, kg) with kg < 4 owns row 4rg + kg of the strip.
-    const int q = kg & 3;
-    const int v = (q == 0 ? r[0] : q == 1 ? r[1] : q == 2 ? r[2] : r[3]) - sx;
-    const int row = s * kTileRows + rg * 4 + q;
-    const bool owner = kg < 4;
+    const int mine = (kg == 0 ? r[0] : kg == 1 ? r[1] : kg == 2 ? r[2] : r[3]) - sx;
+    int tot = 0;
+    int row;
+    bool owner;
+    if (a.WK == 1) {
+        tot = mine;
+        row = s * kTileRows + rg * 4 + kg;
+        owner = kg < 4;
+    } else {
+        if (kg < 4) red[wv * kTileRows + rg * 4 + kg] = mine;
+        __syncthreads();
+        row = s * kTileRows + tid;
+        owner = tid < kTileRows;
+        if (owner)
+            for (int w = 0; w < a.WK; ++w) tot += red[w * kTileRows + tid];
+    }
 
-    if (a.S == 1) {
-        if (owner && row < a.N) store_out(a, row, v);
+    if (a.SG == 1) {
+        if (owner && row < a.N) store_out(a, row, tot);
         return;
     }
+    // k-range split over workgroups: every exchange goes through device-scope
+    // read-modify-write atomics (coherent across the XCDs' L2s); waiting for
+    // their completion orders the partial sums before the arrival ticket, so
+    // no L2 writeback/invalidate fence is needed.
     if (owner)
-        __hip_atomic_fetch_add(a.ws_acc + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    uint32_t ticket = 0;
-    if (lane == 0)
-        ticket = __hip_atomic_fetch_add(a.ws_cnt + s, 1u, __ATOMIC_ACQ_REL,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    ticket = uint32_t(__shfl(int(ticket), 0));
-    if (ticket != uint32_t(a.S - 1)) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_fetch_add(a.ws_acc + row, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        *ticket = __hip_atomic_fetch_add(a.ws_cnt + s, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*ticket != uint32_t(a.SG - 1)) return;
     if (owner) {
-        const int tot =
+        const int v =
             __hip_atomic_exchange(a.ws_acc + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (row < a.N) store_out(a, row, tot);
+        if (row < a.N) store_out(a, row, v);
     }
-    if (lane == 0)
-        __hip_atomic_store(a.ws_cnt + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+        __hip_atomic_exchange(a.ws_cnt + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
+size_t gemv_lds_bytes(const GemvLaunch &a) {
+    return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4 + 16;
+}
+
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream) {
-    const int64_t waves = int64_t(a.NS) * a.S;
-    const unsigned blocks = unsigned((waves + 3) / 4);
+    const unsigned blocks = unsigned(int64_t(a.NS) * a.SG);
     void *args[] = {const_cast<GemvLaunch *>(&a)};
     const void *fn;
     switch (a.unroll) {
     case 2: fn = reinterpret_cast<const void *>(&gemv_kernel<2>); break;
-    case 8: fn = reinterpret_cast<const void *>(&gemv_kernel<8>); break;
-    default: fn = reinterpret_cast<const void *>(&gemv_kernel<4>); break;
+    case 4: fn = reinterpret_cast<const void *>(&gemv_kernel<4>); break;
+    default: fn = reinterpret_cast<const void *>(&gemv_kernel<8>); break;
     }
-    return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * a.WK)), args, gemv_lds_bytes(a),
+                           stream);
 }
 
 }  // namespace w2a8

@@ -50,21 +50,41 @@ int current_device(DeviceInfo *out) {
 }
 
 GemvPolicy &gemv_policy() {
-    static GemvPolicy p = {16, 8, 4};
+    static GemvPolicy p = {4, 8, 8, 256, 128};
     return p;
 }
 
-// Split of a GEMV into work-waves: each 32-row strip is cut into S k-parts
-// of at least `min_tiles` tiles, S chosen so that NS*S waves cover the
-// device about `waves_per_cu` deep.  S == 1 needs no cross-wave reduction.
-static int gemv_parts(int64_t NS, int64_t KT, int cus) {
+// GEMV launch plan.
+//  * SG workgroups share a 32-row strip (each one k-range of ktw tiles).  A
+//    strip is split only when it is long (KT >= split_min_tiles): then the
+//    per-CU memory parallelism of all CUs is needed and the cost of combining
+//    partials through workspace atomics is small against the stream time.  The
+//    split aims at wg_per_cu workgroups per CU, keeps at least tiles_per_wave
+//    tiles per workgroup, and keeps ktw <= krange_tiles.
+//  * A workgroup splits its range over WK <= 16 waves with runs of about
+//    tiles_per_wave tiles (at most 32: each lane stages at most four 16-byte
+//    activation chunks).
+//  * The load batch U (two in flight per wave) is the smallest of 2, 4, 8
+//    (at most `unroll`) whose two batches cover the run.
+void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll) {
     const GemvPolicy &p = gemv_policy();
-    int64_t target = int64_t(cus) * std::max(1, p.waves_per_cu);
-    int64_t s = ceil_div(target, NS);
-    int64_t smax = std::max<int64_t>(1, KT / std::max(1, p.min_tiles));
-    s = std::min(s, smax);
-    s = std::max<int64_t>(1, std::min(s, KT));
-    return int(s);
+    const int64_t tpw = std::max(1, p.tiles_per_wave);
+    int64_t SG = ceil_div(KT, std::max(1, p.krange_tiles));
+    if (KT >= p.split_min_tiles) {
+        const int64_t want = ceil_div(int64_t(cus) * std::max(1, p.wg_per_cu), NS);
+        SG = std::max(SG, std::min(want, std::max<int64_t>(1, KT / tpw)));
+    }
+    SG = std::max<int64_t>(1, std::min(SG, KT));
+    const int64_t ktw = ceil_div(KT, SG);
+    int64_t WK = ceil_div(ktw, tpw);
+    WK = std::min<int64_t>(WK, std::min<int64_t>(16, ktw));
+    WK = std::max<int64_t>(WK, std::max<int64_t>(1, ceil_div(ktw, 32)));
+    const int64_t R = ceil_div(ktw, WK);
+    *wk = int(WK);
+    *sg = int(SG);
+    *run = int(R);
+    const int u = R <= 4 ? 2 : R <= 8 ? 4 : 8;
+    *unroll = std::min(u, p.unroll);
 }
 
 }  // namespace w2a8
@@ -243,8 +263,7 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
-    a.S = gemv_parts(a.NS, a.KT, dev.cus);
-    a.unroll = gemv_policy().unroll;
+    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
     hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
@@ -294,22 +313,30 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
 // ---------------------------------------------------------------------------
 // Tuning knobs (w2a8_tuning.h)
 // ---------------------------------------------------------------------------
-int w2a8_tune_gemv(int waves_per_cu, int min_tiles, int unroll) {
-    if (waves_per_cu < 1 || waves_per_cu > 64 || min_tiles < 1 ||
-        !(unroll == 2 || unroll == 4 || unroll == 8))
+int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_tiles,
+                   int split_min_tiles) {
+    if (wg_per_cu < 1 || wg_per_cu > 64 || tiles_per_wave < 1 || tiles_per_wave > 32 ||
+        !(unroll == 2 || unroll == 4 || unroll == 8) || krange_tiles < 1 || krange_tiles > 256 ||
+        split_min_tiles < 1)
         return W2A8_ERR_VALUE;
     GemvPolicy &p = gemv_policy();
-    p.waves_per_cu = waves_per_cu;
-    p.min_tiles = min_tiles;
+    p.wg_per_cu = wg_per_cu;
+    p.tiles_per_wave = tiles_per_wave;
     p.unroll = unroll;
+    p.krange_tiles = krange_tiles;
+    p.split_min_tiles = split_min_tiles;
     return W2A8_OK;
 }
 
-int w2a8_gemv_split(int64_t N, int64_t K, int cus) {
-    if (!nk_ok(N, K) || cus < 1) return -1;
+int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
+                   int *unroll) {
+    if (!waves_per_wg || !wgs_per_strip || !unroll) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K) || cus < 1) return W2A8_ERR_SHAPE;
     const int64_t NS = round_up(N, kTileRows) / kTileRows;
     const int64_t KT = round_up(K, kTileK) / kTileK;
-    return gemv_parts(NS, KT, cus);
+    int run = 0;
+    gemv_plan(NS, KT, cus, waves_per_wg, wgs_per_strip, &run, unroll);
+    return W2A8_OK;
 }
 
 }  // extern "C"

@@ -50,7 +50,18 @@ METRIC = "W2A8 GEMV us/call and cold-cache HBM GB/s (% of peak) per (N,K), M=1"
 PEAK_HBM_GBPS = 8000.0
 ROTATE_BYTES = 700e6          # > 256 MB Infinity Cache + 8 x 4 MB L2, with margin
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
-GEMV_SRC = os.path.join(ROOT, "w2a8_gemv_amd", "csrc", "gemv.hip")
+# Sources that decide what the GEMV kernel reads and writes: the kernel, its
+# shared helpers and the host-side launch plan.
+GEMV_SRCS = [os.path.join(ROOT, "w2a8_gemv_amd", "csrc", f)
+             for f in ("gemv.hip", "common.h", "host.hip")]
+
+
+def gemv_sources_sha256():
+    h = hashlib.sha256()
+    for path in GEMV_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 # The page's A100 40GB numbers for the same shapes (host-timed mean of 50
 # calls; another machine): context only.
@@ -110,18 +121,18 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
     wf, write = load(write_csv)
     shapes = []
     for n, k in synth.SWEEP_SHAPES:
-        wk, sg, _ = w2a8.gemv_plan(n, k, cus)
+        wk, sg, _, g = w2a8.gemv_plan(n, k, cus)
+        assert g == 0, "traffic summary expects the workgroup kernel"
         grid = (-(-n // 32)) * sg * 64 * wk
         f = sum(fetch[grid]) / len(fetch[grid]) * ff
         w = sum(write[grid]) / len(write[grid]) * wf
         shapes.append({"n": n, "k": k, "algorithmic_bytes": algo_bytes(n, k),
                        "fetch_bytes": round(f), "write_bytes": round(w),
                        "ratio": round((f + w) / algo_bytes(n, k), 4)})
-    with open(GEMV_SRC, "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
+    sha = gemv_sources_sha256()
     per_launch = sum(x["fetch_bytes"] + x["write_bytes"] for x in shapes) / len(shapes)
     algo = sum(x["algorithmic_bytes"] for x in shapes) / len(shapes)
-    out = {"gemv_hip_sha256": sha, "bytes_per_launch": round(per_launch),
+    out = {"gemv_sources_sha256": sha, "bytes_per_launch": round(per_launch),
            "algorithmic_bytes_per_launch": round(algo),
            "ratio": round(per_launch / algo, 4),
            "fetch_scale": round(ff, 5), "write_scale": round(wf, 5),
@@ -284,15 +295,15 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30):
 
 def traffic_summary():
     """Measured HBM bytes per launch from the committed counter summary, if the
-    GEMV kernel source is unchanged since the counters were taken."""
+    GEMV kernel sources (kernel, helpers, launch plan) are unchanged since the
+    counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(GEMV_SRC, "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()
+        h = gemv_sources_sha256()
     except (OSError, ValueError):
         return None
-    if t.get("gemv_hip_sha256") != h:
+    if t.get("gemv_sources_sha256") != h:
         return None
     return t.get("bytes_per_launch")
 

@@ -15,23 +15,34 @@ extern "C" {
 #endif
 
 /* GEMV launch plan (w2a8_gemv).  A 32-row strip with at least
- * `split_min_tiles` k-tiles (1 KiB each) is split over workgroups, aiming at
- * `wg_per_cu` workgroups per compute unit (1..64), never below
- * `tiles_per_wave` tiles per workgroup, and never above `krange_tiles`
- * (1..256) tiles per workgroup; split strips combine their partial sums
- * through the workspace.  A workgroup splits its k-range over up to 16 waves
- * with runs of about `tiles_per_wave` tiles (1..32).  Each wave keeps two
- * load batches in flight; a batch is the smallest of 2, 4, 8 tiles whose two
- * batches cover the run, but at most `unroll` (2, 4 or 8).  Returns W2A8_OK
- * or W2A8_ERR_VALUE for out-of-range knobs. */
+ * `split_min_tiles` k-tiles (1 KiB each) is split over workgroups: about one
+ * per `tiles_per_wave` tiles, at most 12, and more when there are too few
+ * strips to give `wg_per_cu` (1..64) workgroups per compute unit; never more
+ * than `krange_tiles` (1..256) tiles per workgroup.  Split strips combine
+ * their partial sums through the workspace.  A workgroup splits its k-range
+ * over up to 16 waves with runs of about `tiles_per_wave` tiles (1..32).
+ * Each wave keeps two load batches in flight; a batch is the smallest of 2,
+ * 4, 8 tiles whose two batches cover the run, but at most `unroll` (2, 4 or
+ * 8).  Defaults: (4, 6, 8, 256, 48).  Returns W2A8_OK or W2A8_ERR_VALUE for
+ * out-of-range knobs. */
 int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_tiles,
                    int split_min_tiles);
 
+/* Streaming GEMV for large matrices: used when the matrix has at least
+ * `min_tiles` 1 KiB tiles (0: never, the default) and 16 <= K <= 32768 (all
+ * activations fit in LDS).  The grid is CUs * `waves_per_cu` (1..64) long-lived waves, each
+ * streaming an equal contiguous share of the tiles with two load batches of
+ * `unroll` (2, 4 or 8) tiles in flight.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
+
 /* The plan w2a8_gemv would use for (N, K) on a device with `cus` compute
- * units under the current knobs: waves per workgroup, workgroups per strip
- * and load batch.  Returns W2A8_OK, W2A8_ERR_NULL or W2A8_ERR_SHAPE. */
+ * units under the current knobs.  Streaming kernel: *stream_waves = grid
+ * waves, *unroll = its batch, the other outputs 0.  Otherwise *stream_waves
+ * = 0 and waves per workgroup, workgroups per strip and load batch of the
+ * workgroup-split kernel.  Returns W2A8_OK, W2A8_ERR_NULL or
+ * W2A8_ERR_SHAPE. */
 int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
-                   int *unroll);
+                   int *unroll, int *stream_waves);
 
 #ifdef __cplusplus
 }

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol():
     expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
-                "w2a8_tune_gemv", "w2a8_gemv_plan"}
+                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemv_stream"}
     assert expected.issubset(set(names)), set(names) ^ expected
     L = ctypes.CDLL(w2a8.LIB_PATH)
     for n in names:
@@ -228,10 +228,10 @@ def test_quant_validation():
 
 
 def test_workspace_formula():
-    # GEMV: 4*Np + 4*NS bytes rounded up to 256
+    # GEMV: one 8-byte combining word per padded row, rounded up to 256 bytes
     for N in (1, 31, 32, 2560, 55296):
         Np = -(-N // 32) * 32
-        assert w2a8.workspace_bytes(1, N, 1000) == -(-(4 * Np + 4 * (Np // 32)) // 256) * 256
+        assert w2a8.workspace_bytes(1, N, 1000) == -(-(8 * Np) // 256) * 256
     # large batched outputs never split K: no workspace needed
     assert w2a8.workspace_bytes(512, 13824, 2560) == 0
 
@@ -243,6 +243,30 @@ def test_tuning_knobs_validate():
             w2a8.tune_gemv(*bad)
     with pytest.raises(w2a8.W2A8Error):
         w2a8.gemv_plan(0, 2560, 256)
+    for bad in [(-1, 4, 4), (1, 0, 4), (1, 65, 4), (1, 4, 3)]:
+        with pytest.raises(w2a8.W2A8Error):
+            w2a8.tune_gemv_stream(*bad)
+
+
+def test_gemv_stream_selection():
+    """The streaming kernel is off by default; when enabled it is chosen only
+    for large matrices whose K fits in LDS."""
+    try:
+        w2a8.tune_gemv_stream(*w2a8.DEFAULT_GEMV_STREAM_POLICY)
+        for N, K in [(55296, 5120), (5120, 27648), (2560, 2560), (1, 16)]:
+            assert w2a8.gemv_plan(N, K, 256)[3] == 0
+        w2a8.tune_gemv_stream(16384, 4, 4)
+        assert w2a8.gemv_plan(55296, 5120, 256)[3] > 0
+        assert w2a8.gemv_plan(5120, 27648, 256)[3] > 0
+        assert w2a8.gemv_plan(2560, 2560, 256)[3] == 0
+        assert w2a8.gemv_plan(4096, 40000, 256)[3] == 0     # K too long for the LDS stage
+        w2a8.tune_gemv_stream(0, 4, 4)
+        assert w2a8.gemv_plan(55296, 5120, 256)[3] == 0
+        w2a8.tune_gemv_stream(1, 4, 4)
+        assert w2a8.gemv_plan(1, 16, 256)[3] == 1
+        assert w2a8.gemv_plan(1, 15, 256)[3] == 0          # K below one 16-byte chunk
+    finally:
+        w2a8.tune_gemv_stream(*w2a8.DEFAULT_GEMV_STREAM_POLICY)
 
 
 def test_gemv_plan_properties():
@@ -255,7 +279,11 @@ def test_gemv_plan_properties():
             for N in (1, 31, 2560, 55296):
                 for K in (1, 127, 128, 2560, 27648, 100000, 1048448):
                     for cus in (1, 80, 256):
-                        wk, sg, u = w2a8.gemv_plan(N, K, cus)
+                        wk, sg, u, g = w2a8.gemv_plan(N, K, cus)
+                        if g:   # streaming plan
+                            assert 1 <= g <= max(1, -(-N // 32) * -(-K // 128))
+                            assert 16 <= K and -(-K // 128) * 8 <= 8 * 256   # K staged whole in LDS
+                            continue
                         kt = -(-K // 128)
                         ktw = -(-kt // sg)
                         run = -(-ktw // wk)

@@ -22,7 +22,8 @@ __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
-    "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY",
+    "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream",
+    "DEFAULT_GEMV_STREAM_POLICY",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw2a8.so")
@@ -74,7 +75,9 @@ def lib():
         L.w2a8_gemm.restype = I32
         L.w2a8_tune_gemv.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv.restype = I32
-        L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P]
+        L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
+        L.w2a8_tune_gemv_stream.argtypes = [I32, I32, I32]
+        L.w2a8_tune_gemv_stream.restype = I32
         L.w2a8_gemv_plan.restype = I32
         if L.w2a8_layout_version() != LAYOUT_VERSION:
             raise RuntimeError("libw2a8.so layout version does not match the binding")
@@ -303,18 +306,26 @@ def linear(x_bf16, w_packed, s_w, N, K, stream=None):
 # ---------------------------------------------------------------------------
 # tuning knobs (w2a8_tuning.h)
 # ---------------------------------------------------------------------------
-DEFAULT_GEMV_POLICY = (4, 8, 8, 256, 128)
+DEFAULT_GEMV_POLICY = (4, 6, 8, 256, 48)
 
 
 def tune_gemv(wg_per_cu: int, tiles_per_wave: int, unroll: int, krange_tiles: int = 256,
-              split_min_tiles: int = 128):
+              split_min_tiles: int = 48):
     _check(lib().w2a8_tune_gemv(wg_per_cu, tiles_per_wave, unroll, krange_tiles,
                                 split_min_tiles), "w2a8_tune_gemv")
 
 
+DEFAULT_GEMV_STREAM_POLICY = (0, 4, 4)
+
+
+def tune_gemv_stream(min_tiles: int, waves_per_cu: int, unroll: int):
+    _check(lib().w2a8_tune_gemv_stream(min_tiles, waves_per_cu, unroll), "w2a8_tune_gemv_stream")
+
+
 def gemv_plan(N: int, K: int, cus: int):
-    """(waves per workgroup, workgroups per strip, load batch) of w2a8_gemv."""
-    wk, sg, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib().w2a8_gemv_plan(N, K, cus, ctypes.byref(wk), ctypes.byref(sg), ctypes.byref(u)),
-           "w2a8_gemv_plan")
-    return wk.value, sg.value, u.value
+    """Launch plan of w2a8_gemv: (waves per workgroup, workgroups per strip,
+    load batch, streaming-grid waves); streaming plans are (0, 0, U, G)."""
+    wk, sg, u, g = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().w2a8_gemv_plan(N, K, cus, ctypes.byref(wk), ctypes.byref(sg), ctypes.byref(u),
+                                ctypes.byref(g)), "w2a8_gemv_plan")
+    return wk.value, sg.value, u.value, g.value

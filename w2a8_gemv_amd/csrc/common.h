@@ -37,6 +37,10 @@ struct GemvPolicy {
     int unroll;           // largest load batch in tiles (two in flight): 2, 4 or 8
     int krange_tiles;     // at most this many k-tiles per workgroup
     int split_min_tiles;  // split a strip over workgroups only if KT >= this
+    // streaming kernel (large matrices)
+    int stream_min_tiles;     // use it when N*K/4096 tiles >= this (0: never)
+    int stream_waves_per_cu;  // grid of CUs * this long-lived waves
+    int stream_unroll;        // load batch in tiles (two in flight): 2, 4 or 8
 };
 GemvPolicy &gemv_policy();
 
@@ -48,17 +52,53 @@ struct GemvLaunch {
     float *y_f32;
     const float *sa;
     float sw;
-    int32_t *ws_acc;
-    uint32_t *ws_cnt;
+    uint64_t *ws_row;   // split-k combining word per padded row (split_word)
     int N, K, KT, NS;
     int WK;       // waves per workgroup, splitting its k-range
     int SG;       // workgroups (k-ranges) per row strip
     int RUN;      // longest run of tiles of one wave (<= 32)
     int unroll;
+    int G;        // streaming kernel: waves in the grid (0: workgroup-split kernel)
+    int TQ, TR;   // streaming kernel: NS*KT = TQ*G + TR (wave w starts at w*TQ + min(w, TR))
 };
+// Split-k combining of a GEMV row with one device-scope atomic per
+// contribution.  Each contributor adds (its k-tile count << 40) + its partial
+// value to the row's 64-bit word.  The counts reach KT exactly with the last
+// contribution, whose returned total then holds the whole row value
+// (|value| <= K*127 < 2^27, far from the count field); that contributor
+// stores the row and clears the word.  Integer addition makes the result
+// independent of arrival order, and no ticket or fence is needed.
+constexpr int kCountShift = 40;
+__device__ __forceinline__ uint64_t split_word(int tiles, int val) {
+    return (uint64_t(uint32_t(tiles)) << kCountShift) + uint64_t(int64_t(val));
+}
+// Given the word's total after adding a contribution: true (with the row
+// value in *v, and the word cleared) when it was the last one.
+__device__ __forceinline__ bool split_done(uint64_t *word, uint64_t tot, int kt, int *v) {
+    const uint64_t cnt = (tot + (uint64_t(1) << (kCountShift - 1))) >> kCountShift;
+    if (cnt != uint64_t(uint32_t(kt))) return false;
+    *v = int(int64_t(tot - (uint64_t(uint32_t(kt)) << kCountShift)));
+    __hip_atomic_store(word, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+// Adds a contribution of `tiles` k-tiles; true (row value in *v) for the last.
+__device__ __forceinline__ bool split_add(uint64_t *word, int tiles, int val, int kt, int *v) {
+    const uint64_t add = split_word(tiles, val);
+    return split_done(
+        word, __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add,
+        kt, v);
+}
+
 // Launch plan for (N, K) on `cus` compute units under the current policy.
 void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll);
 size_t gemv_lds_bytes(const GemvLaunch &a);
+// Streaming kernel for large matrices (gemv_stream.hip).
+bool gemv_stream_fits(int64_t K);
+size_t gemv_stream_lds_bytes(const GemvLaunch &a);
+hipError_t launch_gemv_stream(const GemvLaunch &a, hipStream_t stream);
+// Full plan: G > 0 selects the streaming kernel (then wk = sg = run = 0).
+void gemv_plan_full(int64_t NS, int64_t K, int cus, int *wk, int *sg, int *run, int *unroll,
+                    int *g);
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,

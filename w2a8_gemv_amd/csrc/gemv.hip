@@ -125,7 +125,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     // LDS: per-wave activation regions of RUN tiles, then the row partials.
     uint8_t *xl = smem + wv * (a.RUN * kTileK);
     int *red = reinterpret_cast<int *>(smem + a.WK * a.RUN * kTileK);   // WK*32 ints
-    uint32_t *ticket = reinterpret_cast<uint32_t *>(red + a.WK * kTileRows);
 
     const v4u *wt = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords) + lane;
     // Last tile a load may touch: the run's last tile, or (for an empty run)
@@ -226,32 +225,18 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
         if (owner && row < a.N) store_out(a, row, tot);
         return;
     }
-    // k-range split over workgroups: every exchange goes through device-scope
-    // read-modify-write atomics (coherent across the XCDs' L2s); waiting for
-    // their completion orders the partial sums before the arrival ticket, so
-    // no L2 writeback/invalidate fence is needed.
-    if (owner)
-        __hip_atomic_fetch_add(a.ws_acc + row, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0)
-        *ticket = __hip_atomic_fetch_add(a.ws_cnt + s, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (*ticket != uint32_t(a.SG - 1)) return;
-    if (owner) {
-        const int v =
-            __hip_atomic_exchange(a.ws_acc + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (row < a.N) store_out(a, row, v);
-    }
-    if (tid == 0)
-        __hip_atomic_exchange(a.ws_cnt + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // k-range split over workgroups: one device-scope atomic per row (coherent
+    // across the XCDs' L2s) combines the partials; the last contributor of a
+    // row stores it.
+    int v;
+    if (owner && split_add(a.ws_row + row, ntile, tot, a.KT, &v) && row < a.N)
+        store_out(a, row, v);
 }
 
 }  // namespace
 
 size_t gemv_lds_bytes(const GemvLaunch &a) {
-    return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4 + 16;
+    return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4;
 }
 
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream) {

@@ -50,20 +50,28 @@ int current_device(DeviceInfo *out) {
 }
 
 GemvPolicy &gemv_policy() {
-    static GemvPolicy p = {4, 8, 8, 256, 128};
+    // Streaming kernel off by default (stream_min_tiles 0): on gfx950 the
+    // workgroup kernel is as fast or faster on every measured shape.
+    static GemvPolicy p = {4, 6, 8, 256, 48, 0, 4, 4};
     return p;
 }
 
+// Most workgroups a long strip is split into by default: more only for
+// parallelism when there are few strips (each extra workgroup adds one atomic
+// contribution per row).
+constexpr int64_t kSplitWgs = 12;
+
 // GEMV launch plan.
 //  * SG workgroups share a 32-row strip (each one k-range of ktw tiles).  A
-//    strip is split only when it is long (KT >= split_min_tiles): then the
-//    per-CU memory parallelism of all CUs is needed and the cost of combining
-//    partials through workspace atomics is small against the stream time.  The
-//    split aims at wg_per_cu workgroups per CU, keeps at least tiles_per_wave
-//    tiles per workgroup, and keeps ktw <= krange_tiles.
+//    strip is split when it is long (KT >= split_min_tiles): into about one
+//    workgroup per tiles_per_wave tiles, at most kSplitWgs, and into more
+//    when there are too few strips to give wg_per_cu workgroups per CU.
+//    Partials are combined with one device-scope atomic per row.
+//    ktw <= krange_tiles always.
 //  * A workgroup splits its range over WK <= 16 waves with runs of about
-//    tiles_per_wave tiles (at most 32: each lane stages at most four 16-byte
-//    activation chunks).
+//    tiles_per_wave tiles (tiles_per_wave + 2 in a split strip; at most 32:
+//    each lane stages at most four 16-byte activation chunks); their row sums
+//    are combined through LDS.
 //  * The load batch U (two in flight per wave) is the smallest of 2, 4, 8
 //    (at most `unroll`) whose two batches cover the run.
 void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll) {
@@ -71,12 +79,19 @@ void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int 
     const int64_t tpw = std::max(1, p.tiles_per_wave);
     int64_t SG = ceil_div(KT, std::max(1, p.krange_tiles));
     if (KT >= p.split_min_tiles) {
+        SG = std::max(SG, std::min(ceil_div(KT, tpw), kSplitWgs));
         const int64_t want = ceil_div(int64_t(cus) * std::max(1, p.wg_per_cu), NS);
         SG = std::max(SG, std::min(want, std::max<int64_t>(1, KT / tpw)));
     }
     SG = std::max<int64_t>(1, std::min(SG, KT));
     const int64_t ktw = ceil_div(KT, SG);
-    int64_t WK = ceil_div(ktw, tpw);
+    // Runs of a split strip may be a little longer: its extra waves cost an
+    // LDS combine on top of the atomic one.
+    int64_t WK = ceil_div(ktw, SG > 1 ? tpw + 2 : tpw);
+    // An unsplit strip with more than two waves: a multiple of four, so the
+    // workgroup spreads evenly over the compute unit's four SIMDs (5 or 7
+    // waves measured slower than 4 or 8).
+    if (SG == 1 && WK >= 3) WK = 4 * ((WK + 2) / 4);
     WK = std::min<int64_t>(WK, std::min<int64_t>(16, ktw));
     WK = std::max<int64_t>(WK, std::max<int64_t>(1, ceil_div(ktw, 32)));
     const int64_t R = ceil_div(ktw, WK);
@@ -85,6 +100,27 @@ void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int 
     *run = int(R);
     const int u = R <= 4 ? 2 : R <= 8 ? 4 : 8;
     *unroll = std::min(u, p.unroll);
+}
+
+// Large matrices (at least stream_min_tiles tiles, K staged whole in LDS)
+// use the streaming kernel: a grid of CUs * stream_waves_per_cu long-lived
+// waves, each streaming an equal contiguous share of the tiles.
+void gemv_plan_full(int64_t NS, int64_t K, int cus, int *wk, int *sg, int *run, int *unroll,
+                    int *g) {
+    const GemvPolicy &p = gemv_policy();
+    const int64_t KT = ceil_div(K, kTileK);
+    const int64_t T = NS * KT;
+    // (Tile indices are 32-bit in the streaming kernel: T < 2^30 is 1 TiB of weights.)
+    if (p.stream_min_tiles > 0 && T >= p.stream_min_tiles && T < (int64_t(1) << 30) &&
+        gemv_stream_fits(K)) {
+        const int64_t G = std::min<int64_t>(T, int64_t(cus) * p.stream_waves_per_cu);
+        *wk = *sg = *run = 0;
+        *unroll = p.stream_unroll;
+        *g = int(std::max<int64_t>(1, G));
+        return;
+    }
+    *g = 0;
+    gemv_plan(NS, KT, cus, wk, sg, run, unroll);
 }
 
 }  // namespace w2a8
@@ -121,8 +157,8 @@ int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t NS = Np / kTileRows;
     int64_t bytes = 0;
     if (M == 1) {
-        // GEMV: int32 partial per padded row + one arrival counter per strip.
-        bytes = 4 * Np + 4 * NS;
+        // GEMV: one 64-bit split-k combining word per padded row.
+        bytes = 8 * Np;
     } else if (M * Np <= kGemmSplitMaxOut) {
         // GEMM split-K: int32 partial per output + one counter per
         // (m-block of >= 16 rows, n-block of 4 strips).
@@ -257,14 +293,14 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.y_f32 = y_f32;
     a.sa = s_a;
     a.sw = s_w;
-    a.ws_acc = static_cast<int32_t *>(workspace);
-    a.ws_cnt = reinterpret_cast<uint32_t *>(a.ws_acc + Np);
+    a.ws_row = static_cast<uint64_t *>(workspace);
     a.N = int(N);
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
-    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
-    hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
+    gemv_plan_full(a.NS, K, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll, &a.G);
+    hipError_t e = a.G > 0 ? launch_gemv_stream(a, static_cast<hipStream_t>(stream))
+                           : launch_gemv(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 
@@ -329,13 +365,24 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
 }
 
 int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
-                   int *unroll) {
-    if (!waves_per_wg || !wgs_per_strip || !unroll) return W2A8_ERR_NULL;
+                   int *unroll, int *stream_waves) {
+    if (!waves_per_wg || !wgs_per_strip || !unroll || !stream_waves) return W2A8_ERR_NULL;
     if (!nk_ok(N, K) || cus < 1) return W2A8_ERR_SHAPE;
     const int64_t NS = round_up(N, kTileRows) / kTileRows;
     const int64_t KT = round_up(K, kTileK) / kTileK;
     int run = 0;
-    gemv_plan(NS, KT, cus, waves_per_wg, wgs_per_strip, &run, unroll);
+    gemv_plan_full(NS, K, cus, waves_per_wg, wgs_per_strip, &run, unroll, stream_waves);
+    return W2A8_OK;
+}
+
+int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll) {
+    if (min_tiles < 0 || waves_per_cu < 1 || waves_per_cu > 64 ||
+        !(unroll == 2 || unroll == 4 || unroll == 8))
+        return W2A8_ERR_VALUE;
+    GemvPolicy &p = gemv_policy();
+    p.stream_min_tiles = min_tiles;
+    p.stream_waves_per_cu = waves_per_cu;
+    p.stream_unroll = unroll;
     return W2A8_OK;
 }
 

@@ -60,6 +60,11 @@ struct GemvLaunch {
     int unroll;
     int G;        // streaming kernel: waves in the grid (0: workgroup-split kernel)
     int TQ, TR;   // streaming kernel: NS*KT = TQ*G + TR (wave w starts at w*TQ + min(w, TR))
+    // Workgroup kernel, set by its launcher so that the kernel divides
+    // nothing: KT = KQ*SG + KR (k-range g starts at g*KQ + min(g, KR) and has
+    // KQ + (g < KR) tiles), and a range of KQ + i tiles = WQi*WK + WRi (wave
+    // v starts v*WQi + min(v, WRi) tiles in).
+    int KQ, KR, WQ0, WR0, WQ1, WR1;
 };
 // Split-k combining of a GEMV row with one device-scope atomic per
 // contribution.  Each contributor adds (its k-tile count << 40) + its partial

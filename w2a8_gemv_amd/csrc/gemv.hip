@@ -28,12 +28,11 @@
 //    divided back exactly (each partial is a multiple of its scale), and
 //    sum_k w*x = sum_k c*x - sum_k x.
 //  * Reduction: DPP sums over the 8 lanes of a row group, then the WK waves
-//    combine through LDS (one barrier).  Only when a strip's k-range is split over several
-//    workgroups are int32 partials added atomically into the workspace; the
-//    last workgroup of the strip (an arrival counter) reads the totals,
-//    resets workspace and counter, and applies the epilogue.  Integer
-//    addition makes the result independent of arrival order: exact and
-//    deterministic.
+//    combine through LDS (one barrier).  Only when a strip's k-range is split
+//    over several workgroups do the rows go through the workspace, one
+//    device-scope atomic per row and workgroup (split_add in common.h); the
+//    last contributor of a row stores it with the epilogue.  Integer addition
+//    makes the result independent of arrival order: exact and deterministic.
 #include "common.h"
 
 namespace w2a8 {
@@ -110,15 +109,19 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int s = int(blockIdx.x) / a.SG;             // row strip
-    const int g = int(blockIdx.x) - s * a.SG;         // k-range of the strip
-    const int kt0 = int(int64_t(g) * a.KT / a.SG);
-    const int kt1 = int(int64_t(g + 1) * a.KT / a.SG);
-    const int ntile = kt1 - kt0;
-    // this wave's run of tiles
-    const int w0 = kt0 + int(int64_t(wv) * ntile / a.WK);
-    const int w1 = kt0 + int(int64_t(wv + 1) * ntile / a.WK);
-    const int n = w1 - w0;
+    // Strip s, k-range g of it, and this wave's run of tiles, from quotients
+    // and remainders the launcher computed: a division here (64-bit, in
+    // software) would cost hundreds of scalar instructions before the first
+    // load.
+    const int s = int(blockIdx.x);
+    const int g = int(blockIdx.y);
+    const bool big = g < a.KR;
+    const int kt0 = g * a.KQ + min(g, a.KR);
+    const int ntile = a.KQ + (big ? 1 : 0);
+    const int wq = big ? a.WQ1 : a.WQ0, wr = big ? a.WR1 : a.WR0;
+    const int w0 = kt0 + wv * wq + min(wv, wr);
+    const int n = wq + (wv < wr ? 1 : 0);
+    const int w1 = w0 + n;
     const int nb = (n + U - 1) / U;
     const int kg = lane & 7, rg = lane >> 3;
 
@@ -239,17 +242,24 @@ size_t gemv_lds_bytes(const GemvLaunch &a) {
     return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4;
 }
 
-hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream) {
-    const unsigned blocks = unsigned(int64_t(a.NS) * a.SG);
-    void *args[] = {const_cast<GemvLaunch *>(&a)};
+hipError_t launch_gemv(const GemvLaunch &la, hipStream_t stream) {
+    GemvLaunch a = la;
+    a.KQ = a.KT / a.SG;
+    a.KR = a.KT % a.SG;
+    a.WQ0 = a.KQ / a.WK;
+    a.WR0 = a.KQ % a.WK;
+    a.WQ1 = (a.KQ + 1) / a.WK;
+    a.WR1 = (a.KQ + 1) % a.WK;
+    void *args[] = {&a};
     const void *fn;
     switch (a.unroll) {
     case 2: fn = reinterpret_cast<const void *>(&gemv_kernel<2>); break;
     case 4: fn = reinterpret_cast<const void *>(&gemv_kernel<4>); break;
     default: fn = reinterpret_cast<const void *>(&gemv_kernel<8>); break;
     }
-    return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * a.WK)), args, gemv_lds_bytes(a),
-                           stream);
+    // x: strip, y: k-range of the strip.
+    return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
+                           args, gemv_lds_bytes(a), stream);
 }
 
 }  // namespace w2a8

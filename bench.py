@@ -48,6 +48,7 @@ if ROOT not in sys.path:
 
 METRIC = "W2A8 GEMV us/call and cold-cache HBM GB/s (% of peak) per (N,K), M=1"
 PEAK_HBM_GBPS = 8000.0
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, 5.0 POPS
 ROTATE_BYTES = 700e6          # > 256 MB Infinity Cache + 8 x 4 MB L2, with margin
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
 # Sources that decide what the GEMV kernel reads and writes: the kernel, its
@@ -263,6 +264,132 @@ def kernel_times(torch, lib, shape, reps, stream, rounds=5):
     return out
 
 
+def graph_times(torch, launch, reps, stream, rounds=5):
+    """Device time per call (us): a graph of `reps` calls launch(0..reps-1),
+    replayed `rounds` times after one warm-up replay, two events per replay."""
+    with torch.cuda.stream(stream):
+        launch(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for j in range(reps):
+            launch(j)
+    out = []
+    for r in range(rounds + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            out.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return out
+
+
+def rotation(torch, wp, nbytes):
+    """Copies of a packed matrix so that one graph of launches reads cold weights."""
+    slots = max(2, int(-(-ROTATE_BYTES // max(1, nbytes))) + 1)
+    return [wp] + [wp.clone() for _ in range(slots - 1)]
+
+
+def gemm_extras(torch, w2a8, synth, lib, stream, cus):
+    """The batched product on the prefill configs (M in GEMM_MS x GEMM_SHAPES),
+    cold weights: int8 TOPS against the dense int8 MFMA peak, and GB/s."""
+    out = []
+    vp = ctypes.c_void_p
+    for n, k in synth.GEMM_SHAPES:
+        for m in synth.GEMM_MS:
+            x, w = synth.gemm_case(m, n, k, synth.GEMM_SEEDS[((n, k), m)])
+            wp = w2a8.pack_ternary(torch.from_numpy(w)).to(stream.device)
+            copies = rotation(torch, wp, wp.numel())
+            xd = torch.from_numpy(x).to(stream.device)
+            y = torch.empty((m, n), dtype=torch.int32, device=stream.device)
+            ws = torch.zeros(max(256, w2a8.workspace_bytes(m, n, k)), dtype=torch.uint8,
+                             device=stream.device)
+            ptrs = [vp(c.data_ptr()) for c in copies]
+            args = (vp(xd.data_ptr()), m, n, k, vp(y.data_ptr()), None, ctypes.c_float(1.0),
+                    None, vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))
+
+            def launch(j, ptrs=ptrs, args=args):
+                rc = lib.w2a8_gemm(ptrs[j % len(ptrs)], *args)
+                if rc != 0:
+                    raise RuntimeError(f"w2a8_gemm failed with status {rc}")
+            ts = graph_times(torch, launch, 12, stream)
+            med = sorted(ts)[len(ts) // 2]
+            ops = 2 * m * n * k
+            nbytes = n * k // 4 + m * k + 4 * m * n
+            out.append({"m": m, "n": n, "k": k, "median_us": round(med, 3),
+                        "mean_us": round(sum(ts) / len(ts), 3),
+                        "TOPS": round(ops / med / 1e6, 1),
+                        "pct_int8_peak": round(100 * ops / med / 1e6 / PEAK_INT8_TOPS, 1),
+                        "GBps": round(nbytes / med / 1e3, 1),
+                        "pct_hbm_peak": round(100 * nbytes / med / 1e3 / PEAK_HBM_GBPS, 1),
+                        "rotation_copies": len(copies)})
+            del copies, wp, xd, y, ws
+            torch.cuda.empty_cache()
+    return out
+
+
+def linear_extras(torch, w2a8, synth, lib, stream):
+    """Activation quantizer alone, and the whole linear layer (quantize, then
+    GEMV or GEMM with the fp32 epilogue) on the 13824 x 2560 layer, M = 1 and
+    128, cold weights."""
+    import numpy as np
+    vp = ctypes.c_void_p
+    n, k = 13824, 2560
+    out = {}
+    for m in (1, 128):
+        xb, W = synth.linear_case(m, n, k, synth.LINEAR_SEEDS[m])
+        wq, sw = w2a8.ternarize_absmean(torch.from_numpy(W))
+        del W
+        wp = w2a8.pack_ternary(wq).to(stream.device)
+        copies = rotation(torch, wp, wp.numel())
+        xd = torch.from_numpy(xb.view(np.int16)).to(stream.device)
+        xq = torch.empty((m, k), dtype=torch.int8, device=stream.device)
+        sa = torch.empty(m, dtype=torch.float32, device=stream.device)
+        y = torch.empty((m, n), dtype=torch.float32, device=stream.device)
+        ws = torch.zeros(max(256, w2a8.workspace_bytes(m, n, k)), dtype=torch.uint8,
+                         device=stream.device)
+        sp = vp(stream.cuda_stream)
+        ptrs = [vp(c.data_ptr()) for c in copies]
+
+        def quant(j):
+            rc = lib.quant_act_int8(vp(xd.data_ptr()), m, k, vp(xq.data_ptr()),
+                                    vp(sa.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"quant_act_int8 failed with status {rc}")
+
+        def layer(j):
+            quant(j)
+            if m == 1:
+                rc = lib.w2a8_gemv(ptrs[j % len(ptrs)], vp(xq.data_ptr()), n, k, None,
+                                   vp(sa.data_ptr()), ctypes.c_float(float(sw)),
+                                   vp(y.data_ptr()), vp(ws.data_ptr()), ws.numel(), sp)
+            else:
+                rc = lib.w2a8_gemm(ptrs[j % len(ptrs)], vp(xq.data_ptr()), m, n, k, None,
+                                   vp(sa.data_ptr()), ctypes.c_float(float(sw)),
+                                   vp(y.data_ptr()), vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"linear product failed with status {rc}")
+        tq = graph_times(torch, quant, 24, stream)
+        tl = graph_times(torch, layer, 12, stream)
+        mq, ml = sorted(tq)[len(tq) // 2], sorted(tl)[len(tl) // 2]
+        qbytes = 3 * m * k + 4 * m
+        lbytes = qbytes + n * k // 4 + m * k + 4 * m * n + 4 * m
+        out[f"M={m}"] = {"quant_median_us": round(mq, 3),
+                         "quant_GBps": round(qbytes / mq / 1e3, 1),
+                         "layer_median_us": round(ml, 3),
+                         "layer_GBps": round(lbytes / ml / 1e3, 1),
+                         "layer_bytes": lbytes,
+                         "layer": "quant_act_int8 + " + ("w2a8_gemv" if m == 1 else "w2a8_gemm")
+                                  + " with fp32 epilogue, 13824 x 2560, two launches"}
+        del copies, wp, xd, xq, sa, y, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def host_call_us(torch, launcher, reps=50):
     """Mean latency of one synchronised call (the page's timeit(50) style)."""
     launcher(0)
@@ -460,6 +587,9 @@ def main():
                 torch.cuda.empty_cache()
         out["detail"]["large_shapes"] = large
         out["detail"]["device_copy_GBps_read_plus_write"] = round(copy_bandwidth(torch, dev), 1)
+        out["detail"]["gemm"] = gemm_extras(torch, w2a8, synth, lib, stream, cus)
+        out["detail"]["gemm_peak_int8_TOPS"] = PEAK_INT8_TOPS
+        out["detail"]["linear_13824x2560"] = linear_extras(torch, w2a8, synth, lib, stream)
 
     if args.calibrate_copy:
         a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)

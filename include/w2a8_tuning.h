@@ -35,6 +35,12 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
  * `unroll` (2, 4 or 8) tiles in flight.  Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
 
+/* Batched product kernel (w2a8_gemm): 0 = automatic (default), 1 = the
+ * pipelined kernel whenever K is a multiple of 16 (it never splits K), 2 = the
+ * general kernel (split-K for small outputs) always.  Returns W2A8_OK or
+ * W2A8_ERR_VALUE. */
+int w2a8_tune_gemm(int kernel);
+
 /* The plan w2a8_gemv would use for (N, K) on a device with `cus` compute
  * units under the current knobs.  Streaming kernel: *stream_waves = grid
  * waves, *unroll = its batch, the other outputs 0.  Otherwise *stream_waves

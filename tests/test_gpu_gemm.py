@@ -17,6 +17,12 @@ from gpu_util import CANARY_I32, GUARD, check_guard, dev, packed_on_device, to_d
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True)
+def _restore_gemm_kernel():
+    yield
+    w2a8.tune_gemm(0)
+
+
 def _gemm_dev(wp, xd, M, N, K, sa=None, sw=1.0, want_f32=False):
     y = torch.full((M * N + GUARD,), CANARY_I32, dtype=torch.int32, device=dev())
     yf = None
@@ -43,6 +49,38 @@ def test_gemm_small_ragged(M, N, K):
     x, w = synth.gemm_case(M, N, K, seed=M + 10 * N + 100 * K)
     y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
     np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+
+
+# Each kernel forced onto ragged shapes: every pipelined configuration
+# (M <= 32, <= 64, <= 128, larger), K below one ring of tiles (K = 16, 144),
+# a k-tile remainder (KT % 4 = 1, 2, 3), a partial last tile (K = 1040) and
+# ragged N (strips past the matrix, rows past N in the last strip).
+FORCED = [(8, 1000, 1040), (33, 100, 16), (64, 2560, 144), (100, 97, 2560), (128, 200, 384),
+          (200, 1000, 1040), (257, 33, 3200), (2, 4096, 896), (17, 130, 640)]
+
+
+@pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
+@pytest.mark.parametrize("M,N,K", FORCED + [s for s in SMALL if s[2] % 16 == 0])
+def test_gemm_forced_kernel(kernel, M, N, K):
+    w2a8.tune_gemm(kernel)
+    x, w = synth.gemm_case(M, N, K, seed=7 * M + 3 * N + K)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+
+
+@pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
+def test_gemm_forced_kernel_fp32_epilogue(kernel):
+    w2a8.tune_gemm(kernel)
+    M, N, K = 150, 700, 1024
+    x, w = synth.gemm_case(M, N, K, seed=99)
+    rng = np.random.default_rng(5)
+    sa = (rng.random(M, dtype=np.float32) * 0.05 + 1e-3).astype(np.float32)
+    sw = np.float32(0.0173)
+    yi, yf = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K, sa=to_dev(sa), sw=float(sw),
+                       want_f32=True)
+    acc = oracle.gemm_i32(x, w)
+    np.testing.assert_array_equal(yi, acc)
+    np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw))
 
 
 @pytest.mark.parametrize("key", list(synth.GEMM_SEEDS.keys()),

@@ -22,7 +22,7 @@ __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
-    "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream",
+    "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream", "tune_gemm",
     "DEFAULT_GEMV_STREAM_POLICY",
 ]
 
@@ -78,6 +78,8 @@ def lib():
         L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
         L.w2a8_tune_gemv_stream.argtypes = [I32, I32, I32]
         L.w2a8_tune_gemv_stream.restype = I32
+        L.w2a8_tune_gemm.argtypes = [I32]
+        L.w2a8_tune_gemm.restype = I32
         L.w2a8_gemv_plan.restype = I32
         if L.w2a8_layout_version() != LAYOUT_VERSION:
             raise RuntimeError("libw2a8.so layout version does not match the binding")
@@ -320,6 +322,11 @@ DEFAULT_GEMV_STREAM_POLICY = (0, 4, 4)
 
 def tune_gemv_stream(min_tiles: int, waves_per_cu: int, unroll: int):
     _check(lib().w2a8_tune_gemv_stream(min_tiles, waves_per_cu, unroll), "w2a8_tune_gemv_stream")
+
+
+def tune_gemm(kernel: int):
+    """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general."""
+    _check(lib().w2a8_tune_gemm(kernel), "w2a8_tune_gemm")
 
 
 def gemv_plan(N: int, K: int, cus: int):

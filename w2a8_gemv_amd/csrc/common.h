@@ -113,8 +113,12 @@ hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
 // n-blocks (n-block = 4 strips = 128 weight rows), k-parts S, work units.
 struct GemmShape {
     int BM, MBLK, NBLK, S, tiles;
+    int pipe;   // pipelined-kernel configuration, or -1 for the general kernel
 };
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split);
+// Kernel choice knob (w2a8_tune_gemm): 0 automatic, 1 pipelined kernel
+// whenever K allows it, 2 general kernel always.
+int &gemm_kernel_mode();
 
 // Split-K is only ever used when M * Np <= kGemmSplitMaxOut, which bounds the
 // workspace that w2a8_workspace_bytes reports.

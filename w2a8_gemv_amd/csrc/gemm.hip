@@ -5,17 +5,21 @@
 // "如何判断结果" and "限制与注意事项" — the reference stops at M == 1), for M
 // token rows, Y[m][n] = sum_k X[m][k] * W[n][k], plus the fp32 epilogue.
 //
-// Design:
-//  * v_mfma_i32_16x16x64_i8: A = 16 activation rows x 64 k, B = 64 k x 16
-//    weight rows; lane l supplies row (l % 16) and the 16 bytes of k-group
-//    (l / 16) of each operand.  A and B use the same lane/byte -> k
-//    assignment, so the contraction is exact whatever order the unit sums in.
+// Both kernels use v_mfma_i32_16x16x64_i8: A = 16 activation rows x 64 k,
+// B = 64 k x 16 weight rows; lane l supplies row (l % 16) and the 16 bytes of
+// k-group (l / 16) of each operand.  A and B use the same lane/byte -> k
+// assignment, so the contraction is exact whatever order the unit sums in.
+// Weight codes are expanded in registers: (word >> 2j) & 0x03030303 gives
+// codes c in bytes, and v_perm_b32 maps c -> c - 1 (0xFF, 0x00, 0x01).
+//
+// The pipelined kernel (gemm_pipe_kernel, below) serves K a multiple of 16:
+// both operands stream through a ring of LDS stages by direct global->LDS
+// loads, several k-tiles ahead.  The general kernel serves every shape and
+// adds split-K for small outputs:
 //  * Workgroup = 4 waves; wave w owns one 32-row weight strip (two 16-row B
 //    blocks) and all BM activation rows of the workgroup (BM/16 A blocks).
 //  * Weights never go through LDS: a lane loads exactly the packed 32-bit
-//    word that holds its B operand (16 codes of one row, 16 consecutive k) and
-//    expands it in registers: (word >> 2j) & 0x03030303 gives codes c in
-//    bytes, and v_perm_b32 maps c -> c - 1 (0xFF, 0x00, 0x01) in one step.
+//    word that holds its B operand (16 codes of one row, 16 consecutive k).
 //  * Activations: one [BM x 128] int8 tile per k-step in LDS (rows padded to
 //    144 bytes), double buffered; global loads of the next tile are issued
 //    before the MFMAs of the current one.
@@ -47,6 +51,9 @@ struct GemmArgs {
     uint32_t *ws_cnt;
     int M, N, K, KT, NS, Np;
     int MBLK, NBLK, S, tiles;
+    // Set by the launcher so that the kernel divides nothing: KT = KQ*S + KR
+    // (k-part p starts at p*KQ + min(p, KR)).
+    int KQ, KR;
 };
 
 // Codes {0,1,2} in each byte -> signed weights {-1,0,1}.
@@ -79,6 +86,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     __shared__ uint32_t s_ticket;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // Work unit (m-block fastest, then n-block, then k-part), remapped from
+    // the block id so that consecutive units land on one XCD.
     const int R = int(gridDim.x);  // multiple of 8
     const int unit = (int(blockIdx.x) & 7) * (R >> 3) + (int(blockIdx.x) >> 3);
     if (unit >= a.tiles) return;   // uniform over the workgroup
@@ -86,7 +95,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int rest = unit / a.MBLK;
     const int nb = rest % a.NBLK;
     const int kp = rest / a.NBLK;
-    const int t0 = int(int64_t(kp) * a.KT / a.S), t1 = int(int64_t(kp + 1) * a.KT / a.S);
+    const int t0 = kp * a.KQ + min(kp, a.KR);
+    const int t1 = t0 + a.KQ + (kp < a.KR ? 1 : 0);
     const int m0 = mb * BM;
     const int strip = nb * 4 + wv;
     const bool active = strip < a.NS;
@@ -259,11 +269,252 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         __hip_atomic_exchange(a.ws_cnt + cidx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int BM, int WM, int WN, int SPW, int S>
+struct Pipe {
+    static constexpr int NW = WM * WN;
+    static constexpr int MBW = BM / WM / 16;           // A blocks per wave
+    static constexpr int NBW = 2 * SPW;                // B blocks per wave
+    static constexpr int NSTRIP = WN * SPW;            // strips per workgroup
+    static_assert(NSTRIP == NW, "one weight strip load per wave per tile");
+    static constexpr int DPW = BM * 8 / 64 / NW;       // activation loads per wave per tile
+    static_assert(DPW >= 1 && DPW * 64 * NW == BM * 8, "tile must split evenly over waves");
+    static constexpr int LPT = DPW + 1;                // loads per wave per tile
+    static constexpr int WAITN = (S - 2) * LPT;        // issued after a tile's group when used
+    static_assert(WAITN <= 63, "wait count must fit vmcnt");
+    static constexpr int XBYTES = BM * kTileK;
+    static constexpr int STAGE = XBYTES + NSTRIP * kTileBytes;
+};
+
+// Loads of tile tt into ring stage `slot`: this wave's DPW activation
+// instructions and its weight strip (tiles past the last repeat it).
+template <int BM, int WM, int WN, int SPW, int S>
+__device__ __forceinline__ void pipe_issue(int8_t *ring, int tt, int slot, int KT, int K, int wv,
+                                           const int8_t *const (&xsrc)[Pipe<BM, WM, WN, SPW, S>::DPW],
+                                           const int (&kcb)[Pipe<BM, WM, WN, SPW, S>::DPW],
+                                           const int8_t *wsrc) {
+    using P = Pipe<BM, WM, WN, SPW, S>;
+    const int tc = tt < KT - 1 ? tt : KT - 1;
+    int8_t *stage = ring + slot * P::STAGE;
+#pragma unroll
+    for (int d = 0; d < P::DPW; ++d) {
+        const int k0 = tc * kTileK + kcb[d];
+        const int k = k0 < K - 16 ? k0 : K - 16;
+        __builtin_amdgcn_global_load_lds(
+            xsrc[d] + k,
+            (__attribute__((address_space(3))) void *)(stage + (wv * P::DPW + d) * 1024), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(
+        wsrc + int64_t(tc) * kTileBytes,
+        (__attribute__((address_space(3))) void *)(stage + P::XBYTES + wv * kTileBytes), 16, 0, 0);
+}
+
+// MFMAs of the tile in ring stage s.
+template <int BM, int WM, int WN, int SPW, int S>
+__device__ __forceinline__ void pipe_mma(const int8_t *stage,
+                                         const int (&aoff)[Pipe<BM, WM, WN, SPW, S>::MBW][2],
+                                         const int (&boff)[Pipe<BM, WM, WN, SPW, S>::NBW][2],
+                                         v4i (&acc)[Pipe<BM, WM, WN, SPW, S>::MBW]
+                                                   [Pipe<BM, WM, WN, SPW, S>::NBW]) {
+    using P = Pipe<BM, WM, WN, SPW, S>;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        v4i bf[P::NBW];
+#pragma unroll
+        for (int j = 0; j < P::NBW; ++j)
+            bf[j] = expand_word(*reinterpret_cast<const uint32_t *>(stage + boff[j][h]));
+#pragma unroll
+        for (int i = 0; i < P::MBW; ++i) {
+            const v4i av = *reinterpret_cast<const v4i *>(stage + aoff[i][h]);
+#pragma unroll
+            for (int j = 0; j < P::NBW; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bf[j], acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel (K a multiple of 16).
+//
+//  * Workgroup = WM x WN waves; wave (wm, wn) owns rows m0 + wm*BM/WM ..
+//    (BM/WM rows, MBW A blocks) and SPW consecutive 32-row weight strips
+//    (NBW = 2*SPW B blocks).  Workgroup tile: BM rows x WN*SPW strips.
+//  * Both operands reach LDS by direct global->LDS loads (global_load_lds,
+//    16 bytes per lane, 1 KiB per wave instruction) into a ring of S
+//    stages, so S-1 k-tiles are in flight with no register staging.  A stage
+//    holds the [BM x 128] activation tile, 16-byte chunk (r, c) at position
+//    8r + (c ^ (r & 7)) (row loads stay 128-byte coalesced, A fragment reads
+//    of 16 rows at one chunk spread over the banks), then the packed 1 KiB
+//    tile of each of the workgroup's strips, as stored in HBM.
+//  * Each lane reads the four packed words of its B operands from LDS and
+//    expands them in registers (codes -> {-1, 0, 1} with v_perm_b32).
+//  * Per k-tile: wait for this wave's loads of the tile (the compiler does not
+//    track global->LDS loads: the count is explicit), barrier, refill the
+//    stage freed by the previous tile, then the MFMAs.
+//  * Rows past M read row M-1 and k-chunks past K read a chunk inside the
+//    row: their products reach only discarded outputs or meet the weight
+//    padding (code 01, weight 0).  Strips past the matrix read its last strip.
+template <int BM, int WM, int WN, int SPW, int S>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
+    using P = Pipe<BM, WM, WN, SPW, S>;
+    constexpr int MBW = P::MBW, NBW = P::NBW, DPW = P::DPW, WAITN = P::WAITN;
+    __shared__ __attribute__((aligned(1024))) int8_t ring[S * P::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv / WN, wn = wv - (wv / WN) * WN;
+    const int R = int(gridDim.x);  // multiple of 8
+    const int unit = (int(blockIdx.x) & 7) * (R >> 3) + (int(blockIdx.x) >> 3);
+    if (unit >= a.tiles) return;   // uniform over the workgroup
+    const int mb = unit % a.MBLK;
+    const int nb = unit / a.MBLK;
+    const int m0 = mb * BM;
+    const int KT = a.KT;
+
+    // Activation loads: instruction d of this wave covers chunk positions
+    // p = (wv*DPW + d)*64 + lane of a stage.
+    const int8_t *xsrc[DPW];
+    int kcb[DPW];
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+        const int p = (wv * DPW + d) * 64 + lane;
+        const int r = p >> 3, c = (p & 7) ^ (r & 7);
+        xsrc[d] = a.x + int64_t(min(m0 + r, a.M - 1)) * a.K;
+        kcb[d] = 16 * c;
+    }
+    // Weight load: this wave brings strip wv of the workgroup.
+    const int sload = min(nb * P::NSTRIP + wv, a.NS - 1);
+    const int8_t *wsrc = reinterpret_cast<const int8_t *>(a.wp) +
+                         int64_t(sload) * KT * kTileBytes + 16 * lane;
+
+    v4i acc[MBW][NBW];
+#pragma unroll
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    // A fragment byte offsets within a stage, per block i and k-half h.
+    int aoff[MBW][2];
+#pragma unroll
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = wm * (BM / WM) + 16 * i + (lane & 15);
+            const int c = 4 * h + (lane >> 4);
+            aoff[i][h] = (r * 8 + (c ^ (r & 7))) * 16;
+        }
+    // B operand word offsets (bytes) within a stage: strip sp of the wave,
+    // rows 16jb..16jb+15 of it, k-half h.
+    int boff[NBW][2];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 16 * jb + (lane & 15);
+                const int kg = 4 * h + (lane >> 4);
+                boff[2 * sp + jb][h] = P::XBYTES + (wn * SPW + sp) * kTileBytes +
+                                       ((8 * (r >> 2) + kg) * 4 + (r & 3)) * 4;
+            }
+
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        pipe_issue<BM, WM, WN, SPW, S>(ring, s, s, KT, a.K, wv, xsrc, kcb, wsrc);
+
+    // One k-tile: this wave's loads of the tile have landed and its LDS reads
+    // of the previous tile are done (lgkmcnt 0); after the barrier that holds
+    // for every wave.  A plain s_barrier: a fence here would wait for every
+    // load in flight; the empty asm keeps the compiler from moving memory
+    // accesses across it.  Then refill the stage the previous tile used
+    // (past the last tile: a repeat of it, never used, which keeps the wait
+    // count exact) and multiply.
+#define W2A8_PIPE_STEP(s, tt)                                                                    \
+    do {                                                                                         \
+        __builtin_amdgcn_s_waitcnt((WAITN & 15) | ((WAITN >> 4) << 14) | (0x7 << 4));            \
+        __builtin_amdgcn_s_barrier();                                                            \
+        __asm__ volatile("" ::: "memory");                                                       \
+        pipe_issue<BM, WM, WN, SPW, S>(ring, (tt) + S - 1, ((s) + S - 1) % S, KT, a.K, wv, xsrc,  \
+                                       kcb, wsrc);                                               \
+        pipe_mma<BM, WM, WN, SPW, S>(ring + (s) * P::STAGE, aoff, boff, acc);                    \
+    } while (0)
+
+    // Whole groups of S tiles, then the remainder.
+    int t = 0;
+    for (; t + S <= KT; t += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) W2A8_PIPE_STEP(s, t + s);
+    }
+    const int rem = KT - t;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (s < rem) W2A8_PIPE_STEP(s, t + s);
+#undef W2A8_PIPE_STEP
+
+    // Output element of acc[i][j][e]: row m0 + wm*BM/WM + 16i + 4*(lane/16) + e,
+    // column strip(j/2)*32 + 16*(j%2) + lane%16.  Activation scales of this
+    // lane's rows are all loaded before any store (a wait between stores would
+    // also wait for the stores before it).
+    float sa[MBW][4] = {};
+    if (a.y_f32) {
+#pragma unroll
+        for (int i = 0; i < MBW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sa[i][e] = a.sa[min(m0 + wm * (BM / WM) + 16 * i + 4 * (lane >> 4) + e, a.M - 1)];
+        __builtin_amdgcn_s_waitcnt(0x0070 | (0xF << 8));   // vmcnt(0)
+    }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int strip = nb * P::NSTRIP + wn * SPW + j / 2;
+        const int n = strip * kTileRows + 16 * (j & 1) + (lane & 15);
+        if (strip >= a.NS || n >= a.N) continue;
+#pragma unroll
+        for (int i = 0; i < MBW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * (BM / WM) + 16 * i + 4 * (lane >> 4) + e;
+                if (m < a.M) {
+                    const int v = acc[i][j][e];
+                    if (a.y_i32) a.y_i32[int64_t(m) * a.N + n] = v;
+                    if (a.y_f32) a.y_f32[int64_t(m) * a.N + n] = (float(v) * sa[i][e]) * a.sw;
+                }
+            }
+    }
+}
+
 }  // namespace
 
 // Shape of a GEMM launch: block rows BM by M, k-split S when few output tiles.
+// Pipelined-kernel configurations: (BM, WM, WN, SPW), ring depth 4.
+struct PipeCfg {
+    int BM, WM, WN, SPW;
+};
+constexpr PipeCfg kPipeCfg[4] = {{32, 1, 4, 1}, {64, 1, 4, 1}, {128, 2, 1, 2}, {128, 2, 2, 2}};
+
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
     GemmShape g;
+    g.pipe = -1;
+    if (K >= 16 && K % 16 == 0) {
+        // Pipelined kernel: rows per workgroup by M; at M <= 128 two strips
+        // per workgroup (twice the workgroups of four).  It has no k-split:
+        // when its grid is tiny (under one workgroup per 8 CUs; measured: 20
+        // workgroups for M = 8 at 2560 x 6912) and the output is small enough
+        // for split-K, the general kernel with split-K is used.
+        const int pipe = M <= 32 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 3;
+        const PipeCfg &c = kPipeCfg[pipe];
+        const int64_t NS = round_up(N, kTileRows) / kTileRows;
+        const int64_t mblk = ceil_div(M, c.BM), nblk = ceil_div(NS, int64_t(c.WN) * c.SPW);
+        const int mode = gemm_kernel_mode();
+        if (mode == 1 || (mode == 0 && !(can_split && mblk * nblk < cus / 8))) {
+            g.pipe = pipe;
+            g.BM = c.BM;
+            g.MBLK = int(mblk);
+            g.NBLK = int(nblk);
+            g.S = 1;
+            g.tiles = g.MBLK * g.NBLK;
+            return g;
+        }
+    }
     g.BM = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
     const int64_t NS = round_up(N, kTileRows) / kTileRows;
     const int64_t KT = round_up(K, kTileK) / kTileK;
@@ -301,9 +552,21 @@ hipError_t launch_gemm(const GemmLaunch &l, hipStream_t stream) {
     a.NBLK = l.shape.NBLK;
     a.S = l.shape.S;
     a.tiles = l.shape.tiles;
+    a.KQ = a.KT / a.S;
+    a.KR = a.KT % a.S;
     const unsigned blocks = unsigned(round_up(a.tiles, 8));
     void *args[] = {&a};
     const void *fn;
+    if (l.shape.pipe >= 0) {
+        const PipeCfg &c = kPipeCfg[l.shape.pipe];
+        switch (l.shape.pipe) {
+        case 0: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<32, 1, 4, 1, 4>); break;
+        case 1: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<64, 1, 4, 1, 4>); break;
+        case 2: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<128, 2, 1, 2, 4>); break;
+        default: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<128, 2, 2, 2, 4>); break;
+        }
+        return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN)), args, 0, stream);
+    }
     switch (l.shape.BM) {
     case 16: fn = reinterpret_cast<const void *>(&gemm_kernel<16>); break;
     case 32: fn = reinterpret_cast<const void *>(&gemm_kernel<32>); break;

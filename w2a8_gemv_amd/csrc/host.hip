@@ -49,6 +49,11 @@ int current_device(DeviceInfo *out) {
     return g_dev_status[dev];
 }
 
+int &gemm_kernel_mode() {
+    static int mode = 0;
+    return mode;
+}
+
 GemvPolicy &gemv_policy() {
     // Streaming kernel off by default (stream_min_tiles 0): on gfx950 the
     // workgroup kernel is as fast or faster on every measured shape.
@@ -372,6 +377,12 @@ int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_pe
     const int64_t KT = round_up(K, kTileK) / kTileK;
     int run = 0;
     gemv_plan_full(NS, K, cus, waves_per_wg, wgs_per_strip, &run, unroll, stream_waves);
+    return W2A8_OK;
+}
+
+int w2a8_tune_gemm(int kernel) {
+    if (kernel < 0 || kernel > 2) return W2A8_ERR_VALUE;
+    gemm_kernel_mode() = kernel;
     return W2A8_OK;
 }
 

@@ -344,7 +344,8 @@ __device__ __forceinline__ void pipe_mma(const int8_t *stage,
 //    holds the [BM x 128] activation tile, 16-byte chunk (r, c) at position
 //    8r + (c ^ (r & 7)) (row loads stay 128-byte coalesced, A fragment reads
 //    of 16 rows at one chunk spread over the banks), then the packed 1 KiB
-//    tile of each of the workgroup's strips, as stored in HBM.
+//    tile of each of the workgroup's strips with its 16-byte slots permuted
+//    (XOR within groups of 8) so that B operand reads are conflict-free.
 //  * Each lane reads the four packed words of its B operands from LDS and
 //    expands them in registers (codes -> {-1, 0, 1} with v_perm_b32).
 //  * Per k-tile: wait for this wave's loads of the tile (the compiler does not
@@ -381,10 +382,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
         xsrc[d] = a.x + int64_t(min(m0 + r, a.M - 1)) * a.K;
         kcb[d] = 16 * c;
     }
-    // Weight load: this wave brings strip wv of the workgroup.
+    // Weight load: this wave brings strip wv of the workgroup.  Lane l loads
+    // 16-byte slot 8(l>>3) + ((l & 7) ^ 2((l>>3) & 3)) of the tile into LDS
+    // position l (an XOR within each group of 8 slots, its own inverse), so
+    // that the B operand reads below hit 32 distinct banks.
     const int sload = min(nb * P::NSTRIP + wv, a.NS - 1);
+    const int wslot = 8 * (lane >> 3) + ((lane & 7) ^ (2 * ((lane >> 3) & 3)));
     const int8_t *wsrc = reinterpret_cast<const int8_t *>(a.wp) +
-                         int64_t(sload) * KT * kTileBytes + 16 * lane;
+                         int64_t(sload) * KT * kTileBytes + 16 * wslot;
 
     v4i acc[MBW][NBW];
 #pragma unroll
@@ -413,8 +418,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
             for (int h = 0; h < 2; ++h) {
                 const int r = 16 * jb + (lane & 15);
                 const int kg = 4 * h + (lane >> 4);
+                const int g = r >> 2;                    // slot 8g + kg, stored at
+                const int pos = 8 * g + (kg ^ (2 * (g & 3)));   // position pos
                 boff[2 * sp + jb][h] = P::XBYTES + (wn * SPW + sp) * kTileBytes +
-                                       ((8 * (r >> 2) + kg) * 4 + (r & 3)) * 4;
+                                       (pos * 4 + (r & 3)) * 4;
             }
 
 #pragma unroll
@@ -485,22 +492,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
 }  // namespace
 
 // Shape of a GEMM launch: block rows BM by M, k-split S when few output tiles.
-// Pipelined-kernel configurations: (BM, WM, WN, SPW), ring depth 4.
+// Pipelined-kernel configurations: (BM, WM, WN, SPW, ring depth).  Chosen by
+// a sweep on MI355X over block rows 32..256, four wave layouts and depths
+// 3..8: 32 rows (depth 4) for M <= 32 and 64 rows (depth 6) above won or tied
+// on every prefill shape; larger blocks leave too few workgroups.
 struct PipeCfg {
-    int BM, WM, WN, SPW;
+    int BM, WM, WN, SPW, S;
 };
-constexpr PipeCfg kPipeCfg[4] = {{32, 1, 4, 1}, {64, 1, 4, 1}, {128, 2, 1, 2}, {128, 2, 2, 2}};
+constexpr PipeCfg kPipeCfg[2] = {{32, 1, 4, 1, 4}, {64, 1, 4, 1, 6}};
 
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
     GemmShape g;
     g.pipe = -1;
     if (K >= 16 && K % 16 == 0) {
-        // Pipelined kernel: rows per workgroup by M; at M <= 128 two strips
-        // per workgroup (twice the workgroups of four).  It has no k-split:
+        // Pipelined kernel: 32 or 64 rows per workgroup by M.  It has no k-split:
         // when its grid is tiny (under one workgroup per 8 CUs; measured: 20
         // workgroups for M = 8 at 2560 x 6912) and the output is small enough
         // for split-K, the general kernel with split-K is used.
-        const int pipe = M <= 32 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 3;
+        const int pipe = M <= 32 ? 0 : 1;
         const PipeCfg &c = kPipeCfg[pipe];
         const int64_t NS = round_up(N, kTileRows) / kTileRows;
         const int64_t mblk = ceil_div(M, c.BM), nblk = ceil_div(NS, int64_t(c.WN) * c.SPW);
@@ -559,12 +568,8 @@ hipError_t launch_gemm(const GemmLaunch &l, hipStream_t stream) {
     const void *fn;
     if (l.shape.pipe >= 0) {
         const PipeCfg &c = kPipeCfg[l.shape.pipe];
-        switch (l.shape.pipe) {
-        case 0: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<32, 1, 4, 1, 4>); break;
-        case 1: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<64, 1, 4, 1, 4>); break;
-        case 2: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<128, 2, 1, 2, 4>); break;
-        default: fn = reinterpret_cast<const void *>(&gemm_pipe_kernel<128, 2, 2, 2, 4>); break;
-        }
+        fn = l.shape.pipe == 0 ? reinterpret_cast<const void *>(&gemm_pipe_kernel<32, 1, 4, 1, 4>)
+                               : reinterpret_cast<const void *>(&gemm_pipe_kernel<64, 1, 4, 1, 6>);
         return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN)), args, 0, stream);
     }
     switch (l.shape.BM) {

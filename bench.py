@@ -385,6 +385,20 @@ def linear_extras(torch, w2a8, synth, lib, stream):
                          "layer_bytes": lbytes,
                          "layer": "quant_act_int8 + " + ("w2a8_gemv" if m == 1 else "w2a8_gemm")
                                   + " with fp32 epilogue, 13824 x 2560, two launches"}
+        if m == 1:
+            def fused(j):
+                rc = lib.w2a8_linear_gemv(ptrs[j % len(ptrs)], vp(xd.data_ptr()), n, k,
+                                          ctypes.c_float(float(sw)), vp(y.data_ptr()), None,
+                                          vp(ws.data_ptr()), ws.numel(), sp)
+                if rc != 0:
+                    raise RuntimeError(f"w2a8_linear_gemv failed with status {rc}")
+            tf = graph_times(torch, fused, 24, stream)
+            mf = sorted(tf)[len(tf) // 2]
+            fbytes = 2 * k + n * k // 4 + 4 * n      # bf16 row, packed weights, fp32 out
+            out["M=1"].update({"fused_median_us": round(mf, 3),
+                               "fused_GBps": round(fbytes / mf / 1e3, 1),
+                               "fused_bytes": fbytes,
+                               "fused": "w2a8_linear_gemv: the same layer in one launch"})
         del copies, wp, xd, xq, sa, y, ws
         torch.cuda.empty_cache()
     return out

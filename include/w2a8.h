@@ -171,6 +171,21 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K,
               int32_t *y_i32, const float *s_a, float s_w, float *y_f32,
               void *workspace, int64_t ws_bytes, void *stream);
 
+/* Whole linear layer for one token, in one launch: the result of
+ * quant_act_int8 (M = 1) followed by w2a8_gemv with its fp32 epilogue,
+ * bit-identical to that pair.
+ * [WIN] §3.1: integer product of the quantized activations and the ternary
+ * weights, the scales multiplied back afterwards; [TEST] (introduction):
+ * 8-bit activations.  Every workgroup takes the row maximum itself, so the
+ * quantized row never goes through memory (it reads the bf16 row once per
+ * workgroup from the L2).
+ * x_bf16: device, bf16 [K] bit patterns, 16-byte aligned.  y_f32: device,
+ * fp32 [N] (required).  y_i32: device, int32 [N] of the integer product, or
+ * NULL.  s_w, workspace, ws_bytes, stream: as w2a8_gemv. */
+int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, int64_t K,
+                     float s_w, float *y_f32, int32_t *y_i32, void *workspace,
+                     int64_t ws_bytes, void *stream);
+
 /* W2A8 batched product, M >= 1 (prefill).
  * [TEST] "限制与注意事项": the reference handles only M == 1; this entry
  * computes the same product for M token rows:

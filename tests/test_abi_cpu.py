@@ -52,7 +52,8 @@ def test_library_exports_every_declared_symbol():
     expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
-                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemv_stream", "w2a8_tune_gemm"}
+                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemv_stream", "w2a8_tune_gemm",
+                "w2a8_linear_gemv"}
     assert expected.issubset(set(names)), set(names) ^ expected
     L = ctypes.CDLL(w2a8.LIB_PATH)
     for n in names:

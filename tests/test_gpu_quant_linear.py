@@ -67,16 +67,84 @@ def _check_f32(y, ref):
     np.testing.assert_array_equal(y, ref)
 
 
-@pytest.mark.parametrize("M", [1, 128])
-def test_full_linear_layer(M):
+@pytest.mark.parametrize("M,fused", [(1, True), (1, False), (128, False)],
+                         ids=["M1-fused", "M1-two-launch", "M128"])
+def test_full_linear_layer(M, fused):
     N, K = 13824, 2560
     xb, W = synth.linear_case(M, N, K, seed=synth.LINEAR_SEEDS[M])
     wq, sw = oracle.ternarize_absmean(W)
     wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
-    y = w2a8.linear(_bf16_dev(xb), wp, float(sw), N, K)
+    y = w2a8.linear(_bf16_dev(xb), wp, float(sw), N, K, fused=fused)
     torch.cuda.synchronize()
     ref, _ = _linear_ref(xb, wq, sw)
     _check_f32(y.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# Fused linear GEMV (quantize + product + epilogue in one launch)
+# ---------------------------------------------------------------------------
+def _fused_dev(xb, wq, N, K, sw):
+    wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
+    yf = torch.full((N,), float("nan"), dtype=torch.float32, device=dev())
+    yi = torch.full((N,), -7, dtype=torch.int32, device=dev())
+    w2a8.w2a8_linear_gemv(wp, _bf16_dev(xb.reshape(-1)), N, K, float(sw), yf, y_i32=yi)
+    torch.cuda.synchronize()
+    return yf.cpu().numpy(), yi.cpu().numpy()
+
+
+# ragged K (K % 16 != 0, K < 16, K = 1), split strips (K = 27648, 10240),
+# several workgroup shapes
+FUSED_SHAPES = [(1000, 2560), (97, 100), (33, 7), (5, 1), (64, 15), (300, 16), (129, 129),
+                (2560, 6912), (3200, 10240), (5120, 27648), (40, 4000), (2, 130)]
+
+
+@pytest.mark.parametrize("N,K", FUSED_SHAPES)
+def test_fused_linear_gemv_matches_oracle(N, K):
+    xb, _ = synth.linear_case(1, 1, K, seed=N + 3 * K)
+    _, wq = synth.gemv_case(N, K, seed=N + K, sparse=True)
+    sw = np.float32(0.0137)
+    yf, yi = _fused_dev(xb, wq, N, K, sw)
+    ref, acc = _linear_ref(xb, wq, sw)
+    np.testing.assert_array_equal(yi, acc[0])
+    _check_f32(yf, ref[0])
+
+
+def test_fused_linear_gemv_zero_and_single_value_rows():
+    N, K = 300, 1000
+    _, wq = synth.gemv_case(N, K, seed=4)
+    for row in (np.zeros(K, np.float32), np.eye(1, K, 517, dtype=np.float32)[0] * -3.5):
+        xb = synth.fp32_to_bf16_bits(row.reshape(1, K))
+        yf, yi = _fused_dev(xb, wq, N, K, np.float32(0.5))
+        ref, acc = _linear_ref(xb, wq, np.float32(0.5))
+        np.testing.assert_array_equal(yi, acc[0])
+        np.testing.assert_array_equal(yf, ref[0])
+
+
+@pytest.mark.parametrize("policy", [(1, 32, 8, 256, 10 ** 6), (1, 1, 4, 256, 10 ** 6),
+                                    (64, 1, 8, 256, 1), (2, 2, 8, 7, 1), (16, 32, 4, 1, 1)])
+def test_fused_linear_gemv_forced_splits(policy):
+    try:
+        w2a8.tune_gemv(*policy)
+        for N, K in [(200, 3200), (96, 27648), (33, 1000)]:
+            xb, _ = synth.linear_case(1, 1, K, seed=K)
+            _, wq = synth.gemv_case(N, K, seed=N)
+            yf, yi = _fused_dev(xb, wq, N, K, np.float32(0.02))
+            ref, acc = _linear_ref(xb, wq, np.float32(0.02))
+            np.testing.assert_array_equal(yi, acc[0])
+            np.testing.assert_array_equal(yf, ref[0])
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+def test_fused_equals_two_launch_path():
+    N, K = 13824, 2560
+    xb, W = synth.linear_case(1, N, K, seed=synth.LINEAR_SEEDS[1])
+    wq, sw = oracle.ternarize_absmean(W)
+    wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
+    a = w2a8.linear(_bf16_dev(xb), wp, float(sw), N, K, fused=True)
+    b = w2a8.linear(_bf16_dev(xb), wp, float(sw), N, K, fused=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
 def test_full_linear_uses_library_ternarizer_identically():

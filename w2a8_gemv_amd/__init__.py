@@ -22,7 +22,7 @@ __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
-    "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream", "tune_gemm",
+    "w2a8_linear_gemv", "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream", "tune_gemm",
     "DEFAULT_GEMV_STREAM_POLICY",
 ]
 
@@ -73,6 +73,8 @@ def lib():
         L.w2a8_gemv.restype = I32
         L.w2a8_gemm.argtypes = [P, P, I64, I64, I64, P, P, F32, P, P, I64, P]
         L.w2a8_gemm.restype = I32
+        L.w2a8_linear_gemv.argtypes = [P, P, I64, I64, F32, P, P, P, I64, P]
+        L.w2a8_linear_gemv.restype = I32
         L.w2a8_tune_gemv.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv.restype = I32
         L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
@@ -271,6 +273,29 @@ def w2a8_gemm(w_packed, x, M, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
            "w2a8_gemm")
 
 
+def w2a8_linear_gemv(w_packed, x_bf16, N, K, s_w, y_f32, y_i32=None, workspace=None,
+                     stream=None):
+    """Raw C-ABI call: fused quantize + GEMV + fp32 epilogue for one token."""
+    _need(w_packed, "w_packed", torch.uint8, "cuda")
+    if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not x_bf16.is_cuda:
+        raise TypeError("x_bf16 must be a bfloat16 (or 16-bit bit pattern) CUDA tensor")
+    if not x_bf16.is_contiguous() or x_bf16.numel() != K:
+        raise ValueError("x_bf16 must be contiguous with K elements")
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than packed_bytes(N, K)")
+    _need(y_f32, "y_f32", torch.float32, "cuda")
+    if y_f32.numel() != N:
+        raise ValueError("y_f32 must have N elements")
+    if y_i32 is not None:
+        _need(y_i32, "y_i32", torch.int32, "cuda")
+        if y_i32.numel() != N:
+            raise ValueError("y_i32 must have N elements")
+    ws = _ws(workspace_bytes(1, N, K), x_bf16.device, stream, workspace)
+    _check(lib().w2a8_linear_gemv(_ptr(w_packed), _ptr(x_bf16), N, K, ctypes.c_float(s_w),
+                                  _ptr(y_f32), _ptr(y_i32), _ptr(ws), ws.numel(),
+                                  _stream_handle(stream)), "w2a8_linear_gemv")
+
+
 def gemv(w_packed, x, N, K, *, out_i32=True, s_a=None, s_w=1.0, stream=None):
     """y_i32 [N] (and y_f32 [N] when s_a is given) for one int8 activation row."""
     y_i32 = torch.empty(N, dtype=torch.int32, device=x.device) if out_i32 else None
@@ -288,14 +313,20 @@ def gemm(w_packed, x, N, K, *, out_i32=True, s_a=None, s_w=1.0, stream=None):
     return y_i32 if y_f32 is None else (y_i32, y_f32)
 
 
-def linear(x_bf16, w_packed, s_w, N, K, stream=None):
+def linear(x_bf16, w_packed, s_w, N, K, stream=None, fused=True):
     """Full W2A8 linear layer: bf16 activations [M, K] -> fp32 [M, N].
 
+    M == 1 with fused=True: w2a8_linear_gemv (one launch).  Otherwise
     quant_act_int8, then w2a8_gemv (M == 1) or w2a8_gemm (M > 1) with the
     fp32 epilogue, all enqueued on one stream with no host synchronisation.
+    Both routes give bit-identical results.
     """
     x2 = x_bf16.view(1, -1) if x_bf16.dim() == 1 else x_bf16
     M = x2.shape[0]
+    if M == 1 and fused:
+        y = torch.empty((1, N), dtype=torch.float32, device=x2.device)
+        w2a8_linear_gemv(w_packed, x2.reshape(-1), N, K, s_w, y.view(-1), stream=stream)
+        return y
     xq, sa = quant_act_int8(x2, stream=stream)
     y = torch.empty((M, N), dtype=torch.float32, device=x2.device)
     if M == 1:

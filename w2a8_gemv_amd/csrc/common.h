@@ -48,6 +48,7 @@ GemvPolicy &gemv_policy();
 struct GemvLaunch {
     const uint32_t *wp;
     const int8_t *x;
+    const uint16_t *xb;   // fused linear GEMV: the bf16 activation row (x unused)
     int32_t *y_i32;
     float *y_f32;
     const float *sa;
@@ -66,6 +67,19 @@ struct GemvLaunch {
     // v starts v*WQi + min(v, WRi) tiles in).
     int KQ, KR, WQ0, WR0, WQ1, WR1;
 };
+// Activation quantization, per element (shared by the quantizer kernel and
+// the fused linear GEMV so both produce the same codes): bf16 halves of a
+// 32-bit word as fp32, and q = clamp(round_half_even(x * inv), -127, 127)
+// as a byte.  Each step is one correctly rounded fp32 operation (the product
+// is not contracted: the library is built with -ffp-contract=off).
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t q8(float x, float inv) {
+    float r = __builtin_rintf(x * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return uint32_t(uint8_t(int8_t(int(r))));
+}
+
 // Split-k combining of a GEMV row with one device-scope atomic per
 // contribution.  Each contributor adds (its k-tile count << 40) + its partial
 // value to the row's 64-bit word.  The counts reach KT exactly with the last
@@ -101,6 +115,9 @@ size_t gemv_lds_bytes(const GemvLaunch &a);
 bool gemv_stream_fits(int64_t K);
 size_t gemv_stream_lds_bytes(const GemvLaunch &a);
 hipError_t launch_gemv_stream(const GemvLaunch &a, hipStream_t stream);
+// Fused linear GEMV: quantize the bf16 row in every workgroup, then the
+// workgroup kernel with the fp32 epilogue (gemv.hip).
+hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream);
 // Full plan: G > 0 selects the streaming kernel (then wk = sg = run = 0).
 void gemv_plan_full(int64_t NS, int64_t K, int cus, int *wk, int *sg, int *run, int *unroll,
                     int *g);

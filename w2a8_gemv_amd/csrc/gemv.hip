@@ -73,10 +73,34 @@ __device__ __forceinline__ int sum8(int v) {
     return v;
 }
 
-__device__ __forceinline__ void store_out(const GemvLaunch &a, int row, int v) {
+__device__ __forceinline__ void store_out(const GemvLaunch &a, float sa, int row, int v) {
     if (a.y_i32) a.y_i32[row] = v;
-    if (a.y_f32) a.y_f32[row] = (float(v) * a.sa[0]) * a.sw;
+    if (a.y_f32) a.y_f32[row] = (float(v) * sa) * a.sw;
 }
+
+// Largest |x| of bf16 words (8 values per v4u... 2 per word).
+__device__ __forceinline__ float absmax_words(const v4u v, float m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(lo_bf16(v[j])), fabsf(hi_bf16(v[j]))));
+    return m;
+}
+
+// 16 bf16 activations (two v4u) quantized with `inv`, packed as 16 bytes.
+__device__ __forceinline__ v4u quant16(const v4u lo, const v4u hi, float inv) {
+    v4u o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t p = w < 2 ? lo[2 * w] : hi[2 * (w - 2)];
+        const uint32_t q = w < 2 ? lo[2 * w + 1] : hi[2 * (w - 2) + 1];
+        o[w] = q8(lo_bf16(p), inv) | (q8(hi_bf16(p), inv) << 8) | (q8(lo_bf16(q), inv) << 16) |
+               (q8(hi_bf16(q), inv) << 24);
+    }
+    return o;
+}
+
+// Bf16 activation chunks that each thread loads, before the weights, for the
+// row maximum of the fused kernel (the rest, if any, after them).
+constexpr int kAmaxChunks = 2;
 
 // Loads of batch b (tiles w0 + b*U + u, clamped to the run's last tile).
 template <int U>
@@ -103,7 +127,12 @@ __device__ __forceinline__ void mac_batch(const v4u (&w)[U], const uint8_t *xl, 
     }
 }
 
-template <int U>
+// FUSED: the activations arrive as one bf16 row (a.xb).  Every workgroup
+// takes the row's largest |x| itself, quantizes its own k-range with the same
+// per-element operations as the quantizer kernel (q8 in common.h) and scale
+// s_a = amax/127, so the result is bit-identical to quant_act_int8 followed
+// by the plain GEMV, in one launch.
+template <int U, bool FUSED>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -141,14 +170,43 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     const int kbase = w0 * kTileK;
     const int nchunk = n * (kTileK / 16);
     v4u xr[kXChunks];
+    // Fused: the run's 16-value chunks as bf16 (two v4u each) and this
+    // thread's share of the whole row for its maximum.
+    v4u xh[FUSED ? kXChunks : 1][2];
+    v4u am[FUSED ? kAmaxChunks : 1][2];
+    const int nfull = a.K >> 4;                    // 16-value chunks entirely below K
+    const int nthr = 64 * a.WK;
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int j = 0; j < kXChunks; ++j) {
-        const int c = lane + 64 * j;
-        xr[j] = v4u{0u, 0u, 0u, 0u};
-        if (c < nchunk && kbase + 16 * c + 16 <= a.K)
-            xr[j] = *reinterpret_cast<const v4u *>(a.x + kbase + 16 * c);
+        for (int j = 0; j < kXChunks; ++j) {
+            const int c = lane + 64 * j;
+            xh[j][0] = xh[j][1] = v4u{0u, 0u, 0u, 0u};
+            if (c < nchunk && kbase + 16 * c + 16 <= a.K) {
+                const v4u *p = reinterpret_cast<const v4u *>(a.xb + kbase + 16 * c);
+                xh[j][0] = p[0];
+                xh[j][1] = p[1];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kAmaxChunks; ++i) {
+            const int c = tid + nthr * i;
+            am[i][0] = am[i][1] = v4u{0u, 0u, 0u, 0u};
+            if (c < nfull) {
+                const v4u *p = reinterpret_cast<const v4u *>(a.xb + 16 * c);
+                am[i][0] = p[0];
+                am[i][1] = p[1];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kXChunks; ++j) {
+            const int c = lane + 64 * j;
+            xr[j] = v4u{0u, 0u, 0u, 0u};
+            if (c < nchunk && kbase + 16 * c + 16 <= a.K)
+                xr[j] = *reinterpret_cast<const v4u *>(a.x + kbase + 16 * c);
+        }
     }
-    if ((a.K & 15) != 0) {
+    if (!FUSED && (a.K & 15) != 0) {
 #pragma unroll
         for (int j = 0; j < kXChunks; ++j) {
             const int c = lane + 64 * j;
@@ -168,6 +226,50 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     v4u wa[U], wb[U];
     load_batch<U>(wt, w0, last, 0, wa);
     load_batch<U>(wt, w0, last, 1, wb);
+
+    // 2b. Fused: the row maximum (chunks beyond the first share and the
+    //     values past the last whole chunk after the weight loads), combined
+    //     over the workgroup through LDS; then this run's codes.
+    float sa = 0.0f;
+    if constexpr (FUSED) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kAmaxChunks; ++i)
+            amax = absmax_words(am[i][1], absmax_words(am[i][0], amax));
+        for (int c = tid + nthr * kAmaxChunks; c < nfull; c += nthr) {
+            const v4u *p = reinterpret_cast<const v4u *>(a.xb + 16 * c);
+            amax = absmax_words(p[1], absmax_words(p[0], amax));
+        }
+        if (tid == 0)
+            for (int k = 16 * nfull; k < a.K; ++k)
+                amax = fmaxf(amax, fabsf(__uint_as_float(uint32_t(a.xb[k]) << 16)));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        float *fred = reinterpret_cast<float *>(red + a.WK * kTileRows);   // WK floats
+        if (lane == 0) fred[wv] = amax;
+        __syncthreads();
+        amax = 0.0f;
+        for (int w = 0; w < a.WK; ++w) amax = fmaxf(amax, fred[w]);
+        // The quantizer's scale and reciprocal; a zero row quantizes to 0.
+        sa = amax / 127.0f;
+        const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+#pragma unroll
+        for (int j = 0; j < kXChunks; ++j) {
+            const int c = lane + 64 * j;
+            xr[j] = v4u{0u, 0u, 0u, 0u};
+            if (64 * j >= nchunk) continue;   // the whole group lies past the run
+            xr[j] = quant16(xh[j][0], xh[j][1], inv);
+            const int k0 = kbase + 16 * c;
+            if ((a.K & 15) != 0 && c < nchunk && k0 < a.K && k0 + 16 > a.K) {
+                uint32_t b4[4] = {0u, 0u, 0u, 0u};
+                for (int i = 0; i < 16; ++i)
+                    if (k0 + i < a.K)
+                        b4[i >> 2] |= q8(__uint_as_float(uint32_t(a.xb[k0 + i]) << 16), inv)
+                                      << (8 * (i & 3));
+                xr[j] = v4u{b4[0], b4[1], b4[2], b4[3]};
+            }
+        }
+    }
 
     // 3. Stage the run's activations into the wave's LDS region and sum them.
     int sx = 0;
@@ -224,8 +326,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
             for (int w = 0; w < a.WK; ++w) tot += red[w * kTileRows + tid];
     }
 
+    if constexpr (!FUSED) sa = a.y_f32 ? a.sa[0] : 0.0f;
     if (a.SG == 1) {
-        if (owner && row < a.N) store_out(a, row, tot);
+        if (owner && row < a.N) store_out(a, sa, row, tot);
         return;
     }
     // k-range split over workgroups: one device-scope atomic per row (coherent
@@ -233,13 +336,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     // row stores it.
     int v;
     if (owner && split_add(a.ws_row + row, ntile, tot, a.KT, &v) && row < a.N)
-        store_out(a, row, v);
+        store_out(a, sa, row, v);
 }
 
 }  // namespace
 
 size_t gemv_lds_bytes(const GemvLaunch &a) {
-    return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4;
+    // activation regions, row partials, and the fused kernel's per-wave maxima
+    return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4 + 16 * 4;
 }
 
 hipError_t launch_gemv(const GemvLaunch &la, hipStream_t stream) {
@@ -252,14 +356,22 @@ hipError_t launch_gemv(const GemvLaunch &la, hipStream_t stream) {
     a.WR1 = (a.KQ + 1) % a.WK;
     void *args[] = {&a};
     const void *fn;
-    switch (a.unroll) {
-    case 2: fn = reinterpret_cast<const void *>(&gemv_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void *>(&gemv_kernel<4>); break;
-    default: fn = reinterpret_cast<const void *>(&gemv_kernel<8>); break;
+    const bool fused = a.xb != nullptr;
+    switch (a.unroll * 2 + (fused ? 1 : 0)) {
+    case 4: fn = reinterpret_cast<const void *>(&gemv_kernel<2, false>); break;
+    case 5: fn = reinterpret_cast<const void *>(&gemv_kernel<2, true>); break;
+    case 8: fn = reinterpret_cast<const void *>(&gemv_kernel<4, false>); break;
+    case 9: fn = reinterpret_cast<const void *>(&gemv_kernel<4, true>); break;
+    case 17: fn = reinterpret_cast<const void *>(&gemv_kernel<8, true>); break;
+    default: fn = reinterpret_cast<const void *>(&gemv_kernel<8, false>); break;
     }
     // x: strip, y: k-range of the strip.
     return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
                            args, gemv_lds_bytes(a), stream);
+}
+
+hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream) {
+    return a.xb ? launch_gemv(a, stream) : hipErrorInvalidValue;
 }
 
 }  // namespace w2a8

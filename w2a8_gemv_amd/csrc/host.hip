@@ -294,6 +294,7 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     GemvLaunch a;
     a.wp = static_cast<const uint32_t *>(w_packed);
     a.x = x;
+    a.xb = nullptr;
     a.y_i32 = y_i32;
     a.y_f32 = y_f32;
     a.sa = s_a;
@@ -306,6 +307,41 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     gemv_plan_full(a.NS, K, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll, &a.G);
     hipError_t e = a.G > 0 ? launch_gemv_stream(a, static_cast<hipStream_t>(stream))
                            : launch_gemv(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+}
+
+// Fused linear layer for one token: quant_act_int8 + w2a8_gemv (fp32
+// epilogue) in one launch.  Always the workgroup kernel.
+int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, int64_t K, float s_w,
+                     float *y_f32, int32_t *y_i32, void *workspace, int64_t ws_bytes,
+                     void *stream) {
+    if (!w_packed || !x_bf16 || !y_f32 || !workspace) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    if (!aligned(w_packed, 16) || !aligned(x_bf16, 16) || !aligned(y_f32, 16) ||
+        (y_i32 && !aligned(y_i32, 16)) || !aligned(workspace, 16))
+        return W2A8_ERR_ALIGN;
+    if (ws_bytes < w2a8_workspace_bytes(1, N, K)) return W2A8_ERR_BUFSIZE;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+
+    const int64_t Np = round_up(N, kTileRows);
+    GemvLaunch a;
+    a.wp = static_cast<const uint32_t *>(w_packed);
+    a.x = nullptr;
+    a.xb = x_bf16;
+    a.y_i32 = y_i32;
+    a.y_f32 = y_f32;
+    a.sa = nullptr;
+    a.sw = s_w;
+    a.ws_row = static_cast<uint64_t *>(workspace);
+    a.N = int(N);
+    a.K = int(K);
+    a.KT = int(round_up(K, kTileK) / kTileK);
+    a.NS = int(Np / kTileRows);
+    a.G = 0;
+    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+    hipError_t e = launch_gemv_fused(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 

@@ -18,15 +18,6 @@ namespace {
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t q8(float x, float inv) {
-    float r = __builtin_rintf(x * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return uint32_t(uint8_t(int8_t(int(r))));
-}
-
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *xb, int M, int K, int8_t *xq,
                                                     float *sa) {
     const int m = blockIdx.x;

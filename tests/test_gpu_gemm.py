@@ -83,6 +83,55 @@ def test_gemm_forced_kernel_fp32_epilogue(kernel):
     np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw))
 
 
+# Few-row kernel (M <= 8) forced: every M, ragged N and K (K % 16 != 0 takes
+# the byte-wise activation path), long K (strips split over workgroups).
+FEW = [(2, 1, 1), (2, 33, 129), (3, 100, 300), (4, 257, 1000), (5, 64, 2560), (6, 97, 15),
+       (7, 1000, 4000), (8, 2560, 6912), (8, 13824, 2560), (3, 96, 27648), (8, 200, 10240)]
+
+
+@pytest.mark.parametrize("M,N,K", FEW)
+def test_gemm_few_rows_kernel(M, N, K):
+    w2a8.tune_gemm(3)
+    x, w = synth.gemm_case(M, N, K, seed=11 * M + N + 5 * K)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+
+
+@pytest.mark.parametrize("policy", [(1, 32, 8, 256, 10 ** 6), (64, 1, 8, 256, 1),
+                                    (2, 2, 8, 7, 1), (16, 32, 4, 1, 1)])
+def test_gemm_few_rows_forced_splits(policy):
+    try:
+        w2a8.tune_gemm(3)
+        w2a8.tune_gemv(*policy)
+        for M, N, K in [(4, 200, 3200), (8, 96, 27648), (2, 33, 1000)]:
+            x, w = synth.gemm_case(M, N, K, seed=M + N + K)
+            y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+            np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+def test_gemm_few_rows_fp32_epilogue_and_workspace_reset():
+    w2a8.tune_gemm(3)
+    M, N, K = 6, 700, 27648                 # strips split over workgroups
+    x, w = synth.gemm_case(M, N, K, seed=77)
+    rng = np.random.default_rng(3)
+    sa = (rng.random(M, dtype=np.float32) * 0.05 + 1e-3).astype(np.float32)
+    sw = np.float32(0.011)
+    wp, xd = packed_on_device(w), to_dev(x)
+    ws = torch.zeros(w2a8.workspace_bytes(M, N, K), dtype=torch.uint8, device=dev())
+    acc = oracle.gemm_i32(x, w)
+    for _ in range(3):
+        yi = torch.empty(M * N, dtype=torch.int32, device=dev())
+        yf = torch.empty(M * N, dtype=torch.float32, device=dev())
+        w2a8.w2a8_gemm(wp, xd, M, N, K, y_i32=yi, s_a=to_dev(sa), s_w=float(sw), y_f32=yf,
+                       workspace=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(yi.cpu().numpy().reshape(M, N), acc)
+        np.testing.assert_array_equal(yf.cpu().numpy().reshape(M, N), oracle.epilogue(acc, sa, sw))
+        assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
+
+
 @pytest.mark.parametrize("key", list(synth.GEMM_SEEDS.keys()),
                          ids=[f"{n}x{k}_M{m}" for (n, k), m in synth.GEMM_SEEDS.keys()])
 def test_gemm_prefill_shapes(key):

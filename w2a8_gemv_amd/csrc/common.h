@@ -55,6 +55,7 @@ struct GemvLaunch {
     float sw;
     uint64_t *ws_row;   // split-k combining word per padded row (split_word)
     int N, K, KT, NS;
+    int M;        // activation rows (the few-row kernel; 1 otherwise)
     int WK;       // waves per workgroup, splitting its k-range
     int SG;       // workgroups (k-ranges) per row strip
     int RUN;      // longest run of tiles of one wave (<= 32)
@@ -115,6 +116,13 @@ size_t gemv_lds_bytes(const GemvLaunch &a);
 bool gemv_stream_fits(int64_t K);
 size_t gemv_stream_lds_bytes(const GemvLaunch &a);
 hipError_t launch_gemv_stream(const GemvLaunch &a, hipStream_t stream);
+// Few activation rows (2 <= M <= 8): plan with runs of at most 8 tiles, and
+// the kernel (gemv.hip).  Workspace: 8 bytes per (row, padded output) when
+// strips are split.
+void gemv_rows_plan(int64_t NS, int64_t KT, int64_t M, int cus, int *wk, int *sg, int *run,
+                    int *unroll);
+hipError_t launch_gemv_rows(const GemvLaunch &a, hipStream_t stream);
+constexpr int64_t kRowsMaxM = 8;
 // Fused linear GEMV: quantize the bf16 row in every workgroup, then the
 // workgroup kernel with the fp32 epilogue (gemv.hip).
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream);
@@ -134,7 +142,8 @@ struct GemmShape {
 };
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split);
 // Kernel choice knob (w2a8_tune_gemm): 0 automatic, 1 pipelined kernel
-// whenever K allows it, 2 general kernel always.
+// whenever K allows it, 2 general kernel always, 3 few-row GEMV-style kernel
+// whenever M <= 8.  Modes 1 and 2 never pick the few-row kernel.
 int &gemm_kernel_mode();
 
 // Split-K is only ever used when M * Np <= kGemmSplitMaxOut, which bounds the

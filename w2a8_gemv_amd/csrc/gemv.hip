@@ -339,7 +339,222 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
         store_out(a, sa, row, v);
 }
 
+
+// ---------------------------------------------------------------------------
+// Few activation rows (2 <= M <= MR <= 8): the product of a short batch of
+// tokens with the same weight stream.  Same work split, layout, loads and
+// reductions as gemv_kernel; each lane decodes its weight words once (codes
+// c = w + 1 as bytes) and multiplies them against the M activation rows, each row
+// staged in its own LDS region of the wave (runs of at most 8 tiles, one
+// 16-byte chunk per lane per row).  Rows are y[m][n], row-major.
+// ---------------------------------------------------------------------------
+// With several rows the codes are shifted back to bytes 0..2 once per word
+// (shared by the rows), so each row keeps one accumulator per word instead
+// of three scaled ones: registers, not VALU, limit this kernel.
+struct AccR {
+    int a[4];
+};
+
+template <int MR>
+__device__ __forceinline__ void mac_rows(const v4u w, const v4u (&xv)[MR], AccR (&acc)[MR]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t v = w[q];
+        const uint32_t c0 = v & 0x03030303u, c1 = (v >> 2) & 0x03030303u,
+                       c2 = (v >> 4) & 0x03030303u, c3 = (v >> 6) & 0x03030303u;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            int s = dot4(c0, xv[m][0], acc[m].a[q]);
+            s = dot4(c1, xv[m][1], s);
+            s = dot4(c2, xv[m][2], s);
+            acc[m].a[q] = dot4(c3, xv[m][3], s);
+        }
+    }
+}
+
+template <int U, int MR>
+__device__ __forceinline__ void mac_batch_rows(const v4u (&w)[U], const uint8_t *xl, int rstride,
+                                               int n, int b, int kg, AccR (&acc)[MR]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (b * U + u < n) {
+            v4u xv[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                xv[m] = *reinterpret_cast<const v4u *>(xl + m * rstride + (b * U + u) * kTileK +
+                                                       16 * kg);
+            mac_rows<MR>(w[u], xv, acc);
+        }
+    }
+}
+
+// At most 32/MR waves per workgroup (the plan's limit), which leaves room
+// for MR rows of accumulators without spilling.
+template <int U, int MR>
+__global__ __launch_bounds__(2048 / MR) __attribute__((amdgpu_waves_per_eu(3)))
+void gemv_rows_kernel(GemvLaunch a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = int(blockIdx.x);
+    const int g = int(blockIdx.y);
+    const bool big = g < a.KR;
+    const int kt0 = g * a.KQ + min(g, a.KR);
+    const int ntile = a.KQ + (big ? 1 : 0);
+    const int wq = big ? a.WQ1 : a.WQ0, wr = big ? a.WR1 : a.WR0;
+    const int w0 = kt0 + wv * wq + min(wv, wr);
+    const int n = wq + (wv < wr ? 1 : 0);
+    const int w1 = w0 + n;
+    const int nb = (n + U - 1) / U;
+    const int kg = lane & 7, rg = lane >> 3;
+    const int M = a.M;
+
+    // LDS: per wave MR row regions of RUN tiles, then WK*MR*32 row partials.
+    const int rstride = a.RUN * kTileK;
+    uint8_t *xl = smem + wv * (MR * rstride);
+    int *red = reinterpret_cast<int *>(smem + a.WK * MR * rstride);
+
+    const v4u *wt = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords) + lane;
+    const int last = min(max(w0, w1 - 1), a.KT - 1);
+
+    // 1. Activation chunk `lane` of the run for each row (runs are at most 8
+    //    tiles: 64 chunks), before the weights; rows past M are zero.
+    const int kbase = w0 * kTileK;
+    const int nchunk = n * (kTileK / 16);
+    const int k0 = kbase + 16 * lane;
+    // Rows are 16-byte aligned only when K % 16 == 0; otherwise every chunk
+    // is assembled byte by byte (and the one straddling K is zero-padded).
+    v4u xr[MR];
+    const bool xvec = (a.K & 15) == 0;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        xr[m] = v4u{0u, 0u, 0u, 0u};
+        if (xvec && m < M && lane < nchunk && k0 + 16 <= a.K)
+            xr[m] = *reinterpret_cast<const v4u *>(a.x + int64_t(m) * a.K + k0);
+    }
+    if (!xvec && lane < nchunk && k0 < a.K) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= M) continue;
+            uint32_t b4[4] = {0u, 0u, 0u, 0u};
+            for (int i = 0; i < 16; ++i)
+                if (k0 + i < a.K)
+                    b4[i >> 2] |= uint32_t(uint8_t(a.x[int64_t(m) * a.K + k0 + i])) << (8 * (i & 3));
+            xr[m] = v4u{b4[0], b4[1], b4[2], b4[3]};
+        }
+    }
+
+    // 2. Two batches of weight loads in flight.
+    v4u wa[U], wb[U];
+    load_batch<U>(wt, w0, last, 0, wa);
+    load_batch<U>(wt, w0, last, 1, wb);
+
+    // 3. Stage each row's chunk in its LDS region and sum the rows.
+    int sx[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (lane < nchunk) *reinterpret_cast<v4u *>(xl + m * rstride + 16 * lane) = xr[m];
+        int t = dot4(xr[m][0], 0x01010101u, 0);
+        t = dot4(xr[m][1], 0x01010101u, t);
+        t = dot4(xr[m][2], 0x01010101u, t);
+        t = dot4(xr[m][3], 0x01010101u, t);
+        t = sum8(t);
+        t += __shfl_xor(t, 8);
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        sx[m] = t;
+    }
+
+    // 4. Stream the run.
+    AccR acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[m].a[q] = 0;
+    if (n > 0) {
+        int b = 0;
+        for (; b + 2 < nb; b += 2) {
+            mac_batch_rows<U, MR>(wa, xl, rstride, n, b, kg, acc);
+            load_batch<U>(wt, w0, last, b + 2, wa);
+            mac_batch_rows<U, MR>(wb, xl, rstride, n, b + 1, kg, acc);
+            load_batch<U>(wt, w0, last, b + 3, wb);
+        }
+        mac_batch_rows<U, MR>(wa, xl, rstride, n, b, kg, acc);
+        if (b + 1 < nb) mac_batch_rows<U, MR>(wb, xl, rstride, n, b + 1, kg, acc);
+    }
+
+    // 5. Per row: 8 lanes per row group, the run's sum x, then the waves.
+    int tot[MR];
+    int row;
+    bool owner;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        int r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = sum8(acc[m].a[q]);
+        tot[m] = (kg == 0 ? r[0] : kg == 1 ? r[1] : kg == 2 ? r[2] : r[3]) - sx[m];
+    }
+    if (a.WK == 1) {
+        row = s * kTileRows + rg * 4 + kg;
+        owner = kg < 4;
+    } else {
+        if (kg < 4)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) red[(m * a.WK + wv) * kTileRows + rg * 4 + kg] = tot[m];
+        __syncthreads();
+        row = s * kTileRows + tid;
+        owner = tid < kTileRows;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            tot[m] = 0;
+            if (owner)
+                for (int w = 0; w < a.WK; ++w) tot[m] += red[(m * a.WK + w) * kTileRows + tid];
+        }
+    }
+    if (!owner) return;
+    const int64_t Np = int64_t(a.NS) * kTileRows;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m >= M) break;
+        int v = tot[m];
+        if (a.SG > 1 && !split_add(a.ws_row + m * Np + row, ntile, tot[m], a.KT, &v)) continue;
+        if (row < a.N) {
+            const int64_t o = int64_t(m) * a.N + row;
+            if (a.y_i32) a.y_i32[o] = v;
+            if (a.y_f32) a.y_f32[o] = (float(v) * a.sa[m]) * a.sw;
+        }
+    }
+}
+
 }  // namespace
+
+size_t gemv_rows_lds_bytes(const GemvLaunch &a, int MR) {
+    return size_t(a.WK) * MR * a.RUN * kTileK + size_t(a.WK) * MR * kTileRows * 4;
+}
+
+hipError_t launch_gemv_rows(const GemvLaunch &la, hipStream_t stream) {
+    GemvLaunch a = la;
+    a.KQ = a.KT / a.SG;
+    a.KR = a.KT % a.SG;
+    a.WQ0 = a.KQ / a.WK;
+    a.WR0 = a.KQ % a.WK;
+    a.WQ1 = (a.KQ + 1) / a.WK;
+    a.WR1 = (a.KQ + 1) % a.WK;
+    void *args[] = {&a};
+    const int MR = a.M <= 2 ? 2 : a.M <= 4 ? 4 : 8;
+    const void *fn;
+    switch (MR * 10 + a.unroll) {
+    case 22: fn = reinterpret_cast<const void *>(&gemv_rows_kernel<2, 2>); break;
+    case 24: fn = reinterpret_cast<const void *>(&gemv_rows_kernel<4, 2>); break;
+    case 42: fn = reinterpret_cast<const void *>(&gemv_rows_kernel<2, 4>); break;
+    case 44: fn = reinterpret_cast<const void *>(&gemv_rows_kernel<4, 4>); break;
+    case 82: fn = reinterpret_cast<const void *>(&gemv_rows_kernel<2, 8>); break;
+    default: fn = reinterpret_cast<const void *>(&gemv_rows_kernel<4, 8>); break;
+    }
+    return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
+                           args, gemv_rows_lds_bytes(a, MR), stream);
+}
 
 size_t gemv_lds_bytes(const GemvLaunch &a) {
     // activation regions, row partials, and the fused kernel's per-wave maxima

@@ -107,6 +107,34 @@ void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int 
     *unroll = std::min(u, p.unroll);
 }
 
+// Few activation rows: the GEMV plan with runs of at most 8 tiles (one
+// activation chunk per lane per row) and at most 32/MR waves per workgroup
+// (LDS <= 36 KiB for the MR row regions); more workgroups per strip when
+// needed.
+void gemv_rows_plan(int64_t NS, int64_t KT, int64_t M, int cus, int *wk, int *sg, int *run,
+                    int *unroll) {
+    int r = 0;
+    gemv_plan(NS, KT, cus, wk, sg, &r, unroll);
+    const int64_t MR = M <= 2 ? 2 : M <= 4 ? 4 : 8;
+    const int64_t wkmax = 32 / MR;
+    int64_t SG = *sg, WK = *wk;
+    int64_t ktw = ceil_div(KT, SG);
+    if (WK > wkmax || r > 8) {
+        WK = std::min(wkmax, ceil_div(ktw, 8));
+        if (ceil_div(ktw, WK) > 8) {
+            SG = std::max(SG, ceil_div(KT, wkmax * 8));
+            ktw = ceil_div(KT, SG);
+            WK = std::min(wkmax, ceil_div(ktw, 8));
+        }
+        WK = std::max<int64_t>(1, std::min(WK, ktw));
+    }
+    const int64_t R = ceil_div(ktw, WK);
+    *wk = int(WK);
+    *sg = int(SG);
+    *run = int(R);
+    *unroll = R <= 4 ? 2 : 4;
+}
+
 // Large matrices (at least stream_min_tiles tiles, K staged whole in LDS)
 // use the streaming kernel: a grid of CUs * stream_waves_per_cu long-lived
 // waves, each streaming an equal contiguous share of the tiles.
@@ -164,6 +192,10 @@ int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M == 1) {
         // GEMV: one 64-bit split-k combining word per padded row.
         bytes = 8 * Np;
+    } else if (M <= kRowsMaxM) {
+        // Few rows: a combining word per (row, padded output), or the general
+        // kernel's split-K partials and counters, whichever is larger.
+        bytes = std::max(8 * M * Np, 4 * M * Np + 4 * ceil_div(M, 16) * ceil_div(NS, 4));
     } else if (M * Np <= kGemmSplitMaxOut) {
         // GEMM split-K: int32 partial per output + one counter per
         // (m-block of >= 16 rows, n-block of 4 strips).
@@ -295,6 +327,7 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.wp = static_cast<const uint32_t *>(w_packed);
     a.x = x;
     a.xb = nullptr;
+    a.M = 1;
     a.y_i32 = y_i32;
     a.y_f32 = y_f32;
     a.sa = s_a;
@@ -330,6 +363,7 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
     a.wp = static_cast<const uint32_t *>(w_packed);
     a.x = nullptr;
     a.xb = x_bf16;
+    a.M = 1;
     a.y_i32 = y_i32;
     a.y_f32 = y_f32;
     a.sa = nullptr;
@@ -382,6 +416,34 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
     a.shape = gemm_shape(M, N, K, dev.cus, need > 0);
+    // Few rows: the GEMV-style kernel over M activation rows.  Automatic
+    // choice (measured on MI355X): it wins for M <= 4 on every shape tried
+    // (M = 2: about 5.3 us against 9.4 us for the MFMA kernels), and up to M = 8
+    // where the MFMA path would fall back to the split-K general kernel.
+    const int mode = gemm_kernel_mode();
+    const bool few = M <= kRowsMaxM &&
+                     (mode == 3 || (mode == 0 && (M <= 4 || a.shape.pipe < 0)));
+    if (few) {
+        GemvLaunch g;
+        g.wp = a.wp;
+        g.x = x;
+        g.xb = nullptr;
+        g.y_i32 = y_i32;
+        g.y_f32 = y_f32;
+        g.sa = s_a;
+        g.sw = s_w;
+        g.ws_row = static_cast<uint64_t *>(workspace);
+        g.N = int(N);
+        g.K = int(K);
+        g.KT = a.KT;
+        g.NS = a.NS;
+        g.M = int(M);
+        g.G = 0;
+        gemv_rows_plan(g.NS, g.KT, M, dev.cus, &g.WK, &g.SG, &g.RUN, &g.unroll);
+        if (g.SG > 1 && !workspace) return W2A8_ERR_NULL;
+        hipError_t e = launch_gemv_rows(g, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+    }
     if (int64_t(a.shape.tiles) + 8 > int64_t(INT32_MAX)) return W2A8_ERR_SHAPE;
     hipError_t e = launch_gemm(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
@@ -417,7 +479,7 @@ int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_pe
 }
 
 int w2a8_tune_gemm(int kernel) {
-    if (kernel < 0 || kernel > 2) return W2A8_ERR_VALUE;
+    if (kernel < 0 || kernel > 3) return W2A8_ERR_VALUE;
     gemm_kernel_mode() = kernel;
     return W2A8_OK;
 }

@@ -404,6 +404,93 @@ def linear_extras(torch, w2a8, synth, lib, stream):
     return out
 
 
+# Decode projections of a 2560-wide layer that share one activation row:
+# query/key/value (2560 + 640 + 640 rows) and gate/up (2 x 6912 rows).
+GROUP_SETS = {"qkv": ([2560, 640, 640], 2560), "gate_up": ([6912, 6912], 2560)}
+
+
+def grouped_extras(torch, w2a8, synth, lib, stream):
+    """Several projections sharing x: one w2a8_gemv per projection against one
+    grouped launch (int8 x), and quant_act_int8 + those GEMVs against one
+    grouped linear launch (bf16 x), cold weights, fp32 outputs."""
+    import numpy as np
+    vp, F = ctypes.c_void_p, ctypes.c_float
+    out = {}
+    for name, (Ns, k) in GROUP_SETS.items():
+        G = len(Ns)
+        x, _ = synth.gemv_case(1, k, seed=50)
+        xb, _ = synth.linear_case(1, 1, k, seed=51)
+        wps = [w2a8.pack_ternary(torch.from_numpy(synth.gemv_case(n, k, seed=52 + g)[1]))
+               .to(stream.device) for g, n in enumerate(Ns)]
+        total = sum(w.numel() for w in wps)
+        slots = max(2, int(-(-ROTATE_BYTES // total)) + 1)   # copies of the whole set
+        sets = [wps] + [[w.clone() for w in wps] for _ in range(slots - 1)]
+        xd = torch.from_numpy(x).to(stream.device)
+        xbd = torch.from_numpy(xb.view(np.int16)).to(stream.device)
+        xq = torch.empty(k, dtype=torch.int8, device=stream.device)
+        sa = torch.full((1,), 0.02, dtype=torch.float32, device=stream.device)
+        ys = [torch.empty(n, dtype=torch.float32, device=stream.device) for n in Ns]
+        need = sum(w2a8.workspace_bytes(1, n, k) for n in Ns)
+        ws = torch.zeros(max(256, need), dtype=torch.uint8, device=stream.device)
+        sp = vp(stream.cuda_stream)
+        sw = [0.01 * (g + 1) for g in range(G)]
+        n_arr = (ctypes.c_int64 * G)(*Ns)
+        sw_arr = (ctypes.c_float * G)(*sw)
+        y_arr = (vp * G)(*[y.data_ptr() for y in ys])
+        w_arrs = [(vp * G)(*[w.data_ptr() for w in s]) for s in sets]
+
+        def gemvs(j, xp=None):
+            for g in range(G):
+                rc = lib.w2a8_gemv(vp(sets[j % slots][g].data_ptr()), xp or vp(xd.data_ptr()),
+                                   Ns[g], k, None, vp(sa.data_ptr()), F(sw[g]),
+                                   vp(ys[g].data_ptr()), vp(ws.data_ptr()), ws.numel(), sp)
+                if rc != 0:
+                    raise RuntimeError(f"w2a8_gemv failed with status {rc}")
+
+        def grouped(j):
+            rc = lib.w2a8_gemv_grouped(G, w_arrs[j % slots], n_arr, k, vp(xd.data_ptr()),
+                                       vp(sa.data_ptr()), sw_arr, None, y_arr,
+                                       vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a8_gemv_grouped failed with status {rc}")
+
+        def quant_gemvs(j):
+            rc = lib.quant_act_int8(vp(xbd.data_ptr()), 1, k, vp(xq.data_ptr()),
+                                    vp(sa.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"quant_act_int8 failed with status {rc}")
+            gemvs(j, vp(xq.data_ptr()))
+
+        def linear_grouped(j):
+            rc = lib.w2a8_linear_gemv_grouped(G, w_arrs[j % slots], n_arr, k,
+                                              vp(xbd.data_ptr()), sw_arr, y_arr, None,
+                                              vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a8_linear_gemv_grouped failed with status {rc}")
+
+        med = {}
+        for key, fn in (("separate", gemvs), ("grouped", grouped),
+                        ("linear_separate", quant_gemvs), ("linear_grouped", linear_grouped)):
+            ts = graph_times(torch, fn, 12, stream)
+            med[key] = sorted(ts)[len(ts) // 2]
+        wbytes = sum(n * k // 4 for n in Ns)
+        ybytes = 4 * sum(Ns)
+        out[name] = {"N": Ns, "K": k,
+                     "separate_us": round(med["separate"], 3),
+                     "grouped_us": round(med["grouped"], 3),
+                     "grouped_GBps": round((wbytes + k + ybytes) / med["grouped"] / 1e3, 1),
+                     "linear_separate_us": round(med["linear_separate"], 3),
+                     "linear_grouped_us": round(med["linear_grouped"], 3),
+                     "linear_grouped_GBps": round((wbytes + 2 * k + ybytes)
+                                                  / med["linear_grouped"] / 1e3, 1),
+                     "separate": f"{G} w2a8_gemv launches (linear: quant_act_int8 first)",
+                     "grouped": "one w2a8_gemv_grouped launch (linear: one "
+                                "w2a8_linear_gemv_grouped launch)"}
+        del sets, wps, xd, xbd, xq, sa, ys, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def host_call_us(torch, launcher, reps=50):
     """Mean latency of one synchronised call (the page's timeit(50) style)."""
     launcher(0)
@@ -604,6 +691,7 @@ def main():
         out["detail"]["gemm"] = gemm_extras(torch, w2a8, synth, lib, stream, cus)
         out["detail"]["gemm_peak_int8_TOPS"] = PEAK_INT8_TOPS
         out["detail"]["linear_13824x2560"] = linear_extras(torch, w2a8, synth, lib, stream)
+        out["detail"]["grouped_decode"] = grouped_extras(torch, w2a8, synth, lib, stream)
 
     if args.calibrate_copy:
         a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)

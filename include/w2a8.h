@@ -186,6 +186,45 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
                      float s_w, float *y_f32, int32_t *y_i32, void *workspace,
                      int64_t ws_bytes, void *stream);
 
+/* Most projections in one grouped call. */
+#define W2A8_MAX_GROUPS 8
+
+/* Several decode GEMVs that share the activation row and K, in one launch
+ * (for example a layer's query, key and value projections, or its gate and
+ * up projections).  For each projection g the result is exactly that of
+ *   w2a8_gemv(w_packed[g], x, N[g], K, y_i32[g], s_a, s_w[g], y_f32[g], ...):
+ *   y_i32[g][n] = sum_k w_g[n][k] * x[k]
+ *   y_f32[g][n] = ((float)y_i32[g][n] * s_a[0]) * s_w[g]
+ * ([TEST] "运行 test.py 做 GEMV 基准测试" / "如何判断结果" for the exact
+ * integer product, [WIN] §3.1 for the scales).  One launch instead of G
+ * saves the launch gaps and fills the device with the projections' strips
+ * together.
+ * G: 1 <= G <= W2A8_MAX_GROUPS.  w_packed, N, s_w: HOST arrays of G entries,
+ * read during the call only; w_packed[g] is a device T32x128 buffer of
+ * W_g [N[g]][K] (16-byte aligned).  y_i32, y_f32: HOST arrays of G device
+ * pointers, or NULL for no outputs of that kind; single entries may be NULL,
+ * but every projection needs at least one output.  x, s_a: as w2a8_gemv
+ * (s_a required when any y_f32 entry is given).  The padded rows
+ * (sum_g N[g] rounded up to 32 each) must not exceed 2^30.  workspace:
+ * device, at least sum_g w2a8_workspace_bytes(1, N[g], K) bytes, zeroed
+ * before first use.  Errors: W2A8_ERR_SHAPE for G or an N[g] out of range,
+ * otherwise as w2a8_gemv. */
+int w2a8_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int64_t K,
+                      const int8_t *x, const float *s_a, const float *s_w,
+                      int32_t *const *y_i32, float *const *y_f32, void *workspace,
+                      int64_t ws_bytes, void *stream);
+
+/* Grouped form of w2a8_linear_gemv: quantize the bf16 row (as
+ * quant_act_int8, M = 1) and apply G projections sharing it, in one launch;
+ * bit-identical to quant_act_int8 followed by w2a8_gemv_grouped.
+ * y_f32: HOST array of G device pointers, all required.  y_i32: HOST array
+ * of G device pointers (entries may be NULL), or NULL.  Other arguments as
+ * w2a8_gemv_grouped and w2a8_linear_gemv. */
+int w2a8_linear_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int64_t K,
+                             const uint16_t *x_bf16, const float *s_w, float *const *y_f32,
+                             int32_t *const *y_i32, void *workspace, int64_t ws_bytes,
+                             void *stream);
+
 /* W2A8 batched product, M >= 1 (prefill).
  * [TEST] "限制与注意事项": the reference handles only M == 1; this entry
  * computes the same product for M token rows:

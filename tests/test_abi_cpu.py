@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol():
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
                 "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemv_stream", "w2a8_tune_gemm",
-                "w2a8_linear_gemv"}
+                "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped"}
     assert expected.issubset(set(names)), set(names) ^ expected
     L = ctypes.CDLL(w2a8.LIB_PATH)
     for n in names:
@@ -214,6 +214,75 @@ def test_gemm_validation():
     assert _gemm(x=FAKE + 4) == ST["ALIGN"]
     assert _gemm(y=FAKE_ODD) == ST["ALIGN"]
     assert _gemm(wsb=w2a8.workspace_bytes(8, 64, 256) - 1) == ST["BUFSIZE"]
+
+
+def _linear(**kw):
+    a = dict(wp=FAKE, xb=FAKE, N=64, K=256, sw=1.0, yf=FAKE, y=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return w2a8.lib().w2a8_linear_gemv(a["wp"], a["xb"], a["N"], a["K"], F(a["sw"]), a["yf"],
+                                       a["y"], a["ws"], a["wsb"], None)
+
+
+def test_linear_gemv_validation():
+    assert _linear(wp=None) == ST["NULL"]
+    assert _linear(xb=None) == ST["NULL"]
+    assert _linear(yf=None) == ST["NULL"]          # the fp32 output is required
+    assert _linear(ws=None) == ST["NULL"]
+    assert _linear(N=0) == ST["SHAPE"]
+    assert _linear(K=1048448 + 1) == ST["SHAPE"]
+    assert _linear(xb=FAKE + 2) == ST["ALIGN"]
+    assert _linear(yf=FAKE_ODD) == ST["ALIGN"]
+    assert _linear(y=FAKE_ODD) == ST["ALIGN"]
+    assert _linear(wsb=w2a8.workspace_bytes(1, 64, 256) - 1) == ST["BUFSIZE"]
+
+
+def _arr(ctype, vals):
+    return None if vals is None else (ctype * len(vals))(*vals)
+
+
+def _grouped(linear=False, **kw):
+    Ns = kw.pop("Ns", [64, 33, 100])
+    G = len(Ns)
+    a = dict(G=G, wp=[FAKE] * G, x=FAKE, K=256, sa=FAKE, sw=[1.0] * G, y=[FAKE] * G,
+             yf=[FAKE] * G, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    L = w2a8.lib()
+    V, I64A = ctypes.c_void_p, ctypes.c_int64
+    args = (a["G"], _arr(V, a["wp"]), _arr(I64A, Ns), a["K"])
+    if linear:
+        return L.w2a8_linear_gemv_grouped(*args, a["x"], _arr(F, a["sw"]), _arr(V, a["yf"]),
+                                          _arr(V, a["y"]), a["ws"], a["wsb"], None)
+    return L.w2a8_gemv_grouped(*args, a["x"], a["sa"], _arr(F, a["sw"]), _arr(V, a["y"]),
+                               _arr(V, a["yf"]), a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("linear", [False, True], ids=["gemv", "linear"])
+def test_grouped_validation(linear):
+    g = lambda **kw: _grouped(linear, **kw)                      # noqa: E731
+    assert g(G=0) == ST["SHAPE"]
+    assert g(G=9, Ns=[64] * 9) == ST["SHAPE"]                    # more than W2A8_MAX_GROUPS
+    assert g(Ns=[64, 0, 100]) == ST["SHAPE"]
+    assert g(K=0) == ST["SHAPE"]
+    assert g(Ns=[1 << 30, 32]) == ST["SHAPE"]                    # padded rows above 2^30
+    assert g(wp=None) == ST["NULL"]
+    assert g(wp=[FAKE, None, FAKE]) == ST["NULL"]
+    assert g(sw=None) == ST["NULL"]
+    assert g(x=None) == ST["NULL"]
+    assert g(ws=None) == ST["NULL"]
+    if linear:
+        assert g(yf=None) == ST["NULL"]
+    assert g(wp=[FAKE, FAKE + 8, FAKE]) == ST["ALIGN"]
+    assert g(yf=[FAKE, FAKE, FAKE_ODD]) == ST["ALIGN"]
+    assert g(y=[FAKE_ODD, FAKE, FAKE]) == ST["ALIGN"]
+    assert g(x=FAKE + 2) == ST["ALIGN"]
+    need = sum(w2a8.workspace_bytes(1, n, 256) for n in (64, 33, 100))
+    assert g(wsb=need - 1) == ST["BUFSIZE"]
+    if linear:
+        assert g(yf=[FAKE, None, FAKE]) == ST["NULL"]          # every fp32 output required
+    else:
+        assert g(y=[FAKE, None, FAKE], yf=[FAKE, None, FAKE]) == ST["NULL"]   # no output
+        assert g(sa=None) == ST["NULL"]                          # y_f32 needs s_a
+        assert g(sa=FAKE + 2) == ST["ALIGN"]
 
 
 def test_quant_validation():

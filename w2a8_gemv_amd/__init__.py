@@ -75,6 +75,10 @@ def lib():
         L.w2a8_gemm.restype = I32
         L.w2a8_linear_gemv.argtypes = [P, P, I64, I64, F32, P, P, P, I64, P]
         L.w2a8_linear_gemv.restype = I32
+        L.w2a8_gemv_grouped.argtypes = [I32, P, P, I64, P, P, P, P, P, P, I64, P]
+        L.w2a8_gemv_grouped.restype = I32
+        L.w2a8_linear_gemv_grouped.argtypes = [I32, P, P, I64, P, P, P, P, P, I64, P]
+        L.w2a8_linear_gemv_grouped.restype = I32
         L.w2a8_tune_gemv.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv.restype = I32
         L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
@@ -294,6 +298,80 @@ def w2a8_linear_gemv(w_packed, x_bf16, N, K, s_w, y_f32, y_i32=None, workspace=N
     _check(lib().w2a8_linear_gemv(_ptr(w_packed), _ptr(x_bf16), N, K, ctypes.c_float(s_w),
                                   _ptr(y_f32), _ptr(y_i32), _ptr(ws), ws.numel(),
                                   _stream_handle(stream)), "w2a8_linear_gemv")
+
+
+MAX_GROUPS = 8
+
+
+def _host_array(ctype, values):
+    return (ctype * len(values))(*values)
+
+
+def _grouped_args(w_packed, Ns, K, s_w, y_i32, y_f32):
+    G = len(w_packed)
+    if not (1 <= G <= MAX_GROUPS) or len(Ns) != G or len(s_w) != G:
+        raise ValueError(f"need 1..{MAX_GROUPS} projections with one N and one s_w each")
+    for g, (w, n) in enumerate(zip(w_packed, Ns)):
+        _need(w, f"w_packed[{g}]", torch.uint8, "cuda")
+        if w.numel() < packed_bytes(n, K):
+            raise ValueError(f"w_packed[{g}] is smaller than packed_bytes(N[{g}], K)")
+    arrays = []
+    for ys, nm, dt in ((y_i32, "y_i32", torch.int32), (y_f32, "y_f32", torch.float32)):
+        if ys is None:
+            arrays.append(None)
+            continue
+        if len(ys) != G:
+            raise ValueError(f"{nm} must have one entry per projection")
+        for g, (y, n) in enumerate(zip(ys, Ns)):
+            if y is not None:
+                _need(y, f"{nm}[{g}]", dt, "cuda")
+                if y.numel() != n:
+                    raise ValueError(f"{nm}[{g}] must have N[{g}] elements")
+        arrays.append(_host_array(ctypes.c_void_p, [None if y is None else y.data_ptr() for y in ys]))
+    need = sum(workspace_bytes(1, n, K) for n in Ns)
+    return (G, _host_array(ctypes.c_void_p, [w.data_ptr() for w in w_packed]),
+            _host_array(ctypes.c_int64, list(Ns)), _host_array(ctypes.c_float, list(s_w)),
+            arrays[0], arrays[1], need)
+
+
+def w2a8_gemv_grouped(w_packed, x, Ns, K, s_w, y_i32=None, y_f32=None, s_a=None,
+                      workspace=None, stream=None):
+    """Raw C-ABI call: several projections (lists of equal length) sharing one
+    int8 activation row x [K], in one launch; returns nothing."""
+    _need(x, "x", torch.int8, "cuda")
+    if x.numel() != K:
+        raise ValueError("x must have K elements")
+    if s_a is not None:
+        _need(s_a, "s_a", torch.float32, "cuda")
+    G, wp, n_arr, sw_arr, yi_arr, yf_arr, need = _grouped_args(w_packed, Ns, K, s_w, y_i32, y_f32)
+    ws = _ws(need, x.device, stream, workspace)
+    _check(lib().w2a8_gemv_grouped(G, wp, n_arr, K, _ptr(x), _ptr(s_a), sw_arr, yi_arr, yf_arr,
+                                   _ptr(ws), ws.numel(), _stream_handle(stream)),
+           "w2a8_gemv_grouped")
+
+
+def w2a8_linear_gemv_grouped(w_packed, x_bf16, Ns, K, s_w, y_f32, y_i32=None, workspace=None,
+                             stream=None):
+    """Raw C-ABI call: quantize one bf16 token and apply several projections
+    to it, in one launch; returns nothing."""
+    if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not x_bf16.is_cuda:
+        raise TypeError("x_bf16 must be a bfloat16 (or 16-bit bit pattern) CUDA tensor")
+    if not x_bf16.is_contiguous() or x_bf16.numel() != K:
+        raise ValueError("x_bf16 must be contiguous with K elements")
+    G, wp, n_arr, sw_arr, yi_arr, yf_arr, need = _grouped_args(w_packed, Ns, K, s_w, y_i32, y_f32)
+    ws = _ws(need, x_bf16.device, stream, workspace)
+    _check(lib().w2a8_linear_gemv_grouped(G, wp, n_arr, K, _ptr(x_bf16), sw_arr, yf_arr, yi_arr,
+                                          _ptr(ws), ws.numel(), _stream_handle(stream)),
+           "w2a8_linear_gemv_grouped")
+
+
+def linear_grouped(x_bf16, w_packed, s_w, Ns, K, stream=None):
+    """Several W2A8 linear layers applied to one bf16 token (one launch):
+    returns a list of fp32 [1, N_g] outputs."""
+    ys = [torch.empty((1, n), dtype=torch.float32, device=x_bf16.device) for n in Ns]
+    w2a8_linear_gemv_grouped(w_packed, x_bf16.reshape(-1), Ns, K, s_w, [y.view(-1) for y in ys],
+                             stream=stream)
+    return ys
 
 
 def gemv(w_packed, x, N, K, *, out_i32=True, s_a=None, s_w=1.0, stream=None):

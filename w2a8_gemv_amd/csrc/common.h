@@ -68,6 +68,21 @@ struct GemvLaunch {
     // v starts v*WQi + min(v, WRi) tiles in).
     int KQ, KR, WQ0, WR0, WQ1, WR1;
 };
+// Grouped GEMV: up to kMaxGroups projections sharing the activation row and K
+// in one launch (passed to the kernel by value, next to GemvLaunch, whose NS
+// is then the total strip count).  Projection i owns strips [begin[i],
+// begin[i+1]); unused entries have begin = INT32_MAX.
+constexpr int kMaxGroups = W2A8_MAX_GROUPS;
+struct GemvGroups {
+    int begin[kMaxGroups];
+    int N[kMaxGroups];
+    float sw[kMaxGroups];
+    const uint32_t *wp[kMaxGroups];
+    int32_t *y_i32[kMaxGroups];
+    float *y_f32[kMaxGroups];
+};
+hipError_t launch_gemv_grouped(const GemvLaunch &a, const GemvGroups &t, hipStream_t stream);
+
 // Activation quantization, per element (shared by the quantizer kernel and
 // the fused linear GEMV so both produce the same codes): bf16 halves of a
 // 32-bit word as fp32, and q = clamp(round_half_even(x * inv), -127, 127)

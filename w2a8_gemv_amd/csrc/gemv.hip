@@ -73,9 +73,43 @@ __device__ __forceinline__ int sum8(int v) {
     return v;
 }
 
-__device__ __forceinline__ void store_out(const GemvLaunch &a, float sa, int row, int v) {
-    if (a.y_i32) a.y_i32[row] = v;
-    if (a.y_f32) a.y_f32[row] = (float(v) * sa) * a.sw;
+// The projection a strip belongs to.  Plain launch: the launch's own matrix
+// and outputs.  Grouped launch (several projections sharing the activation
+// row and K): strips are numbered across the projections in order and
+// projection i owns strips [begin[i], begin[i+1]); begin is increasing and
+// padded with INT32_MAX, so the choice is a chain of uniform selects over
+// values already in the kernel arguments, with no dependent load.
+struct Proj {
+    const uint32_t *wp;
+    int32_t *y_i32;
+    float *y_f32;
+    float sw;
+    int N;
+    int s;   // strip index within the projection
+};
+
+template <bool GROUPED>
+__device__ __forceinline__ Proj select_proj(const GemvLaunch &a, const GemvGroups &t, int s) {
+    Proj p{a.wp, a.y_i32, a.y_f32, a.sw, a.N, s};
+    if constexpr (GROUPED) {
+        // The last projection that begins at or before s owns it.
+#pragma unroll
+        for (int i = 0; i < kMaxGroups; ++i) {
+            const bool hit = s >= t.begin[i];
+            p.wp = hit ? t.wp[i] : p.wp;
+            p.y_i32 = hit ? t.y_i32[i] : p.y_i32;
+            p.y_f32 = hit ? t.y_f32[i] : p.y_f32;
+            p.sw = hit ? t.sw[i] : p.sw;
+            p.N = hit ? t.N[i] : p.N;
+            p.s = hit ? s - t.begin[i] : p.s;
+        }
+    }
+    return p;
+}
+
+__device__ __forceinline__ void store_proj(const Proj &p, float sa, int row, int v) {
+    if (p.y_i32) p.y_i32[row] = v;
+    if (p.y_f32) p.y_f32[row] = (float(v) * sa) * p.sw;
 }
 
 // Largest |x| of bf16 words (8 values per v4u... 2 per word).
@@ -132,8 +166,11 @@ __device__ __forceinline__ void mac_batch(const v4u (&w)[U], const uint8_t *xl, 
 // per-element operations as the quantizer kernel (q8 in common.h) and scale
 // s_a = amax/127, so the result is bit-identical to quant_act_int8 followed
 // by the plain GEMV, in one launch.
-template <int U, bool FUSED>
-__global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
+// GROUPED: the strip's matrix, outputs and weight scale come from the
+// projection table t (select_proj); the split-k workspace words are indexed
+// by the strip's position in the whole launch.
+template <int U, bool FUSED, bool GROUPED>
+__device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -144,6 +181,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     // load.
     const int s = int(blockIdx.x);
     const int g = int(blockIdx.y);
+    const Proj pj = select_proj<GROUPED>(a, t, s);
     const bool big = g < a.KR;
     const int kt0 = g * a.KQ + min(g, a.KR);
     const int ntile = a.KQ + (big ? 1 : 0);
@@ -158,7 +196,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     uint8_t *xl = smem + wv * (a.RUN * kTileK);
     int *red = reinterpret_cast<int *>(smem + a.WK * a.RUN * kTileK);   // WK*32 ints
 
-    const v4u *wt = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords) + lane;
+    const v4u *wt =
+        reinterpret_cast<const v4u *>(pj.wp + int64_t(pj.s) * a.KT * kTileWords) + lane;
     // Last tile a load may touch: the run's last tile, or (for an empty run)
     // a tile of this strip, never past it.
     const int last = min(max(w0, w1 - 1), a.KT - 1);
@@ -311,32 +350,43 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
     // Lane (rg, kg) with kg < 4 owns row 4rg + kg of the strip.
     const int mine = (kg == 0 ? r[0] : kg == 1 ? r[1] : kg == 2 ? r[2] : r[3]) - sx;
     int tot = 0;
-    int row;
+    int r32;   // row within the strip
     bool owner;
     if (a.WK == 1) {
         tot = mine;
-        row = s * kTileRows + rg * 4 + kg;
+        r32 = rg * 4 + kg;
         owner = kg < 4;
     } else {
         if (kg < 4) red[wv * kTileRows + rg * 4 + kg] = mine;
         __syncthreads();
-        row = s * kTileRows + tid;
+        r32 = tid;
         owner = tid < kTileRows;
         if (owner)
             for (int w = 0; w < a.WK; ++w) tot += red[w * kTileRows + tid];
     }
+    const int row = pj.s * kTileRows + r32;
 
-    if constexpr (!FUSED) sa = a.y_f32 ? a.sa[0] : 0.0f;
+    if constexpr (!FUSED) sa = pj.y_f32 ? a.sa[0] : 0.0f;
     if (a.SG == 1) {
-        if (owner && row < a.N) store_out(a, sa, row, tot);
+        if (owner && row < pj.N) store_proj(pj, sa, row, tot);
         return;
     }
     // k-range split over workgroups: one device-scope atomic per row (coherent
     // across the XCDs' L2s) combines the partials; the last contributor of a
     // row stores it.
     int v;
-    if (owner && split_add(a.ws_row + row, ntile, tot, a.KT, &v) && row < a.N)
-        store_out(a, sa, row, v);
+    if (owner && split_add(a.ws_row + s * kTileRows + r32, ntile, tot, a.KT, &v) && row < pj.N)
+        store_proj(pj, sa, row, v);
+}
+
+template <int U, bool FUSED>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
+    gemv_body<U, FUSED, false>(a, GemvGroups{});
+}
+
+template <int U, bool FUSED>
+__global__ __launch_bounds__(1024) void gemv_grouped_kernel(GemvLaunch a, GemvGroups t) {
+    gemv_body<U, FUSED, true>(a, t);
 }
 
 
@@ -587,6 +637,30 @@ hipError_t launch_gemv(const GemvLaunch &la, hipStream_t stream) {
 
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream) {
     return a.xb ? launch_gemv(a, stream) : hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_grouped(const GemvLaunch &la, const GemvGroups &t, hipStream_t stream) {
+    GemvLaunch a = la;
+    a.KQ = a.KT / a.SG;
+    a.KR = a.KT % a.SG;
+    a.WQ0 = a.KQ / a.WK;
+    a.WR0 = a.KQ % a.WK;
+    a.WQ1 = (a.KQ + 1) / a.WK;
+    a.WR1 = (a.KQ + 1) % a.WK;
+    GemvGroups tt = t;
+    void *args[] = {&a, &tt};
+    const void *fn;
+    const bool fused = a.xb != nullptr;
+    switch (a.unroll * 2 + (fused ? 1 : 0)) {
+    case 4: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<2, false>); break;
+    case 5: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<2, true>); break;
+    case 8: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<4, false>); break;
+    case 9: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<4, true>); break;
+    case 17: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<8, true>); break;
+    default: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<8, false>); break;
+    }
+    return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
+                           args, gemv_lds_bytes(a), stream);
 }
 
 }  // namespace w2a8

@@ -380,6 +380,121 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMV: several projections sharing x and K in one launch
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// Validates the projection arrays and fills the table; the launch's NS is
+// the total strip count.  `need_f32` makes every y_f32 entry mandatory.
+int grouped_setup(int G, const void *const *w_packed, const int64_t *N, int64_t K,
+                  const float *s_w, int32_t *const *y_i32, float *const *y_f32, bool need_f32,
+                  GemvGroups *t, int64_t *ns_total, int64_t *ws_need, bool *any_f32) {
+    if (G < 1 || G > kMaxGroups) return W2A8_ERR_SHAPE;
+    if (!w_packed || !N || !s_w) return W2A8_ERR_NULL;
+    if (need_f32 && !y_f32) return W2A8_ERR_NULL;
+    int64_t ns = 0, ws = 0;
+    *any_f32 = false;
+    for (int g = 0; g < G; ++g) {
+        if (!nk_ok(N[g], K)) return W2A8_ERR_SHAPE;
+        int32_t *yi = y_i32 ? y_i32[g] : nullptr;
+        float *yf = y_f32 ? y_f32[g] : nullptr;
+        if (!w_packed[g] || (!yi && !yf) || (need_f32 && !yf)) return W2A8_ERR_NULL;
+        if (!aligned(w_packed[g], 16) || (yi && !aligned(yi, 16)) || (yf && !aligned(yf, 16)))
+            return W2A8_ERR_ALIGN;
+        *any_f32 = *any_f32 || yf != nullptr;
+        const int64_t Np = round_up(N[g], kTileRows);
+        t->begin[g] = int(ns);
+        t->N[g] = int(N[g]);
+        t->sw[g] = s_w[g];
+        t->wp[g] = static_cast<const uint32_t *>(w_packed[g]);
+        t->y_i32[g] = yi;
+        t->y_f32[g] = yf;
+        ns += Np / kTileRows;
+        ws += w2a8_workspace_bytes(1, N[g], K);
+        if (ns * kTileRows > kMaxN) return W2A8_ERR_SHAPE;
+    }
+    for (int g = G; g < kMaxGroups; ++g) {
+        t->begin[g] = INT32_MAX;
+        t->N[g] = 0;
+        t->sw[g] = 0.0f;
+        t->wp[g] = nullptr;
+        t->y_i32[g] = nullptr;
+        t->y_f32[g] = nullptr;
+    }
+    *ns_total = ns;
+    *ws_need = ws;
+    return W2A8_OK;
+}
+
+int grouped_launch(const GemvGroups &t, int64_t ns, int64_t K, const int8_t *x,
+                   const uint16_t *xb, const float *s_a, void *workspace, void *stream) {
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+    GemvLaunch a;
+    a.wp = nullptr;
+    a.x = x;
+    a.xb = xb;
+    a.M = 1;
+    a.y_i32 = nullptr;
+    a.y_f32 = nullptr;
+    a.sa = s_a;
+    a.sw = 0.0f;
+    a.ws_row = static_cast<uint64_t *>(workspace);
+    a.N = int(ns * kTileRows);
+    a.K = int(K);
+    a.KT = int(round_up(K, kTileK) / kTileK);
+    a.NS = int(ns);
+    a.G = 0;
+    // One plan for the whole launch, as for a matrix of all the strips.
+    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+    hipError_t e = launch_gemv_grouped(a, t, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w2a8_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int64_t K,
+                      const int8_t *x, const float *s_a, const float *s_w,
+                      int32_t *const *y_i32, float *const *y_f32, void *workspace,
+                      int64_t ws_bytes, void *stream) {
+    GemvGroups t;
+    int64_t ns = 0, need = 0;
+    bool any_f32 = false;
+    int st = grouped_setup(G, w_packed, N, K, s_w, y_i32, y_f32, false, &t, &ns, &need, &any_f32);
+    if (st != W2A8_OK) return st;
+    if (!x || !workspace) return W2A8_ERR_NULL;
+    if (any_f32 && !s_a) return W2A8_ERR_NULL;
+    if (!aligned(x, 16) || (s_a && !aligned(s_a, 4)) || !aligned(workspace, 16))
+        return W2A8_ERR_ALIGN;
+    if (ws_bytes < need) return W2A8_ERR_BUFSIZE;
+    return grouped_launch(t, ns, K, x, nullptr, s_a, workspace, stream);
+}
+
+int w2a8_linear_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int64_t K,
+                             const uint16_t *x_bf16, const float *s_w, float *const *y_f32,
+                             int32_t *const *y_i32, void *workspace, int64_t ws_bytes,
+                             void *stream) {
+    GemvGroups t;
+    int64_t ns = 0, need = 0;
+    bool any_f32 = false;
+    int st = grouped_setup(G, w_packed, N, K, s_w, y_i32, y_f32, true, &t, &ns, &need, &any_f32);
+    if (st != W2A8_OK) return st;
+    if (!x_bf16 || !workspace) return W2A8_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(workspace, 16)) return W2A8_ERR_ALIGN;
+    if (ws_bytes < need) return W2A8_ERR_BUFSIZE;
+    return grouped_launch(t, ns, K, nullptr, x_bf16, nullptr, workspace, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+// ---------------------------------------------------------------------------
 // a8: batched product (device)
 // ---------------------------------------------------------------------------
 int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64_t K,

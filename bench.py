@@ -83,14 +83,16 @@ def parse_args():
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="skip the per-shape cold timings and read floors (counter runs)")
     ap.add_argument("--eager", action="store_true",
                     help="launch each GEMV from the host instead of replaying graphs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "`bench.py --steps 4 --warmup 1 --no-extra --no-cpu-baseline "
-                         "--calibrate-copy` into " + os.path.relpath(TRAFFIC_FILE, ROOT))
+                         "`bench.py --steps 4 --warmup 1 --no-extra --no-detail "
+                         "--no-cpu-baseline --calibrate-copy` into " + os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
 
 
@@ -141,9 +143,11 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
            "per_shape": shapes,
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python -u "
-               "bench.py --steps 4 --warmup 1 --no-extra --no-cpu-baseline --calibrate-copy",
+               "bench.py --steps 4 --warmup 1 --no-extra --no-detail --no-cpu-baseline "
+               "--calibrate-copy",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python -u "
-               "bench.py --steps 4 --warmup 1 --no-extra --no-cpu-baseline --calibrate-copy",
+               "bench.py --steps 4 --warmup 1 --no-extra --no-detail --no-cpu-baseline "
+               "--calibrate-copy",
                "python bench.py --traffic-summary <fetch_counter_collection.csv> "
                "<write_counter_collection.csv>"]}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -677,7 +681,7 @@ def main():
     traffic = traffic_summary()
     readref = load_readref()
     per = []
-    for s in shapes:
+    for s in ([] if args.no_detail else shapes):
         solo, _ = make_shapes(torch, w2a8, synth, [(s.n, s.k, s.seed, s.sparse)], args.mode, dev)
         per.append(shape_detail(torch, lib, readref, solo[0], stream))
         del solo

@@ -12,6 +12,9 @@ Functions (parity status in ``oracle.c``):
   epilogue(acc, sa, sw)          O4  fp32 scale epilogue
   pack(w) / unpack(p, N, K)      a2  2-bit packing per the T32x128 layout
   packed_bytes(N, K)
+  quant_act_a4(x_bf16_bits)      O5  per-token absmax int4 quantization
+  pack_act4(q) / unpack_act4(b, M, K), act4_bytes(M, K)
+                                     int4 activation layout "A4I"
 """
 from __future__ import annotations
 
@@ -49,6 +52,14 @@ def _load():
     lib.oracle_pack.restype = ctypes.c_int
     lib.oracle_unpack.argtypes = [P, I64, I64, P]
     lib.oracle_unpack.restype = ctypes.c_int
+    lib.oracle_quant_act_a4.argtypes = [P, I64, I64, P, P]
+    lib.oracle_quant_act_a4.restype = None
+    lib.oracle_act4_bytes.argtypes = [I64, I64]
+    lib.oracle_act4_bytes.restype = I64
+    lib.oracle_pack_act4.argtypes = [P, I64, I64, P]
+    lib.oracle_pack_act4.restype = ctypes.c_int
+    lib.oracle_unpack_act4.argtypes = [P, I64, I64, P]
+    lib.oracle_unpack_act4.restype = None
     _lib = lib
     return lib
 
@@ -123,3 +134,36 @@ def unpack(p: np.ndarray, N: int, K: int) -> np.ndarray:
     if _load().oracle_unpack(_ptr(p2), N, K, _ptr(w)) != 0:
         raise ValueError("code 11 found in packed matrix")
     return w
+
+
+def quant_act_a4(xb: np.ndarray):
+    """xb: uint16 bf16 bit patterns [M, K] -> (q int8 [M, K] in -7..7, sa fp32 [M])."""
+    x2 = np.ascontiguousarray(np.atleast_2d(xb), dtype=np.uint16)
+    M, K = x2.shape
+    q = np.empty((M, K), dtype=np.int8)
+    sa = np.empty(M, dtype=np.float32)
+    _load().oracle_quant_act_a4(_ptr(x2), M, K, _ptr(q), _ptr(sa))
+    return q, sa
+
+
+def act4_bytes(M: int, K: int) -> int:
+    return int(_load().oracle_act4_bytes(M, K))
+
+
+def pack_act4(q: np.ndarray) -> np.ndarray:
+    """q int8 [M, K] (values -8..7) -> uint8 [act4_bytes(M, K)] in the A4I layout."""
+    q2 = np.ascontiguousarray(np.atleast_2d(q), dtype=np.int8)
+    M, K = q2.shape
+    out = np.empty(act4_bytes(M, K), dtype=np.uint8)
+    if _load().oracle_pack_act4(_ptr(q2), M, K, _ptr(out)) != 0:
+        raise ValueError("activation outside -8..7")
+    return out
+
+
+def unpack_act4(b: np.ndarray, M: int, K: int) -> np.ndarray:
+    b2 = np.ascontiguousarray(b, dtype=np.uint8)
+    if b2.size < act4_bytes(M, K):
+        raise ValueError("buffer too small")
+    q = np.empty((M, K), dtype=np.int8)
+    _load().oracle_unpack_act4(_ptr(b2), M, K, _ptr(q))
+    return q

@@ -243,3 +243,105 @@ int oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *w)
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* O5. Per-token absmax int4 activation quantization (W2A4 variant).
+ *
+ * "微软BitNet：1-bit量化大模型CPU部署实践" (its GPU runtime section) names an
+ * "a4.8" extension with lower-precision activations and gives no formula.
+ * Reading: the O3 quantizer with 4-bit signed codes, 7 levels each side:
+ *   a = max_k |x[m][k]|
+ *   inv = 7 / a                         (fp32 division)
+ *   q[m][k] = clamp(round_half_even(x[m][k] * inv), -7, 7)
+ *   sa[m] = a / 7                       (fp32 division, not 1/inv)
+ * A row of zeros gives q = 0 and sa = 0.  The product with ternary weights is
+ * then O1 on these values, and the epilogue O4 with this sa.
+ */
+void oracle_quant_act_a4(const uint16_t *xb, int64_t M, int64_t K, int8_t *xq,
+                         float *sa)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = xb + m * K;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(bf16_to_f32(row[k]));
+            if (v > a) a = v;
+        }
+        if (a == 0.0f) {
+            for (int64_t k = 0; k < K; ++k) xq[m * K + k] = 0;
+            sa[m] = 0.0f;
+            continue;
+        }
+        volatile float inv = 7.0f / a;
+        for (int64_t k = 0; k < K; ++k) {
+            volatile float p = bf16_to_f32(row[k]) * inv;
+            float r = nearbyintf(p);
+            if (r > 7.0f) r = 7.0f;
+            if (r < -7.0f) r = -7.0f;
+            xq[m * K + k] = (int8_t)r;
+        }
+        volatile float s = a / 7.0f;
+        sa[m] = s;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* a4 activation layout "A4I" (this project's own; the pages give none).
+ *
+ * Signed 4-bit values (two's complement nibbles, -8..7) of a row of K
+ * activations, the row padded with zeros to a multiple of 32 values:
+ * Kq = ceil(K/32)*32 values, Kq/2 bytes per row, rows back to back.
+ * Element k of row m:
+ *     c = k/16, i = k%16, h = i/4, j = i%4
+ *     byte  = m*(Kq/2) + c*8 + 4*(h%2) + j
+ *     shift = 4*(h/2)       (low nibble for h < 2, high nibble otherwise)
+ * Why this order: in a T32x128 weight word (see the packing above) byte j
+ * holds the codes of k = j, 4+j, 8+j, 12+j in bit pairs 0, 2, 4, 6.  The
+ * masks 0x33333333 and (word>>2) & 0x33333333 put the codes of
+ * {k = j, 8+j} and {k = 4+j, 12+j} into the nibbles of byte j, which are
+ * exactly where this layout puts those activations in the chunk's first and
+ * second 32-bit words.
+ *
+ * oracle_pack_act4 returns 0, or -1 if a value is outside -8..7.
+ */
+int64_t oracle_act4_bytes(int64_t M, int64_t K)
+{
+    return M * (ceil_to(K, 32) / 2);
+}
+
+static void locate4(int64_t m, int64_t k, int64_t K, int64_t *byte, int *shift)
+{
+    int64_t c = k / 16, i = k % 16, h = i / 4, j = i % 4;
+    *byte = m * (ceil_to(K, 32) / 2) + c * 8 + 4 * (h % 2) + j;
+    *shift = (int)(4 * (h / 2));
+}
+
+int oracle_pack_act4(const int8_t *q, int64_t M, int64_t K, uint8_t *out)
+{
+    memset(out, 0, (size_t)oracle_act4_bytes(M, K));
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            int v = q[m * K + k];
+            if (v < -8 || v > 7)
+                return -1;
+            int64_t byte;
+            int shift;
+            locate4(m, k, K, &byte, &shift);
+            out[byte] = (uint8_t)(out[byte] | (((unsigned)v & 15u) << shift));
+        }
+    }
+    return 0;
+}
+
+void oracle_unpack_act4(const uint8_t *in, int64_t M, int64_t K, int8_t *q)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t byte;
+            int shift;
+            locate4(m, k, K, &byte, &shift);
+            int v = (in[byte] >> shift) & 15;
+            q[m * K + k] = (int8_t)(v >= 8 ? v - 16 : v);
+        }
+    }
+}

@@ -303,6 +303,134 @@ def test_unpack_rejects_code_11():
         oracle.unpack(p, 1, 1)
 
 
+# --------------------------------------------------------------------------
+# O5: per-token absmax int4 quantization (W2A4 variant)
+# --------------------------------------------------------------------------
+
+def quant_a4_pins(quant):
+    for ex in _load("worked_examples.json")["quant_act_a4"]:
+        q, sa = quant(_bf16([ex["x"]]))
+        np.testing.assert_array_equal(q[0], ex["q"])
+        assert sa[0] == np.float32(ex["sa_num"]) / np.float32(ex["sa_den"])
+    q, sa = quant(_bf16(np.zeros((1, 17))))
+    assert np.all(q == 0) and sa[0] == 0.0
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((5, 301)).astype(np.float32)
+    x[3, 7] = -25.0
+    xb = _bf16(x)
+    xf = synth.bf16_bits_to_fp32(xb)
+    q, sa = quant(xb)
+    assert q.min() >= -7 and q.max() <= 7
+    for m in range(5):
+        i = int(np.argmax(np.abs(xf[m])))
+        assert abs(int(q[m, i])) == 7
+        assert sa[m] == np.float32(np.abs(xf[m]).max()) / np.float32(7.0)
+        qm, sam = quant(xb[m:m + 1])
+        np.testing.assert_array_equal(qm[0], q[m])
+        assert sam[0] == sa[m]
+        o = np.argsort(xf[m], kind="stable")
+        assert np.all(np.diff(q[m][o].astype(int)) >= 0)
+    # at most half a step of reconstruction error
+    err = np.abs(xf - q.astype(np.float64) * sa[:, None].astype(np.float64))
+    assert np.all(err <= sa[:, None] * (0.5 + 1e-5) + 1e-30)
+    qn, san = quant(_bf16(-x))
+    np.testing.assert_array_equal(qn, -q)
+    np.testing.assert_array_equal(san, sa)
+    for e in (-3, 5):
+        q2, sa2 = quant(_bf16(x * np.float32(2.0 ** e)))
+        np.testing.assert_array_equal(q2, q)
+        np.testing.assert_array_equal(sa2, sa * np.float32(2.0 ** e))
+
+
+def test_quant_a4_pins():
+    quant_a4_pins(oracle.quant_act_a4)
+
+
+def _sext4(v):
+    v = v.astype(np.int64) & 15
+    return np.where(v >= 8, v - 16, v)
+
+
+def _dot8(a, b):
+    """Signed 4-bit dot product of 8 nibble pairs, element-wise over uint32 arrays."""
+    s = np.zeros(a.shape, np.int64)
+    for p in range(8):
+        s += _sext4(a >> (4 * p)) * _sext4(b >> (4 * p))
+    return s
+
+
+def act4_product(packed_w, act, N, K):
+    """Sum_k w*x through the documented decode: masks 0x33333333 and
+    (word >> 2) & 0x33333333 of each T32x128 weight word, paired nibble by
+    nibble with the two words of the matching A4I activation chunk, minus
+    sum_k x (codes are w + 1).  Pure numpy, from the two layout definitions."""
+    KT = -(-K // 128)
+    W32 = np.ascontiguousarray(packed_w).view("<u4").astype(np.int64)
+    A32 = np.ascontiguousarray(act).view("<u4").astype(np.int64)
+    nchunk = A32.size // 2
+    xa = np.zeros(KT * 8, np.int64)
+    xb = np.zeros(KT * 8, np.int64)
+    xa[:nchunk], xb[:nchunk] = A32[0::2], A32[1::2]
+    sumx = int((_dot8(xa, np.full_like(xa, 0x11111111)) +
+                _dot8(xb, np.full_like(xb, 0x11111111))).sum())
+    t = np.repeat(np.arange(KT), 8)
+    kg = np.tile(np.arange(8), KT)
+    y = np.zeros(N, np.int64)
+    for n in range(N):
+        s, r = divmod(n, 32)
+        rg, q = divmod(r, 4)
+        w = W32[(s * KT + t) * 256 + (8 * rg + kg) * 4 + q]
+        y[n] = int((_dot8(w & 0x33333333, xa) + _dot8((w >> 2) & 0x33333333, xb)).sum()) - sumx
+    return y
+
+
+def act4_pins(pack, unpack, nbytes):
+    ex = _load("worked_examples.json")["act4_layout"]
+    b = pack(np.array([ex["q"]], np.int8))
+    np.testing.assert_array_equal(b, np.array(ex["bytes"], np.uint8))
+    # size: rows padded to 32 values, half a byte per value
+    for M, K in [(1, 1), (1, 32), (2, 33), (3, 2560), (1, 27648)]:
+        assert nbytes(M, K) == M * (-(-K // 32) * 16)
+    # every value position is its own nibble, padding stays zero
+    K = 48
+    base = pack(np.zeros((1, K), np.int8))
+    assert base.size == 32 and not base.any()
+    seen = set()
+    for k in range(K):
+        e = np.zeros((1, K), np.int8)
+        e[0, k] = 1
+        d = np.nonzero(pack(e))[0]
+        assert d.size == 1
+        v = int(pack(e)[d[0]])
+        assert v in (0x01, 0x10)
+        seen.add((int(d[0]), v))
+    assert len(seen) == K and max(i for i, _ in seen) < K // 2
+    # round trip over the whole int4 range, ragged K, several rows
+    rng = np.random.default_rng(17)
+    for M, K in [(1, 1), (1, 15), (2, 33), (3, 300), (1, 2560)]:
+        q = rng.integers(-8, 8, size=(M, K), dtype=np.int8)
+        b = pack(q)
+        assert b.size == nbytes(M, K)
+        np.testing.assert_array_equal(unpack(b, M, K), q)
+    # the layout pairs each activation with its weight code under the decode
+    for N, K in [(5, 16), (40, 300), (33, 129), (7, 1000)]:
+        w = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+        q = rng.integers(-8, 8, size=(1, K), dtype=np.int8)
+        ref = q.astype(np.int64) @ w.astype(np.int64).T
+        np.testing.assert_array_equal(act4_product(oracle.pack(w), pack(q), N, K), ref[0])
+
+
+def test_act4_pins():
+    act4_pins(oracle.pack_act4, oracle.unpack_act4, oracle.act4_bytes)
+
+
+def test_pack_act4_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        oracle.pack_act4(np.array([[8]], np.int8))
+    with pytest.raises(ValueError):
+        oracle.pack_act4(np.array([[-9]], np.int8))
+
+
 def test_synth_distributions():
     x, w = synth.gemv_case(256, 4096, seed=3)
     assert x.dtype == np.int8 and x.min() >= -127 and x.max() <= 127

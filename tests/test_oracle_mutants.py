@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from test_oracle import (epilogue_pins, gemm_pins, pack_pins, quant_pins,
-                         ternarize_pins)
+from test_oracle import (act4_pins, epilogue_pins, gemm_pins, pack_pins, quant_a4_pins,
+                         quant_pins, ternarize_pins)
 import synth
 
 
@@ -226,3 +226,96 @@ def test_pack_mutant_padding_fails():
 
 def test_pack_mutant_collision_fails():
     assert _fails(pack_pins, _p_collide, oracle.unpack, oracle.packed_bytes)
+
+
+# --------------------------- O5 mutants ------------------------------------
+def _q4_generic(xb, qmax=7, lo=-7, hi=7, round_fn=np.rint, amax_fn=lambda r: np.abs(r).max(),
+                per_row=True):
+    xf = synth.bf16_bits_to_fp32(np.atleast_2d(xb)).astype(np.float32)
+    M, K = xf.shape
+    q = np.zeros((M, K), np.int8)
+    sa = np.zeros(M, np.float32)
+    a_all = np.float32(np.abs(xf).max()) if xf.size else np.float32(0)
+    for m in range(M):
+        a = np.float32(amax_fn(xf[m])) if per_row else a_all
+        if a == 0:
+            continue
+        inv = np.float32(qmax) / a
+        q[m] = np.clip(round_fn(xf[m] * inv), lo, hi).astype(np.int8)
+        sa[m] = a / np.float32(qmax)
+    return q, sa
+
+
+@pytest.mark.parametrize("mut", [
+    lambda xb: _q4_generic(xb, round_fn=np.trunc),
+    lambda xb: _q4_generic(xb, qmax=8, lo=-8),
+    lambda xb: _q4_generic(xb, qmax=8, lo=-8, hi=7),
+    lambda xb: _q4_generic(xb, amax_fn=lambda r: r.max()),
+    lambda xb: _q4_generic(xb, per_row=False),
+    lambda xb: _q4_generic(xb, round_fn=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)),
+    lambda xb: oracle.quant_act(xb),
+], ids=["trunc", "scale8", "scale8_clamp7", "no_abs", "per_tensor", "half_away", "int8"])
+def test_quant_a4_mutants_fail(mut):
+    assert _fails(quant_a4_pins, mut)
+
+
+# --------------------------- A4I layout mutants ----------------------------
+def _a4_generic(q, byte_fn, kq_fn=lambda K: -(-K // 32) * 32, signed=True):
+    q2 = np.atleast_2d(np.asarray(q, np.int8))
+    M, K = q2.shape
+    row = kq_fn(K) // 2
+    out = np.zeros(M * row, np.uint8)
+    for m in range(M):
+        for k in range(K):
+            v = int(q2[m, k])
+            if v < -8 or v > 7:
+                raise ValueError("out of range")
+            b, s = byte_fn(k)
+            out[m * row + b] |= ((v & 15) if signed else abs(v) & 15) << s
+    return out
+
+
+def _a4_unpack_generic(b, M, K, byte_fn, kq_fn=lambda K: -(-K // 32) * 32, sext=True):
+    row = kq_fn(K) // 2
+    q = np.zeros((M, K), np.int8)
+    for m in range(M):
+        for k in range(K):
+            bb, s = byte_fn(k)
+            v = (int(b[m * row + bb]) >> s) & 15
+            q[m, k] = v - 16 if (sext and v >= 8) else v
+    return q
+
+
+def _ok_byte(k):
+    c, i = divmod(k, 16)
+    h, j = divmod(i, 4)
+    return c * 8 + 4 * (h % 2) + j, 4 * (h // 2)
+
+
+def _swap_halves(k):
+    c, i = divmod(k, 16)
+    h, j = divmod(i, 4)
+    return c * 8 + 4 * (h // 2) + j, 4 * (h % 2)
+
+
+def _plain_order(k):
+    return k // 2, 4 * (k % 2)
+
+
+def _no_pad_bytes(M, K):
+    return M * (-(-K // 16) * 8)
+
+
+@pytest.mark.parametrize("impl", [
+    (lambda q: _a4_generic(q, _swap_halves),
+     lambda b, M, K: _a4_unpack_generic(b, M, K, _swap_halves), oracle.act4_bytes),
+    (lambda q: _a4_generic(q, _plain_order),
+     lambda b, M, K: _a4_unpack_generic(b, M, K, _plain_order), oracle.act4_bytes),
+    (lambda q: _a4_generic(q, _ok_byte, kq_fn=lambda K: -(-K // 16) * 16),
+     lambda b, M, K: _a4_unpack_generic(b, M, K, _ok_byte, kq_fn=lambda K: -(-K // 16) * 16),
+     _no_pad_bytes),
+    (lambda q: _a4_generic(q, _ok_byte),
+     lambda b, M, K: _a4_unpack_generic(b, M, K, _ok_byte, sext=False), oracle.act4_bytes),
+], ids=["nibble_halves_swapped", "plain_order", "no_pad_to_32", "no_sign_extension"])
+def test_act4_mutants_fail(impl):
+    assert _fails(act4_pins, *impl)

@@ -506,6 +506,80 @@ def grouped_extras(torch, w2a8, synth, lib, stream):
     return out
 
 
+def a4_extras(torch, w2a8, synth, lib, stream):
+    """W2A4 variant (int4 activations): per sweep shape and large shape, cold,
+    the W2A4 GEMV and the W2A8 GEMV over the same rotation of weight copies
+    (one launch per copy per graph), and the whole int4 layer at 13824 x 2560
+    (quant_act_int4 + w2a4_gemv with the fp32 epilogue)."""
+    import numpy as np
+    vp, F = ctypes.c_void_p, ctypes.c_float
+    sp = vp(stream.cuda_stream)
+    out = {"shapes": []}
+    specs = [(n, k, False) for n, k in synth.SWEEP_SHAPES] + \
+            [(n, k, True) for n, k in synth.LARGE_SHAPES]
+    for n, k, sparse in specs:
+        q, w = synth.gemv_a4_case(n, k, seed=60 + n % 97, sparse=sparse)
+        x8 = torch.from_numpy(np.clip(q, -7, 7).astype(np.int8)).to(stream.device)
+        x4 = w2a8.pack_act_int4(torch.from_numpy(q)).to(stream.device)
+        wp = w2a8.pack_ternary(torch.from_numpy(w)).to(stream.device)
+        del w
+        copies = rotation(torch, wp, wp.numel())
+        ptrs = [vp(c.data_ptr()) for c in copies]
+        y = torch.empty(n, dtype=torch.int32, device=stream.device)
+        ws = torch.zeros(max(256, w2a8.workspace_bytes(1, n, k)), dtype=torch.uint8,
+                         device=stream.device)
+
+        def a4(j):
+            rc = lib.w2a4_gemv(ptrs[j % len(ptrs)], vp(x4.data_ptr()), n, k, vp(y.data_ptr()),
+                               None, F(1.0), None, vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a4_gemv failed with status {rc}")
+
+        def a8(j):
+            rc = lib.w2a8_gemv(ptrs[j % len(ptrs)], vp(x8.data_ptr()), n, k, vp(y.data_ptr()),
+                               None, F(1.0), None, vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a8_gemv failed with status {rc}")
+        t4 = graph_times(torch, a4, max(24, len(ptrs)), stream)
+        t8 = graph_times(torch, a8, max(24, len(ptrs)), stream)
+        m4, m8 = sorted(t4)[len(t4) // 2], sorted(t8)[len(t8) // 2]
+        b4 = n * k // 4 + x4.numel() + 4 * n
+        out["shapes"].append({"n": n, "k": k, "w2a4_median_us": round(m4, 3),
+                              "w2a4_GBps": round(b4 / m4 / 1e3, 1),
+                              "w2a8_median_us": round(m8, 3), "rotation_copies": len(ptrs)})
+        del copies, ptrs, wp, x4, x8, y, ws
+        torch.cuda.empty_cache()
+    # the whole int4 linear layer for one token at 13824 x 2560
+    n, k = 13824, 2560
+    xb, W = synth.linear_case(1, n, k, synth.LINEAR_SEEDS[1])
+    wq, sw = w2a8.ternarize_absmean(torch.from_numpy(W))
+    del W
+    wp = w2a8.pack_ternary(wq).to(stream.device)
+    copies = rotation(torch, wp, wp.numel())
+    ptrs = [vp(c.data_ptr()) for c in copies]
+    xd = torch.from_numpy(xb.view(np.int16)).to(stream.device)
+    x4 = torch.empty(w2a8.act4_bytes(1, k), dtype=torch.uint8, device=stream.device)
+    sa = torch.empty(1, dtype=torch.float32, device=stream.device)
+    yf = torch.empty(n, dtype=torch.float32, device=stream.device)
+    ws = torch.zeros(max(256, w2a8.workspace_bytes(1, n, k)), dtype=torch.uint8,
+                     device=stream.device)
+
+    def layer(j):
+        rc = lib.quant_act_int4(vp(xd.data_ptr()), 1, k, vp(x4.data_ptr()), vp(sa.data_ptr()), sp)
+        if rc == 0:
+            rc = lib.w2a4_gemv(ptrs[j % len(ptrs)], vp(x4.data_ptr()), n, k, None,
+                               vp(sa.data_ptr()), F(float(sw)), vp(yf.data_ptr()),
+                               vp(ws.data_ptr()), ws.numel(), sp)
+        if rc != 0:
+            raise RuntimeError(f"int4 layer failed with status {rc}")
+    tl = graph_times(torch, layer, max(12, len(ptrs)), stream)
+    out["linear_13824x2560_layer_us"] = round(sorted(tl)[len(tl) // 2], 3)
+    out["linear"] = "quant_act_int4 + w2a4_gemv with fp32 epilogue, two launches"
+    del copies, ptrs, wp, xd, x4, sa, yf, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def host_call_us(torch, launcher, reps=50):
     """Mean latency of one synchronised call (the page's timeit(50) style)."""
     launcher(0)
@@ -756,6 +830,7 @@ def main():
         out["detail"]["gemm_peak_int8_TOPS"] = PEAK_INT8_TOPS
         out["detail"]["linear_13824x2560"] = linear_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["grouped_decode"] = grouped_extras(torch, w2a8, synth, lib, stream)
+        out["detail"]["w2a4"] = a4_extras(torch, w2a8, synth, lib, stream)
 
     if args.calibrate_copy:
         a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)

@@ -225,6 +225,51 @@ int w2a8_linear_gemv_grouped(int G, const void *const *w_packed, const int64_t *
                              int32_t *const *y_i32, void *workspace, int64_t ws_bytes,
                              void *stream);
 
+/* ------------------------------------------------------------------------
+ * W2A4 variant: int4 activations.
+ * "微软BitNet：1-bit量化大模型CPU部署实践" (its GPU runtime section) names an
+ * "a4.8" extension with lower-precision activations, without a formula.
+ * Reading: the per-token absmax quantizer above with 7 levels per side, and
+ * the same exact integer product and fp32 epilogue.
+ *
+ * Activation layout "A4I": a row of K values padded with zeros to
+ * Kq = ceil(K/32)*32 values, two's complement nibbles, Kq/2 bytes per row,
+ * rows back to back.  Value k: chunk c = k/16, i = k%16, h = i/4, j = i%4;
+ * byte c*8 + 4*(h%2) + j, low nibble for h < 2, high nibble otherwise.  (Byte
+ * j of a chunk's first word holds values j and 8+j, of its second word
+ * values 4+j and 12+j: the positions of their weight codes in a T32x128 word
+ * under the masks 0x33333333 and (w >> 2) & 0x33333333.)
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of M rows of K int4 activations in the A4I layout, or -1 for M or K
+ * out of range. */
+int64_t w2a4_act_bytes(int64_t M, int64_t K);
+
+/* Host: pack int4 values q (int8 [M][K], each in -8..7) into the A4I layout
+ * (out: host, out_bytes >= w2a4_act_bytes(M, K)).  W2A8_ERR_VALUE for a value
+ * outside -8..7 (out then partly written). */
+int pack_act_int4(const int8_t *q, int64_t M, int64_t K, uint8_t *out, int64_t out_bytes);
+
+/* Per-token absmax int4 quantization of bf16 activations (device).  Per row m:
+ *   a = max_k |x[m][k]|;  inv = 7 / a  (fp32 division);
+ *   q[m][k] = clamp(round_half_even(x[m][k] * inv), -7, 7);
+ *   s_a[m] = a / 7  (fp32 division).   A zero row gives 0 and s_a = 0.
+ * x_bf16: device, [M][K] bf16 bit patterns, 16-byte aligned.  x_q4: device,
+ * w2a4_act_bytes(M, K) bytes, 16-byte aligned, written in the A4I layout
+ * (padding nibbles zero).  s_a: device, fp32 [M]. */
+int quant_act_int4(const uint16_t *x_bf16, int64_t M, int64_t K, uint8_t *x_q4,
+                   float *s_a, void *stream);
+
+/* W2A4 GEMV, M = 1: w2a8_gemv with int4 activations.
+ *   y_i32[n] = sum_k w[n][k] * q[k]
+ *   y_f32[n] = ((float)y_i32[n] * s_a[0]) * s_w
+ * x_q4: device, one A4I row (w2a4_act_bytes(1, K) bytes), 16-byte aligned.
+ * Every other argument as w2a8_gemv (same packed weights, same workspace
+ * size w2a8_workspace_bytes(1, N, K)). */
+int w2a4_gemv(const void *w_packed, const uint8_t *x_q4, int64_t N, int64_t K,
+              int32_t *y_i32, const float *s_a, float s_w, float *y_f32,
+              void *workspace, int64_t ws_bytes, void *stream);
+
 /* W2A8 batched product, M >= 1 (prefill).
  * [TEST] "限制与注意事项": the reference handles only M == 1; this entry
  * computes the same product for M token rows:

@@ -96,6 +96,15 @@ def gemv_case(n: int, k: int, seed: int, sparse: bool = False):
     return x, w
 
 
+def gemv_a4_case(n: int, k: int, seed: int, sparse: bool = False):
+    """M=1 case with int4 activations: returns (q int8 [k] uniform in -8..7,
+    W int8 [n, k] as in gemv_case)."""
+    rng = _rng(seed)
+    q = rng.integers(-8, 8, size=(k,), dtype=np.int8)
+    w = ternary_sparse(rng, n, k) if sparse else ternary_uniform(rng, n, k)
+    return q, w
+
+
 def gemm_case(m: int, n: int, k: int, seed: int):
     """Batched case: returns (X int8 [m, k], W int8 [n, k]) with uniform ternary W."""
     rng = _rng(seed)

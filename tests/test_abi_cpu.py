@@ -53,7 +53,8 @@ def test_library_exports_every_declared_symbol():
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
                 "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemv_stream", "w2a8_tune_gemm",
-                "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped"}
+                "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped",
+                "w2a4_act_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv"}
     assert expected.issubset(set(names)), set(names) ^ expected
     L = ctypes.CDLL(w2a8.LIB_PATH)
     for n in names:
@@ -283,6 +284,61 @@ def test_grouped_validation(linear):
         assert g(y=[FAKE, None, FAKE], yf=[FAKE, None, FAKE]) == ST["NULL"]   # no output
         assert g(sa=None) == ST["NULL"]                          # y_f32 needs s_a
         assert g(sa=FAKE + 2) == ST["ALIGN"]
+
+
+def test_act4_bytes_and_host_packer_match_oracle():
+    for M, K in [(1, 1), (1, 31), (1, 32), (2, 33), (3, 2560), (1, 27648)]:
+        assert w2a8.act4_bytes(M, K) == oracle.act4_bytes(M, K)
+    L = w2a8.lib()
+    assert L.w2a4_act_bytes(0, 16) == -1 and L.w2a4_act_bytes(1, 0) == -1
+    rng = np.random.default_rng(4)
+    for M, K in [(1, 1), (1, 15), (2, 33), (3, 300), (1, 2560), (2, 1000)]:
+        q = rng.integers(-8, 8, size=(M, K), dtype=np.int8)
+        np.testing.assert_array_equal(w2a8.pack_act_int4(torch.from_numpy(q)).numpy(),
+                                      oracle.pack_act4(q))
+
+
+def test_pack_act_int4_validation():
+    L = w2a8.lib()
+    q = np.zeros((1, 40), np.int8)
+    out = np.zeros(64, np.uint8)
+    qp, op = q.ctypes.data, out.ctypes.data
+    assert L.pack_act_int4(None, 1, 40, op, 64) == ST["NULL"]
+    assert L.pack_act_int4(qp, 1, 40, None, 64) == ST["NULL"]
+    assert L.pack_act_int4(qp, 0, 40, op, 64) == ST["SHAPE"]
+    assert L.pack_act_int4(qp, 1, 40, op, 31) == ST["BUFSIZE"]
+    for bad in (8, -9, 127):
+        q[0, 17] = bad
+        assert L.pack_act_int4(qp, 1, 40, op, 64) == ST["VALUE"]
+    q[0, 17] = -8
+    assert L.pack_act_int4(qp, 1, 40, op, 64) == ST["OK"]
+
+
+def test_w2a4_validation():
+    L = w2a8.lib()
+    assert L.quant_act_int4(None, 1, 16, FAKE, FAKE, None) == ST["NULL"]
+    assert L.quant_act_int4(FAKE, 1, 16, None, FAKE, None) == ST["NULL"]
+    assert L.quant_act_int4(FAKE, 0, 16, FAKE, FAKE, None) == ST["SHAPE"]
+    assert L.quant_act_int4(FAKE, 1, 0, FAKE, FAKE, None) == ST["SHAPE"]
+    assert L.quant_act_int4(FAKE + 2, 1, 16, FAKE, FAKE, None) == ST["ALIGN"]
+    assert L.quant_act_int4(FAKE, 1, 16, FAKE + 8, FAKE, None) == ST["ALIGN"]
+
+    def g(**kw):
+        a = dict(wp=FAKE, x=FAKE, N=64, K=256, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
+                 wsb=1 << 20)
+        a.update(kw)
+        return L.w2a4_gemv(a["wp"], a["x"], a["N"], a["K"], a["y"], a["sa"], F(a["sw"]),
+                           a["yf"], a["ws"], a["wsb"], None)
+    assert g(wp=None) == ST["NULL"]
+    assert g(x=None) == ST["NULL"]
+    assert g(ws=None) == ST["NULL"]
+    assert g(y=None, yf=None) == ST["NULL"]
+    assert g(sa=None) == ST["NULL"]
+    assert g(N=0) == ST["SHAPE"]
+    assert g(K=1048448 + 1) == ST["SHAPE"]
+    assert g(x=FAKE + 8) == ST["ALIGN"]
+    assert g(yf=FAKE_ODD) == ST["ALIGN"]
+    assert g(wsb=w2a8.workspace_bytes(1, 64, 256) - 1) == ST["BUFSIZE"]
 
 
 def test_quant_validation():

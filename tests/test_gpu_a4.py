@@ -1,0 +1,143 @@
+"""GPU parity of the W2A4 variant (int4 activations, A4I layout).
+
+Quantizer: the packed bytes and per-token scales are bit-identical to the
+oracle's int4 quantizer followed by its A4I packer (both take every decision
+with the same correctly rounded fp32 operations).
+GEMV: the int32 output is bit-exact against the oracle's integer product of
+the int4 values with the ternary weights; the fp32 epilogue is bit-identical
+to the oracle's.  Activations span the whole int4 range -8..7; shapes cover
+ragged N and K (K % 32 != 0 exercises the row padding), several tiles,
+strips split over workgroups, the sweep shapes and the two large shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w2a8_gemv_amd as w2a8
+
+from gpu_util import check_guard, dev, guarded, packed_on_device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return to_dev(bits.astype(np.uint16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (1, 7), (1, 15), (1, 16), (1, 31), (2, 33), (3, 100),
+                                 (1, 2560), (4, 4000), (1, 27648), (17, 64)])
+def test_quant_int4_matches_oracle(M, K):
+    xb, _ = synth.linear_case(M, 1, K, seed=3 * M + K)
+    xq4, sa = w2a8.quant_act_int4(_bf16_dev(xb))
+    torch.cuda.synchronize()
+    q, osa = oracle.quant_act_a4(xb)
+    np.testing.assert_array_equal(xq4.cpu().numpy(), oracle.pack_act4(q))
+    np.testing.assert_array_equal(sa.cpu().numpy(), osa)
+
+
+def test_quant_int4_worked_examples_and_zero_rows():
+    rows = [[1.0, -0.5, 0.25, 0.0], [2.0, 1.0, -1.0, 0.5], [1.75, 0.625, -0.375, 0.125],
+            [0.0, 0.0, 0.0, 0.0], [-3.0, -3.0, -3.0, -3.0]]
+    bits = synth.fp32_to_bf16_bits(np.array(rows, np.float32))
+    xq4, sa = w2a8.quant_act_int4(_bf16_dev(bits))
+    torch.cuda.synchronize()
+    q = oracle.unpack_act4(xq4.cpu().numpy(), 5, 4)
+    assert q[0].tolist() == [7, -4, 2, 0]
+    assert q[1].tolist() == [7, 4, -4, 2]
+    assert q[2].tolist() == [7, 2, -2, 0]
+    assert q[3].tolist() == [0, 0, 0, 0] and sa.cpu().numpy()[3] == 0.0
+    oq, osa = oracle.quant_act_a4(bits)
+    np.testing.assert_array_equal(q, oq)
+    np.testing.assert_array_equal(sa.cpu().numpy(), osa)
+
+
+def _gemv_a4(q, w, N, K, sa=None, sw=1.0, want_f32=False, workspace=None):
+    xq4 = to_dev(oracle.pack_act4(q.reshape(1, -1)))
+    y = guarded(N, torch.int32)
+    yf = guarded(N, torch.float32) if want_f32 else None
+    w2a8.w2a4_gemv(packed_on_device(w), xq4, N, K, y_i32=y[:N], s_a=sa, s_w=sw,
+                   y_f32=None if yf is None else yf[:N], workspace=workspace)
+    torch.cuda.synchronize()
+    check_guard(y, N)
+    if yf is None:
+        return y[:N].cpu().numpy()
+    check_guard(yf, N)
+    return y[:N].cpu().numpy(), yf[:N].cpu().numpy()
+
+
+SHAPES = [(1, 1), (1, 16), (33, 7), (64, 31), (97, 100), (32, 128), (100, 129), (300, 1000),
+          (2560, 2560), (3840, 2560), (13824, 2560), (2560, 6912), (3200, 3200), (4800, 3200),
+          (3200, 10240), (20480, 3200), (96, 27648), (130, 4000)]
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_w2a4_gemv_matches_oracle(N, K):
+    q, w = synth.gemv_a4_case(N, K, seed=N + 7 * K, sparse=N % 2 == 1)
+    y = _gemv_a4(q, w, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(q.reshape(1, -1), w)[0])
+
+
+@pytest.mark.parametrize("N,K", [(5120, 27648), (55296, 5120)])
+def test_w2a4_gemv_large_shapes(N, K):
+    q, w = synth.gemv_a4_case(N, K, seed=N, sparse=True)
+    y = _gemv_a4(q, w, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(q.reshape(1, -1), w)[0])
+
+
+def test_w2a4_gemv_extremes():
+    """-8 everywhere against all -1 and all +1 weights: +-8K, the largest magnitudes."""
+    for N, K in [(40, 3000), (64, 27648)]:
+        q = np.full(K, -8, np.int8)
+        for v in (-1, 1):
+            w = np.full((N, K), v, np.int8)
+            y = _gemv_a4(q, w, N, K)
+            assert np.all(y == -8 * K * v)
+
+
+def test_w2a4_gemv_fp32_epilogue():
+    N, K = 700, 2560
+    q, w = synth.gemv_a4_case(N, K, seed=5)
+    sa = np.array([0.0371], np.float32)
+    sw = np.float32(0.0213)
+    yi, yf = _gemv_a4(q, w, N, K, sa=to_dev(sa), sw=float(sw), want_f32=True)
+    acc = oracle.gemm_i32(q.reshape(1, -1), w)
+    np.testing.assert_array_equal(yi, acc[0])
+    np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw)[0])
+
+
+@pytest.mark.parametrize("policy", [(1, 32, 8, 256, 10 ** 6), (64, 1, 8, 256, 1),
+                                    (2, 2, 8, 7, 1), (16, 32, 4, 1, 1)])
+def test_w2a4_gemv_forced_splits(policy):
+    try:
+        w2a8.tune_gemv(*policy)
+        for N, K in [(200, 3200), (96, 27648), (33, 1000), (64, 100)]:
+            q, w = synth.gemv_a4_case(N, K, seed=K)
+            np.testing.assert_array_equal(_gemv_a4(q, w, N, K),
+                                          oracle.gemm_i32(q.reshape(1, -1), w)[0])
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+def test_w2a4_workspace_left_zeroed():
+    N, K = 500, 27648                       # strips split over workgroups
+    q, w = synth.gemv_a4_case(N, K, seed=8)
+    ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
+    ref = oracle.gemm_i32(q.reshape(1, -1), w)[0]
+    for _ in range(3):
+        np.testing.assert_array_equal(_gemv_a4(q, w, N, K, workspace=ws), ref)
+    assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("N,K", [(13824, 2560), (300, 1000), (64, 33)])
+def test_linear_a4_layer(N, K):
+    """bf16 token -> int4 quantizer -> W2A4 GEMV -> fp32, against the oracle's
+    chain of the same steps (bit-identical)."""
+    xb, W = synth.linear_case(1, N, K, seed=N + K)
+    wq, sw = oracle.ternarize_absmean(W)
+    y = w2a8.linear_a4(_bf16_dev(xb.reshape(-1)), packed_on_device(wq), float(sw), N, K)
+    torch.cuda.synchronize()
+    q, sa = oracle.quant_act_a4(xb)
+    ref = oracle.epilogue(oracle.gemm_i32(q, wq), sa, sw)
+    np.testing.assert_array_equal(y.cpu().numpy(), ref)

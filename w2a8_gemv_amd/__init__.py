@@ -75,6 +75,14 @@ def lib():
         L.w2a8_gemm.restype = I32
         L.w2a8_linear_gemv.argtypes = [P, P, I64, I64, F32, P, P, P, I64, P]
         L.w2a8_linear_gemv.restype = I32
+        L.w2a4_act_bytes.argtypes = [I64, I64]
+        L.w2a4_act_bytes.restype = I64
+        L.pack_act_int4.argtypes = [P, I64, I64, P, I64]
+        L.pack_act_int4.restype = I32
+        L.quant_act_int4.argtypes = [P, I64, I64, P, P, P]
+        L.quant_act_int4.restype = I32
+        L.w2a4_gemv.argtypes = [P, P, I64, I64, P, P, F32, P, P, I64, P]
+        L.w2a4_gemv.restype = I32
         L.w2a8_gemv_grouped.argtypes = [I32, P, P, I64, P, P, P, P, P, P, I64, P]
         L.w2a8_gemv_grouped.restype = I32
         L.w2a8_linear_gemv_grouped.argtypes = [I32, P, P, I64, P, P, P, P, P, I64, P]
@@ -298,6 +306,76 @@ def w2a8_linear_gemv(w_packed, x_bf16, N, K, s_w, y_f32, y_i32=None, workspace=N
     _check(lib().w2a8_linear_gemv(_ptr(w_packed), _ptr(x_bf16), N, K, ctypes.c_float(s_w),
                                   _ptr(y_f32), _ptr(y_i32), _ptr(ws), ws.numel(),
                                   _stream_handle(stream)), "w2a8_linear_gemv")
+
+
+# ---------------------------------------------------------------------------
+# W2A4 variant: int4 activations in the A4I layout (see include/w2a8.h)
+# ---------------------------------------------------------------------------
+def act4_bytes(M: int, K: int) -> int:
+    v = int(lib().w2a4_act_bytes(M, K))
+    if v < 0:
+        raise ValueError("M or K out of range")
+    return v
+
+
+def pack_act_int4(q: torch.Tensor) -> torch.Tensor:
+    """Host int8 [M, K] (values -8..7) -> host uint8 [act4_bytes(M, K)] (A4I layout)."""
+    q2 = q.view(1, -1) if q.dim() == 1 else q
+    _need(q2, "q", torch.int8, "cpu")
+    M, K = q2.shape
+    out = torch.empty(act4_bytes(M, K), dtype=torch.uint8)
+    _check(lib().pack_act_int4(_ptr(q2), M, K, _ptr(out), out.numel()), "pack_act_int4")
+    return out
+
+
+def quant_act_int4(x_bf16: torch.Tensor, x_q4=None, s_a=None, stream=None):
+    """x bf16 [M, K] (device) -> (A4I bytes uint8 [act4_bytes(M, K)], s_a fp32 [M])."""
+    _need(x_bf16, "x_bf16", torch.bfloat16, "cuda")
+    x2 = x_bf16.view(1, -1) if x_bf16.dim() == 1 else x_bf16
+    M, K = x2.shape
+    if x_q4 is None:
+        x_q4 = torch.empty(act4_bytes(M, K), dtype=torch.uint8, device=x2.device)
+    if s_a is None:
+        s_a = torch.empty(M, dtype=torch.float32, device=x2.device)
+    _need(x_q4, "x_q4", torch.uint8, "cuda")
+    _need(s_a, "s_a", torch.float32, "cuda")
+    if x_q4.numel() < act4_bytes(M, K) or s_a.numel() != M:
+        raise ValueError("x_q4 / s_a have the wrong size")
+    _check(lib().quant_act_int4(_ptr(x2), M, K, _ptr(x_q4), _ptr(s_a), _stream_handle(stream)),
+           "quant_act_int4")
+    return x_q4, s_a
+
+
+def w2a4_gemv(w_packed, x_q4, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
+              workspace=None, stream=None):
+    """Raw C-ABI call: W2A4 GEMV over one A4I activation row; returns nothing."""
+    _need(w_packed, "w_packed", torch.uint8, "cuda")
+    _need(x_q4, "x_q4", torch.uint8, "cuda")
+    if x_q4.numel() < act4_bytes(1, K):
+        raise ValueError("x_q4 must hold act4_bytes(1, K) bytes")
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than packed_bytes(N, K)")
+    for t, nm, dt in ((y_i32, "y_i32", torch.int32), (y_f32, "y_f32", torch.float32)):
+        if t is not None:
+            _need(t, nm, dt, "cuda")
+            if t.numel() != N:
+                raise ValueError(f"{nm} must have N elements")
+    if s_a is not None:
+        _need(s_a, "s_a", torch.float32, "cuda")
+    ws = _ws(workspace_bytes(1, N, K), x_q4.device, stream, workspace)
+    _check(lib().w2a4_gemv(_ptr(w_packed), _ptr(x_q4), N, K, _ptr(y_i32), _ptr(s_a),
+                           ctypes.c_float(s_w), _ptr(y_f32), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream_handle(stream)),
+           "w2a4_gemv")
+
+
+def linear_a4(x_bf16, w_packed, s_w, N, K, stream=None):
+    """W2A4 linear layer for one token: quant_act_int4, then w2a4_gemv with the
+    fp32 epilogue (two launches, no host synchronisation) -> fp32 [1, N]."""
+    xq4, sa = quant_act_int4(x_bf16.reshape(1, -1), stream=stream)
+    y = torch.empty((1, N), dtype=torch.float32, device=x_bf16.device)
+    w2a4_gemv(w_packed, xq4, N, K, s_a=sa, s_w=s_w, y_f32=y.view(-1), stream=stream)
+    return y
 
 
 MAX_GROUPS = 8

@@ -52,11 +52,13 @@ def test_gemm_small_ragged(M, N, K):
 
 
 # Each kernel forced onto ragged shapes: every pipelined configuration
-# (M <= 32, <= 64, <= 128, larger), K below one ring of tiles (K = 16, 144),
+# (M <= 32, above, and M >= 256 over >= 256 strips, whose 128 x 256 tile is
+# ragged in M, N and K at 333 x 8230 x 1040), K below one ring of tiles (K = 16, 144),
 # a k-tile remainder (KT % 4 = 1, 2, 3), a partial last tile (K = 1040) and
 # ragged N (strips past the matrix, rows past N in the last strip).
 FORCED = [(8, 1000, 1040), (33, 100, 16), (64, 2560, 144), (100, 97, 2560), (128, 200, 384),
-          (200, 1000, 1040), (257, 33, 3200), (2, 4096, 896), (17, 130, 640)]
+          (200, 1000, 1040), (257, 33, 3200), (2, 4096, 896), (17, 130, 640),
+          (333, 8230, 1040), (256, 8192, 64)]
 
 
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])

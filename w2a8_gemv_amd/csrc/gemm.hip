@@ -275,10 +275,11 @@ struct Pipe {
     static constexpr int MBW = BM / WM / 16;           // A blocks per wave
     static constexpr int NBW = 2 * SPW;                // B blocks per wave
     static constexpr int NSTRIP = WN * SPW;            // strips per workgroup
-    static_assert(NSTRIP == NW, "one weight strip load per wave per tile");
+    static_assert(NSTRIP % NW == 0, "whole weight strips per wave");
+    static constexpr int LS = NSTRIP / NW;             // weight strip loads per wave per tile
     static constexpr int DPW = BM * 8 / 64 / NW;       // activation loads per wave per tile
     static_assert(DPW >= 1 && DPW * 64 * NW == BM * 8, "tile must split evenly over waves");
-    static constexpr int LPT = DPW + 1;                // loads per wave per tile
+    static constexpr int LPT = DPW + LS;               // loads per wave per tile
     static constexpr int WAITN = (S - 2) * LPT;        // issued after a tile's group when used
     static_assert(WAITN <= 63, "wait count must fit vmcnt");
     static constexpr int XBYTES = BM * kTileK;
@@ -286,12 +287,12 @@ struct Pipe {
 };
 
 // Loads of tile tt into ring stage `slot`: this wave's DPW activation
-// instructions and its weight strip (tiles past the last repeat it).
+// instructions and its LS weight strips (tiles past the last repeat it).
 template <int BM, int WM, int WN, int SPW, int S>
 __device__ __forceinline__ void pipe_issue(int8_t *ring, int tt, int slot, int KT, int K, int wv,
                                            const int8_t *const (&xsrc)[Pipe<BM, WM, WN, SPW, S>::DPW],
                                            const int (&kcb)[Pipe<BM, WM, WN, SPW, S>::DPW],
-                                           const int8_t *wsrc) {
+                                           const int8_t *const (&wsrc)[Pipe<BM, WM, WN, SPW, S>::LS]) {
     using P = Pipe<BM, WM, WN, SPW, S>;
     const int tc = tt < KT - 1 ? tt : KT - 1;
     int8_t *stage = ring + slot * P::STAGE;
@@ -303,9 +304,13 @@ __device__ __forceinline__ void pipe_issue(int8_t *ring, int tt, int slot, int K
             xsrc[d] + k,
             (__attribute__((address_space(3))) void *)(stage + (wv * P::DPW + d) * 1024), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(
-        wsrc + int64_t(tc) * kTileBytes,
-        (__attribute__((address_space(3))) void *)(stage + P::XBYTES + wv * kTileBytes), 16, 0, 0);
+#pragma unroll
+    for (int ls = 0; ls < P::LS; ++ls)
+        __builtin_amdgcn_global_load_lds(
+            wsrc[ls] + int64_t(tc) * kTileBytes,
+            (__attribute__((address_space(3))) void *)(stage + P::XBYTES +
+                                                        (wv * P::LS + ls) * kTileBytes),
+            16, 0, 0);
 }
 
 // MFMAs of the tile in ring stage s.
@@ -382,14 +387,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
         xsrc[d] = a.x + int64_t(min(m0 + r, a.M - 1)) * a.K;
         kcb[d] = 16 * c;
     }
-    // Weight load: this wave brings strip wv of the workgroup.  Lane l loads
-    // 16-byte slot 8(l>>3) + ((l & 7) ^ 2((l>>3) & 3)) of the tile into LDS
-    // position l (an XOR within each group of 8 slots, its own inverse), so
-    // that the B operand reads below hit 32 distinct banks.
-    const int sload = min(nb * P::NSTRIP + wv, a.NS - 1);
+    // Weight loads: this wave brings strips wv*LS .. wv*LS+LS-1 of the
+    // workgroup.  Lane l loads 16-byte slot 8(l>>3) + ((l & 7) ^ 2((l>>3) & 3))
+    // of the tile into LDS position l (an XOR within each group of 8 slots,
+    // its own inverse), so that the B operand reads below hit 32 distinct
+    // banks.
     const int wslot = 8 * (lane >> 3) + ((lane & 7) ^ (2 * ((lane >> 3) & 3)));
-    const int8_t *wsrc = reinterpret_cast<const int8_t *>(a.wp) +
-                         int64_t(sload) * KT * kTileBytes + 16 * wslot;
+    const int8_t *wsrc[P::LS];
+#pragma unroll
+    for (int ls = 0; ls < P::LS; ++ls) {
+        const int sload = min(nb * P::NSTRIP + wv * P::LS + ls, a.NS - 1);
+        wsrc[ls] = reinterpret_cast<const int8_t *>(a.wp) + int64_t(sload) * KT * kTileBytes +
+                   16 * wslot;
+    }
 
     v4i acc[MBW][NBW];
 #pragma unroll
@@ -499,17 +509,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
 struct PipeCfg {
     int BM, WM, WN, SPW, S;
 };
-constexpr PipeCfg kPipeCfg[2] = {{32, 1, 4, 1, 4}, {64, 1, 4, 1, 6}};
+constexpr PipeCfg kPipeCfg[3] = {{32, 1, 4, 1, 4}, {64, 1, 4, 1, 6}, {128, 1, 8, 1, 4}};
 
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
     GemmShape g;
     g.pipe = -1;
     if (K >= 16 && K % 16 == 0) {
-        // Pipelined kernel: 32 or 64 rows per workgroup by M.  It has no k-split:
-        // when its grid is tiny (under one workgroup per 8 CUs; measured: 20
+        // Pipelined kernel: 32 or 64 rows per workgroup by M, and a 128 x 256
+        // workgroup tile (8 waves, each decoded weight block used by 8
+        // activation blocks) for M >= 256 over at least 256 strips (measured:
+        // 24.7 against 30 us at M = 512, 13824 x 2560; with fewer strips its
+        // grid is too small: slower at 2560 x 6912).  It has no k-split: when
+        // its grid is tiny (under one workgroup per 8 CUs; measured: 20
         // workgroups for M = 8 at 2560 x 6912) and the output is small enough
         // for split-K, the general kernel with split-K is used.
-        const int pipe = M <= 32 ? 0 : 1;
+        const int64_t NS0 = round_up(N, kTileRows) / kTileRows;
+        const int pipe = M <= 32 ? 0 : (M >= 256 && NS0 >= 256) ? 2 : 1;
         const PipeCfg &c = kPipeCfg[pipe];
         const int64_t NS = round_up(N, kTileRows) / kTileRows;
         const int64_t mblk = ceil_div(M, c.BM), nblk = ceil_div(NS, int64_t(c.WN) * c.SPW);
@@ -568,8 +583,9 @@ hipError_t launch_gemm(const GemmLaunch &l, hipStream_t stream) {
     const void *fn;
     if (l.shape.pipe >= 0) {
         const PipeCfg &c = kPipeCfg[l.shape.pipe];
-        fn = l.shape.pipe == 0 ? reinterpret_cast<const void *>(&gemm_pipe_kernel<32, 1, 4, 1, 4>)
-                               : reinterpret_cast<const void *>(&gemm_pipe_kernel<64, 1, 4, 1, 6>);
+        fn = l.shape.pipe == 0   ? reinterpret_cast<const void *>(&gemm_pipe_kernel<32, 1, 4, 1, 4>)
+             : l.shape.pipe == 1 ? reinterpret_cast<const void *>(&gemm_pipe_kernel<64, 1, 4, 1, 6>)
+                                 : reinterpret_cast<const void *>(&gemm_pipe_kernel<128, 1, 8, 1, 4>);
         return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN)), args, 0, stream);
     }
     switch (l.shape.BM) {

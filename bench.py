@@ -83,6 +83,9 @@ def parse_args():
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only the batched product on the prefill configs (counter runs); "
+                         "prints detail.gemm as one JSON line")
     ap.add_argument("--no-detail", action="store_true",
                     help="skip the per-shape cold timings and read floors (counter runs)")
     ap.add_argument("--eager", action="store_true",
@@ -737,6 +740,10 @@ def main():
     cus = props.multi_processor_count
     lib = w2a8.lib()
     stream = torch.cuda.Stream()
+    if args.gemm_only:
+        print(json.dumps({"gemm": gemm_extras(torch, w2a8, synth, lib, stream, cus),
+                          "gemm_peak_int8_TOPS": PEAK_INT8_TOPS}), flush=True)
+        return
 
     specs = [(n, k, seed, False) for (n, k), seed in zip(synth.SWEEP_SHAPES, synth.SWEEP_SEEDS)]
     shapes, slots = make_shapes(torch, w2a8, synth, specs, args.mode, dev)

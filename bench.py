@@ -583,6 +583,54 @@ def a4_extras(torch, w2a8, synth, lib, stream):
     return out
 
 
+def bf16_context(torch, synth, stream, per):
+    """The pages' comparison on this device, context only: torch.matmul of a
+    bf16 activation row [1, K] with bf16 weights [K, N] (cold rotation of
+    weight copies), next to the W2A8 GEMV of the same shape
+    (detail.per_shape_kernel_times).  The bf16 calls are captured in a graph
+    (one call per copy) and the last replay is checked against an eager call;
+    if they differ, the eager calls are timed instead."""
+    out = []
+    g = torch.Generator(device="cpu").manual_seed(90)
+    for (n, k), p in zip(synth.SWEEP_SHAPES, per):
+        w0 = (torch.randn(k, n, generator=g) * 0.02).to(torch.bfloat16).to(stream.device)
+        x = torch.randn(1, k, generator=g).to(torch.bfloat16).to(stream.device)
+        slots = max(2, int(-(-ROTATE_BYTES // (2 * n * k))) + 1)
+        ws = [w0] + [w0.clone() for _ in range(slots - 1)]
+        y = torch.empty(1, n, dtype=torch.bfloat16, device=stream.device)
+
+        def mm(j):
+            torch.matmul(x, ws[j % slots], out=y)
+        with torch.cuda.stream(stream):
+            ref = torch.matmul(x, ws[(slots - 1) % slots])
+        torch.cuda.synchronize()
+        how = "graph"
+        try:
+            ts = graph_times(torch, mm, max(24, slots), stream)
+            torch.cuda.synchronize()
+            if not torch.equal(y, ref):
+                raise RuntimeError("graph replay differs from eager")
+        except RuntimeError:
+            how = "eager"
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                with torch.cuda.stream(stream):
+                    e0.record(stream)
+                    for j in range(max(24, slots)):
+                        mm(j)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / max(24, slots))
+        med = sorted(ts)[len(ts) // 2]
+        out.append({"n": n, "k": k, "bf16_matmul_us": round(med, 3), "timing": how,
+                    "w2a8_gemv_us": p["median_us"], "bf16_over_w2a8": round(med / p["median_us"], 2)})
+        del ws, w0, x, y, ref
+        torch.cuda.empty_cache()
+    return out
+
+
 def host_call_us(torch, launcher, reps=50):
     """Mean latency of one synchronised call (the page's timeit(50) style)."""
     launcher(0)
@@ -838,6 +886,8 @@ def main():
         out["detail"]["linear_13824x2560"] = linear_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["grouped_decode"] = grouped_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["w2a4"] = a4_extras(torch, w2a8, synth, lib, stream)
+        if per:
+            out["detail"]["bf16_matmul_context"] = bf16_context(torch, synth, stream, per)
 
     if args.calibrate_copy:
         a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)

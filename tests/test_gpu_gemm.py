@@ -52,13 +52,17 @@ def test_gemm_small_ragged(M, N, K):
 
 
 # Each kernel forced onto ragged shapes: every pipelined configuration
-# (M <= 32, above, and M >= 256 over >= 256 strips, whose 128 x 256 tile is
-# ragged in M, N and K at 333 x 8230 x 1040), K below one ring of tiles (K = 16, 144),
-# a k-tile remainder (KT % 4 = 1, 2, 3), a partial last tile (K = 1040) and
-# ragged N (strips past the matrix, rows past N in the last strip).
+# (M <= 32, above, M >= 256 over >= 256 strips, whose 128 x 256 tile is
+# ragged in M, N and K at 333 x 8230 x 1040, and the small-grid ones whose
+# 2 or 4 wave groups split K: k-tile counts 9, 20, 25 for 2 groups and
+# 40, 41, 43 for 4, so that the last group may have fewer tiles), K below one
+# ring of tiles (K = 16, 144), a k-tile remainder (KT % 4 = 1, 2, 3), a
+# partial last tile (K = 1040, 5200) and ragged N (strips past the matrix,
+# rows past N in the last strip).
 FORCED = [(8, 1000, 1040), (33, 100, 16), (64, 2560, 144), (100, 97, 2560), (128, 200, 384),
           (200, 1000, 1040), (257, 33, 3200), (2, 4096, 896), (17, 130, 640),
-          (333, 8230, 1040), (256, 8192, 64)]
+          (333, 8230, 1040), (256, 8192, 64), (40, 300, 5248), (96, 200, 5504),
+          (129, 520, 5200), (48, 640, 5120)]
 
 
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
@@ -70,10 +74,11 @@ def test_gemm_forced_kernel(kernel, M, N, K):
     np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
 
 
+@pytest.mark.parametrize("M,N,K", [(150, 700, 1024), (40, 500, 6912)],
+                         ids=["2-groups", "4-groups"])
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
-def test_gemm_forced_kernel_fp32_epilogue(kernel):
+def test_gemm_forced_kernel_fp32_epilogue(kernel, M, N, K):
     w2a8.tune_gemm(kernel)
-    M, N, K = 150, 700, 1024
     x, w = synth.gemm_case(M, N, K, seed=99)
     rng = np.random.default_rng(5)
     sa = (rng.random(M, dtype=np.float32) * 0.05 + 1e-3).astype(np.float32)
@@ -83,6 +88,17 @@ def test_gemm_forced_kernel_fp32_epilogue(kernel):
     acc = oracle.gemm_i32(x, w)
     np.testing.assert_array_equal(yi, acc)
     np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw))
+
+
+# Automatic choice on small output grids, where the k-range is split over
+# wave groups inside a workgroup (4 groups: 9 x 2560 x 6912, 16 x 100 x 5248;
+# 2 groups: 100 x 13824 x 2176, 32 x 2560 x 1040), with odd tile counts.
+@pytest.mark.parametrize("M,N,K", [(9, 2560, 6912), (16, 100, 5248), (100, 13824, 2176),
+                                   (32, 2560, 1040)])
+def test_gemm_wave_group_split_auto(M, N, K):
+    x, w = synth.gemm_case(M, N, K, seed=M * N + K)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
 
 
 # Few-row kernel (M <= 8) forced: every M, ragged N and K (K % 16 != 0 takes

@@ -286,16 +286,13 @@ struct Pipe {
     static constexpr int STAGE = XBYTES + NSTRIP * kTileBytes;
 };
 
-// Loads of tile tt into ring stage `slot`: this wave's DPW activation
-// instructions and its LS weight strips (tiles past the last repeat it).
+// Loads of k-tile tc into one group's part of a ring stage: this wave's DPW
+// activation instructions and its LS weight strips.
 template <int BM, int WM, int WN, int SPW, int S>
-__device__ __forceinline__ void pipe_issue(int8_t *ring, int tt, int slot, int KT, int K, int wv,
-                                           const int8_t *const (&xsrc)[Pipe<BM, WM, WN, SPW, S>::DPW],
-                                           const int (&kcb)[Pipe<BM, WM, WN, SPW, S>::DPW],
-                                           const int8_t *const (&wsrc)[Pipe<BM, WM, WN, SPW, S>::LS]) {
+__device__ __forceinline__ void pipe_issue(int8_t *stage, int tc, int K, int wv,
+                                           const int8_t *const *xsrc, const int *kcb,
+                                           const int8_t *const *wsrc) {
     using P = Pipe<BM, WM, WN, SPW, S>;
-    const int tc = tt < KT - 1 ? tt : KT - 1;
-    int8_t *stage = ring + slot * P::STAGE;
 #pragma unroll
     for (int d = 0; d < P::DPW; ++d) {
         const int k0 = tc * kTileK + kcb[d];
@@ -359,14 +356,24 @@ __device__ __forceinline__ void pipe_mma(const int8_t *stage,
 //  * Rows past M read row M-1 and k-chunks past K read a chunk inside the
 //    row: their products reach only discarded outputs or meet the weight
 //    padding (code 01, weight 0).  Strips past the matrix read its last strip.
-template <int BM, int WM, int WN, int SPW, int S>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
+//  * KS > 1 (small output grids, where one wave's k-step latency is the
+//    bound): KS groups of WM x WN waves split the k-range inside the
+//    workgroup, group g taking k-tiles g, g + KS, ...; each ring stage holds
+//    one part per group, all groups step together, and at the end groups
+//    1..KS-1 hand their accumulators to group 0 through LDS.
+template <int BM, int WM, int WN, int SPW, int S, int KS>
+__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs a) {
     using P = Pipe<BM, WM, WN, SPW, S>;
     constexpr int MBW = P::MBW, NBW = P::NBW, DPW = P::DPW, WAITN = P::WAITN;
-    __shared__ __attribute__((aligned(1024))) int8_t ring[S * P::STAGE];
+    constexpr int GS = P::STAGE, SS = KS * P::STAGE;   // group part, whole stage
+    static_assert((KS - 1) * P::NW * MBW * NBW * 4 * 64 * 4 <= S * SS,
+                  "group reduction must fit in the ring");
+    __shared__ __attribute__((aligned(1024))) int8_t ring[S * SS];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wvall = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wvall / P::NW;                 // k-group
+    const int wv = wvall - grp * P::NW;            // wave within the group
     const int wm = wv / WN, wn = wv - (wv / WN) * WN;
     const int R = int(gridDim.x);  // multiple of 8
     const int unit = (int(blockIdx.x) & 7) * (R >> 3) + (int(blockIdx.x) >> 3);
@@ -378,8 +385,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
 
     // Activation loads: instruction d of this wave covers chunk positions
     // p = (wv*DPW + d)*64 + lane of a stage.
-    const int8_t *xsrc[DPW];
-    int kcb[DPW];
+    const int8_t *xsrc[P::DPW];
+    int kcb[P::DPW];
 #pragma unroll
     for (int d = 0; d < DPW; ++d) {
         const int p = (wv * DPW + d) * 64 + lane;
@@ -434,9 +441,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
                                        (pos * 4 + (r & 3)) * 4;
             }
 
+    // Group grp's k-tile of step tt (past the last: a repeat of it, loaded
+    // to keep the wait counts exact, never multiplied).
+    const int nsteps = (KT + KS - 1) / KS;
+#define W2A8_PIPE_TILE(tt) min((tt) * KS + grp, KT - 1)
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-        pipe_issue<BM, WM, WN, SPW, S>(ring, s, s, KT, a.K, wv, xsrc, kcb, wsrc);
+        pipe_issue<BM, WM, WN, SPW, S>(ring + s * SS + grp * GS, W2A8_PIPE_TILE(s), a.K, wv, xsrc,
+                                       kcb, wsrc);
 
     // One k-tile: this wave's loads of the tile have landed and its LDS reads
     // of the previous tile are done (lgkmcnt 0); after the barrier that holds
@@ -450,22 +462,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
         __builtin_amdgcn_s_waitcnt((WAITN & 15) | ((WAITN >> 4) << 14) | (0x7 << 4));            \
         __builtin_amdgcn_s_barrier();                                                            \
         __asm__ volatile("" ::: "memory");                                                       \
-        pipe_issue<BM, WM, WN, SPW, S>(ring, (tt) + S - 1, ((s) + S - 1) % S, KT, a.K, wv, xsrc,  \
-                                       kcb, wsrc);                                               \
-        pipe_mma<BM, WM, WN, SPW, S>(ring + (s) * P::STAGE, aoff, boff, acc);                    \
+        pipe_issue<BM, WM, WN, SPW, S>(ring + (((s) + S - 1) % S) * SS + grp * GS,               \
+                                       W2A8_PIPE_TILE((tt) + S - 1), a.K, wv, xsrc, kcb, wsrc);  \
+        if (KS == 1 || (tt) * KS + grp < KT)                                                     \
+            pipe_mma<BM, WM, WN, SPW, S>(ring + (s) * SS + grp * GS, aoff, boff, acc);           \
     } while (0)
 
-    // Whole groups of S tiles, then the remainder.
+    // Whole groups of S steps, then the remainder.
     int t = 0;
-    for (; t + S <= KT; t += S) {
+    for (; t + S <= nsteps; t += S) {
 #pragma unroll
         for (int s = 0; s < S; ++s) W2A8_PIPE_STEP(s, t + s);
     }
-    const int rem = KT - t;
+    const int rem = nsteps - t;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
         if (s < rem) W2A8_PIPE_STEP(s, t + s);
 #undef W2A8_PIPE_STEP
+#undef W2A8_PIPE_TILE
+
+    if constexpr (KS > 1) {
+        // Every load in flight has landed and every LDS read is done once all
+        // waves pass this fence-and-barrier; the ring is then free.
+        __syncthreads();
+        int *red = reinterpret_cast<int *>(ring);
+        if (grp > 0) {
+#pragma unroll
+            for (int i = 0; i < MBW; ++i)
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        red[((((grp - 1) * P::NW + wv) * MBW + i) * NBW * 4 + j * 4 + e) * 64 + lane] =
+                            acc[i][j][e];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int q = 1; q < KS; ++q)
+#pragma unroll
+            for (int i = 0; i < MBW; ++i)
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j][e] +=
+                            red[((((q - 1) * P::NW + wv) * MBW + i) * NBW * 4 + j * 4 + e) * 64 + lane];
+    }
 
     // Output element of acc[i][j][e]: row m0 + wm*BM/WM + 16i + 4*(lane/16) + e,
     // column strip(j/2)*32 + 16*(j%2) + lane%16.  Activation scales of this
@@ -502,34 +545,59 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs a) {
 }  // namespace
 
 // Shape of a GEMM launch: block rows BM by M, k-split S when few output tiles.
-// Pipelined-kernel configurations: (BM, WM, WN, SPW, ring depth).  Chosen by
-// a sweep on MI355X over block rows 32..256, four wave layouts and depths
-// 3..8: 32 rows (depth 4) for M <= 32 and 64 rows (depth 6) above won or tied
-// on every prefill shape; larger blocks leave too few workgroups.
+// Pipelined-kernel configurations: (BM, WM, WN, SPW, ring depth, wave groups
+// splitting K).  Chosen by sweeps on MI355X over block rows 32..256, four
+// wave layouts, depths 3..8 and 1, 2 or 4 wave groups: 32 rows (depth 4) for
+// M <= 32 and 64 rows (depth 3) above won or tied on every prefill shape with
+// a large output grid up to M = 448, a 128 x 256 tile beyond, 32 rows with 2
+// or 4 wave groups (depth 3) on small grids.
 struct PipeCfg {
-    int BM, WM, WN, SPW, S;
+    int BM, WM, WN, SPW, S, KS;
 };
-constexpr PipeCfg kPipeCfg[3] = {{32, 1, 4, 1, 4}, {64, 1, 4, 1, 6}, {128, 1, 8, 1, 4}};
+constexpr PipeCfg kPipeCfg[5] = {{32, 1, 4, 1, 4, 1},  {64, 1, 4, 1, 3, 1}, {128, 1, 8, 1, 4, 1},
+                                 {32, 1, 4, 1, 3, 2},  {32, 1, 4, 1, 3, 4}};
+
+// The kernel instance of configuration P.
+template <int P>
+const void *pipe_kernel_fn() {
+    constexpr PipeCfg c = kPipeCfg[P];
+    return reinterpret_cast<const void *>(&gemm_pipe_kernel<c.BM, c.WM, c.WN, c.SPW, c.S, c.KS>);
+}
 
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
     GemmShape g;
     g.pipe = -1;
     if (K >= 16 && K % 16 == 0) {
-        // Pipelined kernel: 32 or 64 rows per workgroup by M, and a 128 x 256
-        // workgroup tile (8 waves, each decoded weight block used by 8
-        // activation blocks) for M >= 256 over at least 256 strips (measured:
-        // 24.7 against 30 us at M = 512, 13824 x 2560; with fewer strips its
-        // grid is too small: slower at 2560 x 6912).  It has no k-split: when
-        // its grid is tiny (under one workgroup per 8 CUs; measured: 20
-        // workgroups for M = 8 at 2560 x 6912) and the output is small enough
-        // for split-K, the general kernel with split-K is used.
-        const int64_t NS0 = round_up(N, kTileRows) / kTileRows;
-        const int pipe = M <= 32 ? 0 : (M >= 256 && NS0 >= 256) ? 2 : 1;
-        const PipeCfg &c = kPipeCfg[pipe];
+        // Pipelined kernel (measured on MI355X, cold weights):
+        //  * small output grids (at most 7/4 workgroups of 32 rows x 4 strips
+        //    per CU, K of 8 tiles or more): 32-row tiles with the k-range split
+        //    over wave groups inside the workgroup, 4 groups when the grid is
+        //    at most one per CU and K has 40 tiles or more, else 2 (the lone
+        //    wave's k-step latency is the bound there: 2560 x 6912 at M = 128
+        //    went from 22.4 to 12.6 us, 13824 x 2560 at M = 8 from 9.3 to
+        //    7.3 us);
+        //  * otherwise 32 or 64 rows per workgroup by M, and a 128 x 256
+        //    workgroup tile (8 waves, each decoded weight block used by 8
+        //    activation blocks) for M > 448 over at least 256 strips
+        //    (24.7 against 29.9 us at M = 512, 13824 x 2560; at M = 448 the
+        //    64-row tile is still ahead, 23.5 against 24.5 us);
+        //  * a grid of at most one 32-row workgroup per 4 CUs with long K
+        //    (96 k-tiles or more) takes the general kernel split over K
+        //    across workgroups when the workspace allows it (5120 x 27648 at
+        //    M = 8: 24.2 against 34.7 us with 4 wave groups).
         const int64_t NS = round_up(N, kTileRows) / kTileRows;
+        const int64_t KT = round_up(K, kTileK) / kTileK;
+        const int64_t g32 = ceil_div(M, 32) * ceil_div(NS, 4);
+        int pipe;
+        if (KT >= 8 && g32 <= int64_t(cus) * 7 / 4)
+            pipe = (KT >= 40 && g32 <= cus) ? 4 : 3;
+        else
+            pipe = M <= 32 ? 0 : (M > 448 && NS >= 256) ? 2 : 1;
+        const PipeCfg &c = kPipeCfg[pipe];
         const int64_t mblk = ceil_div(M, c.BM), nblk = ceil_div(NS, int64_t(c.WN) * c.SPW);
         const int mode = gemm_kernel_mode();
-        if (mode == 1 || (mode == 0 && !(can_split && mblk * nblk < cus / 8))) {
+        const bool tiny_long = can_split && KT >= 96 && g32 <= cus / 4;
+        if (mode == 1 || (mode == 0 && !tiny_long)) {
             g.pipe = pipe;
             g.BM = c.BM;
             g.MBLK = int(mblk);
@@ -583,10 +651,15 @@ hipError_t launch_gemm(const GemmLaunch &l, hipStream_t stream) {
     const void *fn;
     if (l.shape.pipe >= 0) {
         const PipeCfg &c = kPipeCfg[l.shape.pipe];
-        fn = l.shape.pipe == 0   ? reinterpret_cast<const void *>(&gemm_pipe_kernel<32, 1, 4, 1, 4>)
-             : l.shape.pipe == 1 ? reinterpret_cast<const void *>(&gemm_pipe_kernel<64, 1, 4, 1, 6>)
-                                 : reinterpret_cast<const void *>(&gemm_pipe_kernel<128, 1, 8, 1, 4>);
-        return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN)), args, 0, stream);
+        switch (l.shape.pipe) {
+        case 0: fn = pipe_kernel_fn<0>(); break;
+        case 1: fn = pipe_kernel_fn<1>(); break;
+        case 2: fn = pipe_kernel_fn<2>(); break;
+        case 3: fn = pipe_kernel_fn<3>(); break;
+        default: fn = pipe_kernel_fn<4>(); break;
+        }
+        return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN * c.KS)), args, 0,
+                               stream);
     }
     switch (l.shape.BM) {
     case 16: fn = reinterpret_cast<const void *>(&gemm_kernel<16>); break;

@@ -35,13 +35,18 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
  * `unroll` (2, 4 or 8) tiles in flight.  Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
 
-/* Batched product kernel (w2a8_gemm): 0 = automatic (default: the few-row
- * kernel for M <= 4, and for M <= 8 where the MFMA choice would be the general
- * kernel; otherwise the pipelined kernel unless the output is too small to fill
- * the device, then the general kernel), 1 = the pipelined kernel whenever K is a
- * multiple of 16 (it never splits K), 2 = the general kernel (split-K for small
- * outputs) always, 3 = the few-row kernel (GEMV-style, dot4 on decoded weights)
- * whenever M <= 8.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+/* Batched product kernel (w2a8_gemm): 0 = automatic (default), 1 = the
+ * pipelined MFMA kernel whenever K is a multiple of 16 (its configuration
+ * still chosen by shape, including the wave-group k-split for small output
+ * grids; it never splits K across workgroups), 2 = the general kernel
+ * (split-K across workgroups for small outputs) always, 3 = the few-row
+ * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8.  The automatic
+ * rule, from measurements on MI355X: the few-row kernel for M <= 2, for
+ * M <= 4 up to 49152 weight tiles, for M <= 8 with K of 40 tiles or more over
+ * at most 96 strips, and for K not a multiple of 16; otherwise the general
+ * kernel for K of 96 tiles or more when the 32-row grid is at most one
+ * workgroup per 4 CUs and the output fits the split workspace; otherwise the
+ * pipelined kernel.  Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
 
 /* The plan w2a8_gemv would use for (N, K) on a device with `cus` compute

@@ -512,7 +512,8 @@ def tune_gemv_stream(min_tiles: int, waves_per_cu: int, unroll: int):
 
 
 def tune_gemm(kernel: int):
-    """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general."""
+    """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general,
+    3 few-row whenever M <= 8."""
     _check(lib().w2a8_tune_gemm(kernel), "w2a8_tune_gemm")
 
 

@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
 # Sources that decide what the GEMV kernel reads and writes: the kernel, its
 # shared helpers and the host-side launch plan.
 GEMV_SRCS = [os.path.join(ROOT, "w2a8_gemv_amd", "csrc", f)
-             for f in ("gemv.hip", "common.h", "host.hip")]
+             for f in ("gemv.hip", "common.h", "device.h", "host.hip")]
 
 
 def gemv_sources_sha256():
@@ -90,6 +90,9 @@ def parse_args():
                     help="skip the per-shape cold timings and read floors (counter runs)")
     ap.add_argument("--eager", action="store_true",
                     help="launch each GEMV from the host instead of replaying graphs")
+    ap.add_argument("--steps-per-graph", type=int, default=16,
+                    help="consecutive steps captured in one hipGraph (default 16, one "
+                         "rotation of the weight copies)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -202,44 +205,68 @@ def make_shapes(torch, w2a8, synth, specs, mode, dev):
     return shapes, slots
 
 
-def build_graphs(torch, shapes, lib, count, stream):
-    """One graph per step; step j reads copy j of every matrix."""
+def _upload_graph(lib, g, stream):
+    """Upload an instantiated graph to the device without running it
+    (hipGraphUpload, resolved through the library's own HIP runtime, the one
+    torch uses), so that its first replay carries no one-time setup.  Best
+    effort: without the call the first replay does the upload."""
+    try:
+        up = lib.hipGraphUpload
+        up.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        up.restype = ctypes.c_int
+        up(ctypes.c_void_p(g.raw_cuda_graph_exec()), ctypes.c_void_p(stream.cuda_stream))
+    except (AttributeError, RuntimeError):
+        pass
+
+
+def build_graphs(torch, shapes, lib, first, count, stream, per_graph):
+    """Graphs of up to `per_graph` consecutive steps covering steps
+    first .. first+count-1; step j reads copy j of every matrix.  Returns
+    [(graph, steps)] and the launchers."""
     launchers = [s.launcher(lib, stream) for s in shapes]
     graphs = []
     with torch.cuda.stream(stream):
         for l in launchers:       # eager warm-up (device query, code object load)
             l(0)
     torch.cuda.synchronize()
-    for j in range(count):
+    per_graph = max(1, per_graph)
+    for start in range(first, first + count, per_graph):
+        n = min(per_graph, first + count - start)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for l in launchers:
-                l(j)
-        graphs.append(g)
+            for j in range(start, start + n):
+                for l in launchers:
+                    l(j)
+        _upload_graph(lib, g, stream)
+        graphs.append((g, n))
     torch.cuda.synchronize()
     return graphs, launchers
 
 
-def timed_steps(torch, graphs, launchers, steps, warmup, eager, stream):
-    """Warmup + timed steps.  Returns (host seconds, device us of the timed steps)."""
+def timed_steps(torch, graphs, warm_graphs, launchers, steps, warmup, eager, stream):
+    """Exactly `warmup` untimed steps, then exactly `steps` timed ones (graph
+    replays, or host launches when eager).  Returns (host seconds, device us
+    of the timed steps)."""
     with torch.cuda.stream(stream):
-        for j in range(warmup):
-            if eager:
+        if eager:
+            for j in range(warmup):
                 for l in launchers:
                     l(j)
-            else:
-                graphs[j % len(graphs)].replay()
+        else:
+            for g, _ in warm_graphs:
+                g.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()                      # barrier (one rank)
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for j in range(steps):
-            if eager:
+        if eager:
+            for j in range(steps):
                 for l in launchers:
                     l(warmup + j)
-            else:
-                graphs[j].replay()
+        else:
+            for g, _ in graphs:
+                g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -797,11 +824,16 @@ def main():
     shapes, slots = make_shapes(torch, w2a8, synth, specs, args.mode, dev)
     for s, (_, _, seed, sparse) in zip(shapes, specs):
         s.seed, s.sparse = seed, sparse
-    graphs, launchers = [], [s.launcher(lib, stream) for s in shapes]
+    graphs, warm_graphs, launchers = [], [], [s.launcher(lib, stream) for s in shapes]
     if not args.eager:
-        graphs, launchers = build_graphs(torch, shapes, lib, max(args.steps, 1), stream)
-    secs, region_us = timed_steps(torch, graphs, launchers, args.steps, args.warmup, args.eager,
-                                  stream)
+        # Warm-up steps 0..W-1, timed steps W..W+K-1 (copy j of every matrix
+        # in step j), each in graphs of up to --steps-per-graph steps.
+        warm_graphs, launchers = build_graphs(torch, shapes, lib, 0, args.warmup, stream,
+                                              args.steps_per_graph)
+        graphs, launchers = build_graphs(torch, shapes, lib, args.warmup, args.steps, stream,
+                                         args.steps_per_graph)
+    secs, region_us = timed_steps(torch, graphs, warm_graphs, launchers, args.steps,
+                                  args.warmup, args.eager, stream)
     step_bytes = sum(s.nbytes for s in shapes)
     ms_per_step = secs * 1e3 / args.steps
     value = step_bytes / (secs / args.steps) / 1e9
@@ -835,7 +867,9 @@ def main():
             "weights": "ternary, P(-1)=P(0)=P(1)=1/3, 2-bit packed",
             "activations": "int8 uniform [-127,127]",
             "rotation_copies": slots,
-            "launch": "eager" if args.eager else "one hipGraph per step",
+            "launch": "eager" if args.eager else
+                      f"hipGraphs of up to {max(1, args.steps_per_graph)} steps "
+                      f"({max(1, args.steps_per_graph) * len(shapes)} launches)",
             "bytes_per_step": step_bytes,
         },
         "roofline": {

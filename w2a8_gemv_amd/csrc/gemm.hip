@@ -30,13 +30,12 @@
 //  * Split-K (only when M*N is small): int32 partials are added atomically
 //    into the workspace; the last workgroup of a tile (arrival counter)
 //    takes the totals, resets them and applies the epilogue.
-#include "common.h"
+#include "device.h"
 
 namespace w2a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kXStride = kTileK + 16;  // LDS row stride of the activation tile
 

@@ -33,20 +33,14 @@
 //    device-scope atomic per row and workgroup (split_add in common.h); the
 //    last contributor of a row stores it with the epilogue.  Integer addition
 //    makes the result independent of arrival order: exact and deterministic.
-#include "common.h"
+#include "device.h"
 
 namespace w2a8 {
 namespace {
 
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
 // Activation chunks (16 bytes) staged per lane: a wave's run is at most
 // kXChunks * 64 / 8 = 32 tiles (the launch plan keeps RUN <= 32).
 constexpr int kXChunks = 4;
-
-__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
-    return __builtin_amdgcn_sdot4(int(a), int(b), c, false);
-}
 
 struct Acc {
     int a1[4], a4[4], a16[4];
@@ -62,15 +56,6 @@ __device__ __forceinline__ void mac(const v4u w, const v4u xv, Acc &acc) {
         acc.a16[q] = dot4(v & 0x30303030u, xv[2], acc.a16[q]);
         acc.a16[q] = dot4((v >> 2) & 0x30303030u, xv[3], acc.a16[q]);
     }
-}
-
-// Sum over the 8 lanes of a row group (lanes 8j..8j+7) with DPP moves:
-// xor 1 and xor 2 inside quads, then the mirrored half-row (lane i <-> 7-i).
-__device__ __forceinline__ int sum8(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    return v;
 }
 
 // The projection a strip belongs to.  Plain launch: the launch's own matrix
@@ -135,17 +120,6 @@ __device__ __forceinline__ v4u quant16(const v4u lo, const v4u hi, float inv) {
 // Bf16 activation chunks that each thread loads, before the weights, for the
 // row maximum of the fused kernel (the rest, if any, after them).
 constexpr int kAmaxChunks = 2;
-
-// Loads of batch b (tiles w0 + b*U + u, clamped to the run's last tile).
-template <int U>
-__device__ __forceinline__ void load_batch(const v4u *wt, int w0, int last, int b, v4u (&w)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        w[u] = __builtin_nontemporal_load(wt + min(w0 + b * U + u, last) * (kTileBytes / 16));
-    // Keep the loads here: the scheduler would otherwise sink them towards
-    // their uses and shorten the prefetch distance.
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 // Multiply batch b (only tiles inside the run) against the staged activations.
 template <int U>

@@ -18,36 +18,17 @@
 //    (the int8 kernel needs 9), one accumulator per row;
 //  * sum_k x (for sum w*x = sum c*x - sum x) is v_dot8 against 0x11111111.
 #include "a4.h"
+#include "device.h"
 
 namespace w2a8 {
 namespace {
 
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kA4TileBytes = kTileK / 2;   // activation bytes per k-tile (64)
 // Activation granules (16 bytes, 2 chunks) staged per lane: runs of at most
 // 32 tiles = 128 granules.
 constexpr int kA4Granules = 2;
 
-__device__ __forceinline__ int dot8(uint32_t a, uint32_t b, int c) {
-    return __builtin_amdgcn_sdot8(int(a), int(b), c, false);
-}
-
-__device__ __forceinline__ int sum8(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    return v;
-}
-
-template <int U>
-__device__ __forceinline__ void load_batch(const v4u *wt, int w0, int last, int b, v4u (&w)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        w[u] = __builtin_nontemporal_load(wt + min(w0 + b * U + u, last) * (kTileBytes / 16));
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 __device__ __forceinline__ void mac_a4(const v4u w, const v2u xv, int (&acc)[4]) {
 #pragma unroll

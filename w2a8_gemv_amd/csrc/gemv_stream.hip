@@ -28,21 +28,15 @@
 // Off by default: on gfx950 the workgroup kernel is as fast or faster on the
 // measured shapes (the end-of-stream atomic round trip and the per-workgroup
 // staging of all of K are fixed costs this kernel pays).
-#include "common.h"
+#include "device.h"
 
 namespace w2a8 {
 namespace {
-
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = 64 * kWavesPerBlock;
 // Activation chunks (16 bytes) each thread stages: K <= kStageChunks*16*256.
 constexpr int kStageChunks = 8;
-
-__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
-    return __builtin_amdgcn_sdot4(int(a), int(b), c, false);
-}
 
 struct Acc {
     int a1[4], a4[4], a16[4];
@@ -67,14 +61,6 @@ __device__ __forceinline__ void mac(const v4u w, const v4u xv, Acc &acc) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.sx = dot4(xv[j], 0x01010101u, acc.sx);
-}
-
-// Sum over the 8 lanes of a row group (lanes 8j..8j+7) with DPP moves.
-__device__ __forceinline__ int sum8(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-    return v;
 }
 
 // Row value owned by this lane (rows 4rg + kg for kg < 4) of a finished

@@ -16,12 +16,11 @@
 // place of 127 and writes the A4I layout (a4.h).
 #include "a4.h"
 #include "common.h"
+#include "device.h"
 
 namespace w2a8 {
 namespace {
 
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *xb, int M, int K, int8_t *xq,
                                                     float *sa) {

@@ -103,11 +103,13 @@ int64_t w2a8_packed_bytes(int64_t N, int64_t K);
 /* Device workspace bytes that w2a8_gemv / w2a8_gemm need for (M, N, K),
  * or -1 if out of range.  For M = 1 it holds one 64-bit word per row, padded
  * to 32 rows (the tile count and partial sum of a row whose k-range is split
- * over several waves); for M > 1, int32 partial sums and arrival counters of
- * split-K output blocks (0 bytes when M*N is too large for split-K, which is
- * then not used).  The caller allocates it, zeroes
- * it ONCE before its first use, and may then reuse it for any call with the
- * same or smaller (M, N, K): each call leaves it zeroed again. */
+ * over several waves); for 2 <= M <= 8, the larger of one such word per
+ * (row, padded output) and the split-K space below; for M > 8, int32 partial
+ * sums and arrival counters of split-K output blocks (0 bytes when M*N is
+ * too large for split-K, which is then not used).  The caller allocates it,
+ * zeroes it ONCE before its first use, and may then reuse it for any call
+ * whose w2a8_workspace_bytes is no larger: each call leaves it zeroed
+ * again. */
 int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ------------------------------------------------------------------------

@@ -55,14 +55,17 @@ def test_gemm_small_ragged(M, N, K):
 # (M <= 32, above, M >= 256 over >= 256 strips, whose 128 x 256 tile is
 # ragged in M, N and K at 333 x 8230 x 1040, and the small-grid ones whose
 # 2 or 4 wave groups split K: k-tile counts 9, 20, 25 for 2 groups and
-# 40, 41, 43 for 4, so that the last group may have fewer tiles), K below one
+# 40, 41, 43 for 4, so that the last group may have fewer tiles, with 32-row
+# tiles and, for M <= 16, 16-row tiles whose activation tile is loaded by
+# two waves each), K below one
 # ring of tiles (K = 16, 144), a k-tile remainder (KT % 4 = 1, 2, 3), a
 # partial last tile (K = 1040, 5200) and ragged N (strips past the matrix,
 # rows past N in the last strip).
 FORCED = [(8, 1000, 1040), (33, 100, 16), (64, 2560, 144), (100, 97, 2560), (128, 200, 384),
           (200, 1000, 1040), (257, 33, 3200), (2, 4096, 896), (17, 130, 640),
           (333, 8230, 1040), (256, 8192, 64), (40, 300, 5248), (96, 200, 5504),
-          (129, 520, 5200), (48, 640, 5120)]
+          (129, 520, 5200), (48, 640, 5120), (12, 1000, 2560), (16, 300, 5248), (9, 2600, 1040),
+          (3, 97, 5504)]
 
 
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])

@@ -276,8 +276,18 @@ struct Pipe {
     static constexpr int NSTRIP = WN * SPW;            // strips per workgroup
     static_assert(NSTRIP % NW == 0, "whole weight strips per wave");
     static constexpr int LS = NSTRIP / NW;             // weight strip loads per wave per tile
-    static constexpr int DPW = BM * 8 / 64 / NW;       // activation loads per wave per tile
-    static_assert(DPW >= 1 && DPW * 64 * NW == BM * 8, "tile must split evenly over waves");
+    // The activation tile is NPART parts of 1 KiB (one load instruction
+    // each).  With fewer parts than waves (16-row tiles), waves w and
+    // w + NPART load the same part: every wave then issues the same number of
+    // loads, so the wait counts below stay compile-time constants.
+    static constexpr int NPART = BM * 8 / 64;
+    static constexpr int DPW = NPART >= NW ? NPART / NW : 1;   // activation loads per wave per tile
+    static_assert(NPART >= NW ? DPW * NW == NPART : NW % NPART == 0,
+                  "tile must split evenly over waves");
+    // Part loaded by instruction d of wave wv.
+    static __device__ __forceinline__ int part(int wv, int d) {
+        return NPART >= NW ? wv * DPW + d : wv % NPART;
+    }
     static constexpr int LPT = DPW + LS;               // loads per wave per tile
     static constexpr int WAITN = (S - 2) * LPT;        // issued after a tile's group when used
     static_assert(WAITN <= 63, "wait count must fit vmcnt");
@@ -298,7 +308,7 @@ __device__ __forceinline__ void pipe_issue(int8_t *stage, int tc, int K, int wv,
         const int k = k0 < K - 16 ? k0 : K - 16;
         __builtin_amdgcn_global_load_lds(
             xsrc[d] + k,
-            (__attribute__((address_space(3))) void *)(stage + (wv * P::DPW + d) * 1024), 16, 0, 0);
+            (__attribute__((address_space(3))) void *)(stage + P::part(wv, d) * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int ls = 0; ls < P::LS; ++ls)
@@ -383,12 +393,12 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs a
     const int KT = a.KT;
 
     // Activation loads: instruction d of this wave covers chunk positions
-    // p = (wv*DPW + d)*64 + lane of a stage.
+    // p = part(wv, d)*64 + lane of a stage.
     const int8_t *xsrc[P::DPW];
     int kcb[P::DPW];
 #pragma unroll
     for (int d = 0; d < DPW; ++d) {
-        const int p = (wv * DPW + d) * 64 + lane;
+        const int p = P::part(wv, d) * 64 + lane;
         const int r = p >> 3, c = (p & 7) ^ (r & 7);
         xsrc[d] = a.x + int64_t(min(m0 + r, a.M - 1)) * a.K;
         kcb[d] = 16 * c;
@@ -548,13 +558,14 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs a
 // splitting K).  Chosen by sweeps on MI355X over block rows 32..256, four
 // wave layouts, depths 3..8 and 1, 2 or 4 wave groups: 32 rows (depth 4) for
 // M <= 32 and 64 rows (depth 3) above won or tied on every prefill shape with
-// a large output grid up to M = 448, a 128 x 256 tile beyond, 32 rows with 2
-// or 4 wave groups (depth 3) on small grids.
+// a large output grid up to M = 448, a 128 x 256 tile beyond, 32 rows (16
+// for M <= 16) with 2 or 4 wave groups (depth 3) on small grids.
 struct PipeCfg {
     int BM, WM, WN, SPW, S, KS;
 };
-constexpr PipeCfg kPipeCfg[5] = {{32, 1, 4, 1, 4, 1},  {64, 1, 4, 1, 3, 1}, {128, 1, 8, 1, 4, 1},
-                                 {32, 1, 4, 1, 3, 2},  {32, 1, 4, 1, 3, 4}};
+constexpr PipeCfg kPipeCfg[7] = {{32, 1, 4, 1, 4, 1}, {64, 1, 4, 1, 3, 1}, {128, 1, 8, 1, 4, 1},
+                                 {32, 1, 4, 1, 3, 2}, {32, 1, 4, 1, 3, 4}, {16, 1, 4, 1, 3, 2},
+                                 {16, 1, 4, 1, 3, 4}};
 
 // The kernel instance of configuration P.
 template <int P>
@@ -574,7 +585,8 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         //    at most one per CU and K has 40 tiles or more, else 2 (the lone
         //    wave's k-step latency is the bound there: 2560 x 6912 at M = 128
         //    went from 22.4 to 12.6 us, 13824 x 2560 at M = 8 from 9.3 to
-        //    7.3 us);
+        //    7.3 us); 16-row tiles for M <= 16, whose activation tile is
+        //    half as large (55296 x 5120 at M = 8: 15.2 against 16.9 us);
         //  * otherwise 32 or 64 rows per workgroup by M, and a 128 x 256
         //    workgroup tile (8 waves, each decoded weight block used by 8
         //    activation blocks) for M > 448 over at least 256 strips
@@ -589,7 +601,7 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         const int64_t g32 = ceil_div(M, 32) * ceil_div(NS, 4);
         int pipe;
         if (KT >= 8 && g32 <= int64_t(cus) * 7 / 4)
-            pipe = (KT >= 40 && g32 <= cus) ? 4 : 3;
+            pipe = ((KT >= 40 && g32 <= cus) ? 4 : 3) + (M <= 16 ? 2 : 0);
         else
             pipe = M <= 32 ? 0 : (M > 448 && NS >= 256) ? 2 : 1;
         const PipeCfg &c = kPipeCfg[pipe];
@@ -655,7 +667,9 @@ hipError_t launch_gemm(const GemmLaunch &l, hipStream_t stream) {
         case 1: fn = pipe_kernel_fn<1>(); break;
         case 2: fn = pipe_kernel_fn<2>(); break;
         case 3: fn = pipe_kernel_fn<3>(); break;
-        default: fn = pipe_kernel_fn<4>(); break;
+        case 4: fn = pipe_kernel_fn<4>(); break;
+        case 5: fn = pipe_kernel_fn<5>(); break;
+        default: fn = pipe_kernel_fn<6>(); break;
         }
         return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN * c.KS)), args, 0,
                                stream);

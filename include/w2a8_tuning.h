@@ -41,7 +41,7 @@ int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
  * grids; it never splits K across workgroups), 2 = the general kernel
  * (split-K across workgroups for small outputs) always, 3 = the few-row
  * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8.  The automatic
- * rule, from measurements on MI355X: the few-row kernel for M <= 2, for
+ * rule, from measurements on MI355X: the few-row kernel for
  * M <= 4 up to 49152 weight tiles, for M <= 8 with K of 40 tiles or more over
  * at most 96 strips, and for K not a multiple of 16; otherwise the general
  * kernel for K of 96 tiles or more when the 32-row grid is at most one

@@ -532,16 +532,16 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
     a.NS = int(Np / kTileRows);
     a.shape = gemm_shape(M, N, K, dev.cus, need > 0);
     // Few rows: the GEMV-style kernel over M activation rows.  Automatic
-    // choice (measured on MI355X, cold weights): M <= 2 always (2560 x 6912:
-    // 5.2 against 10.2 us for the best MFMA kernel); M <= 4 up to 49152
-    // weight tiles (5120 x 27648: 16.4 against 23.4 us; at 55296 x 5120 the
-    // MFMA kernel wins, 17.1 against 25.0 us); M <= 8 for long K (40 k-tiles
-    // or more) over at most 96 strips (2560 x 6912: 10.3 against 12.0 us; at
-    // 13824 x 2560 and 5120 x 27648 the MFMA kernels win); and ragged K
-    // (not a multiple of 16), where the MFMA path is the general kernel.
+    // choice (measured on MI355X, cold weights): M <= 4 up to 49152 weight
+    // tiles (2560 x 6912 at M = 2: 5.1 against 10.3 us for the best MFMA
+    // kernel; 5120 x 27648 at M = 4: 16.1 against 22.7 us; at 55296 x 5120
+    // the MFMA kernel wins, 15.7 against 24.9 us at M = 4); M <= 8 for long K
+    // (40 k-tiles or more) over at most 96 strips (2560 x 6912: 10.0 against
+    // 10.7 us); and ragged K (not a multiple of 16), where the MFMA path is
+    // the general kernel.
     const int mode = gemm_kernel_mode();
     const int64_t wtiles = int64_t(a.NS) * a.KT;
-    const bool few_auto = K % 16 != 0 || M <= 2 || (M <= 4 && wtiles <= 49152) ||
+    const bool few_auto = K % 16 != 0 || (M <= 4 && wtiles <= 49152) ||
                           (a.KT >= 40 && a.NS <= 96);
     const bool few = M <= kRowsMaxM && (mode == 3 || (mode == 0 && few_auto));
     if (few) {

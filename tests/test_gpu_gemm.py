@@ -77,8 +77,9 @@ def test_gemm_forced_kernel(kernel, M, N, K):
     np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
 
 
-@pytest.mark.parametrize("M,N,K", [(150, 700, 1024), (40, 500, 6912)],
-                         ids=["2-groups", "4-groups"])
+@pytest.mark.parametrize("M,N,K", [(150, 700, 1024), (40, 500, 6912), (10, 300, 2560),
+                                   (13, 200, 5248)],
+                         ids=["2-groups", "4-groups", "16-rows-2-groups", "16-rows-4-groups"])
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
 def test_gemm_forced_kernel_fp32_epilogue(kernel, M, N, K):
     w2a8.tune_gemm(kernel)

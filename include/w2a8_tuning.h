@@ -40,12 +40,11 @@ int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
  * still chosen by shape, including the wave-group k-split for small output
  * grids; it never splits K across workgroups), 2 = the general kernel
  * (split-K across workgroups for small outputs) always, 3 = the few-row
- * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8.  The automatic
+ * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8, the
+ * automatic choice above that.  The automatic
  * rule, from measurements on MI355X: the few-row kernel for
- * M <= 4 up to 49152 weight tiles, for M <= 8 with K of 40 tiles or more over
- * at most 96 strips, and for K not a multiple of 16; otherwise the general
- * kernel for K of 96 tiles or more when the 32-row grid is at most one
- * workgroup per 4 CUs and the output fits the split workspace; otherwise the
+ * M <= 2 up to 49152 weight tiles and for K not a multiple of 16 (M <= 8);
+ * the general kernel for K not a multiple of 16 above that; otherwise the
  * pipelined kernel.  Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
 

@@ -52,23 +52,25 @@ def test_gemm_small_ragged(M, N, K):
 
 
 # Each kernel forced onto ragged shapes: every pipelined configuration
-# (M <= 32, above, M >= 256 over >= 256 strips, whose 128 x 256 tile is
-# ragged in M, N and K at 333 x 8230 x 1040, and the small-grid ones whose
-# 2 or 4 wave groups split K: k-tile counts 9, 20, 25 for 2 groups and
+# (M <= 32, above, M > 448 over >= 256 strips, whose 128 x 256 tile is
+# ragged in M, N and K at 460 x 8230 x 272, and the small-grid ones whose
+# 2 or 4 wave groups split K: k-tile counts 9 and 20 for 2 groups and
 # 40, 41, 43 for 4, so that the last group may have fewer tiles, with 32-row
 # tiles and, for M <= 16, 16-row tiles whose activation tile is loaded by
-# two waves each; and the workgroups of 2 strips with 8 groups of 16-row
-# tiles or 4 groups of 32-row tiles, on 41, 43, 54 and 40 k-tiles with
-# ragged M and N), K below one
+# two waves each; the workgroups of one strip with 8 groups of 16-row tiles
+# on 20 to 54 k-tiles, and those of 2 strips with 8 groups of 16-row tiles
+# or 4 groups of 32-row tiles, on 21, 40 and 43 k-tiles with ragged M and N),
+# K below one
 # ring of tiles (K = 16, 144), a k-tile remainder (KT % 4 = 1, 2, 3), a
-# partial last tile (K = 1040, 5200) and ragged N (strips past the matrix,
-# rows past N in the last strip).
+# partial last tile (K = 1040, 2608, 5200) and ragged N (strips past the
+# matrix, rows past N in the last strip).
 FORCED = [(8, 1000, 1040), (33, 100, 16), (64, 2560, 144), (100, 97, 2560), (128, 200, 384),
           (200, 1000, 1040), (257, 33, 3200), (2, 4096, 896), (17, 130, 640),
           (333, 8230, 1040), (256, 8192, 64), (40, 300, 5248), (96, 200, 5504),
           (129, 520, 5200), (48, 640, 5120), (12, 1000, 2560), (16, 300, 5248), (9, 2600, 1040),
           (3, 97, 5504), (24, 300, 5248), (100, 700, 6912), (129, 2600, 5120), (40, 97, 5504),
-          (12, 20000, 5120)]
+          (12, 20000, 5504), (100, 1500, 2608), (300, 1000, 2608), (460, 8230, 272),
+          (200, 3000, 2560), (200, 3000, 5248), (41, 5000, 5504)]
 
 
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
@@ -80,10 +82,11 @@ def test_gemm_forced_kernel(kernel, M, N, K):
     np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
 
 
-@pytest.mark.parametrize("M,N,K", [(150, 700, 1024), (200, 3000, 5120), (10, 300, 2560),
-                                   (13, 2600, 1040), (50, 400, 5120), (129, 2600, 5120)],
+@pytest.mark.parametrize("M,N,K", [(150, 700, 1024), (200, 3000, 5120), (10, 300, 2432),
+                                   (13, 2600, 1040), (50, 400, 5120), (100, 1500, 2608),
+                                   (129, 2600, 5120)],
                          ids=["2-groups", "4-groups", "16-rows-2-groups", "16-rows-2-groups-b",
-                              "2-strips-8-groups", "2-strips-4-groups"])
+                              "1-strip-8-groups", "2-strips-8-groups", "2-strips-4-groups"])
 @pytest.mark.parametrize("kernel", [1, 2], ids=["pipelined", "general"])
 def test_gemm_forced_kernel_fp32_epilogue(kernel, M, N, K):
     w2a8.tune_gemm(kernel)
@@ -99,11 +102,12 @@ def test_gemm_forced_kernel_fp32_epilogue(kernel, M, N, K):
 
 
 # Automatic choice on small output grids, where the k-range is split over
-# wave groups inside a workgroup (8 groups in workgroups of 2 strips:
-# 9 x 2560 x 6912, 16 x 100 x 5248; 2 groups: 100 x 13824 x 2176,
+# wave groups inside a workgroup (8 groups in workgroups of one strip:
+# 9 x 2560 x 6912, 16 x 100 x 5248; of 2 strips: 16 x 13824 x 2560; 4 groups
+# in workgroups of 2 strips: 32 x 13824 x 2560; 2 groups: 100 x 13824 x 2176,
 # 32 x 2560 x 1040), with odd tile counts.
-@pytest.mark.parametrize("M,N,K", [(9, 2560, 6912), (16, 100, 5248), (100, 13824, 2176),
-                                   (32, 2560, 1040)])
+@pytest.mark.parametrize("M,N,K", [(9, 2560, 6912), (16, 100, 5248), (16, 13824, 2560),
+                                   (32, 13824, 2560), (100, 13824, 2176), (32, 2560, 1040)])
 def test_gemm_wave_group_split_auto(M, N, K):
     x, w = synth.gemm_case(M, N, K, seed=M * N + K)
     y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)

@@ -560,14 +560,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs a
 // M <= 32 and 64 rows (depth 3) above won or tied on every prefill shape with
 // a large output grid up to M = 448, a 128 x 256 tile beyond, 32 rows (16
 // for M <= 16) with 2 or 4 wave groups (depth 3) on small grids, and
-// workgroups of 2 strips with 4 or 8 wave groups on the smallest grids with
-// long K.
+// workgroups of 1 or 2 strips with 4 or 8 wave groups on the smallest grids
+// with K of 20 tiles or more.
 struct PipeCfg {
     int BM, WM, WN, SPW, S, KS;
 };
-constexpr PipeCfg kPipeCfg[9] = {{32, 1, 4, 1, 4, 1}, {64, 1, 4, 1, 3, 1}, {128, 1, 8, 1, 4, 1},
-                                 {32, 1, 4, 1, 3, 2}, {32, 1, 4, 1, 3, 4}, {16, 1, 4, 1, 3, 2},
-                                 {16, 1, 4, 1, 3, 4}, {32, 1, 2, 1, 3, 4}, {16, 1, 2, 1, 3, 8}};
+constexpr PipeCfg kPipeCfg[10] = {{32, 1, 4, 1, 4, 1}, {64, 1, 4, 1, 3, 1}, {128, 1, 8, 1, 4, 1},
+                                  {32, 1, 4, 1, 3, 2}, {32, 1, 4, 1, 3, 4}, {16, 1, 4, 1, 3, 2},
+                                  {16, 1, 4, 1, 3, 4}, {32, 1, 2, 1, 3, 4}, {16, 1, 2, 1, 3, 8},
+                                  {16, 1, 1, 1, 3, 8}};
 
 // The kernel instance of configuration P.
 template <int P>
@@ -594,23 +595,32 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         //    activation blocks) for M > 448 over at least 256 strips
         //    (24.7 against 29.9 us at M = 512, 13824 x 2560; at M = 448 the
         //    64-row tile is still ahead, 23.5 against 24.5 us);
-        //  * long K (40 k-tiles or more) over few strips: workgroups of 2
-        //    strips, so that the grid doubles, with 8 wave groups and 16-row
-        //    tiles while that grid is at most one workgroup per CU, else 4
-        //    groups and 32-row tiles while that one is (2560 x 6912 at
-        //    M = 64: 8.0 against 13.1 us, at M = 128: 9.6 against 12.6 us;
-        //    5120 x 27648 at M = 32: 18.6 against 31 us);
-        //  * otherwise a grid of at most one 32-row workgroup per 4 CUs with
-        //    long K (96 k-tiles or more) takes the general kernel split over
-        //    K across workgroups when the workspace allows it.
+        //  * K of 20 tiles or more over few strips: workgroups of one strip
+        //    with 8 wave groups and 16-row tiles while that grid is at most
+        //    one workgroup per CU (2560 x 6912 at M = 8: 6.0 against 8.2 us,
+        //    5120 x 27648 at M = 16: 14.8 against 18.2 us), else workgroups
+        //    of 2 strips, so that the grid doubles, with 8 wave groups and
+        //    16-row tiles while that grid is, else 4 groups and 32-row tiles
+        //    while that one is (2560 x 6912 at M = 64: 8.0 against 13.1 us,
+        //    at M = 128: 9.6 against 12.6 us; 5120 x 27648 at M = 32: 18.6
+        //    against 31 us; 13824 x 2560 at M = 16: 6.2 against 8.2 us).
+        //    These also beat the general kernel's split over K across
+        //    workgroups on every grid it used to take (at most one 32-row
+        //    workgroup per 4 CUs with 96 k-tiles or more: 5120 x 27648 at
+        //    M = 8, 14.6 against 23.6 us), so the automatic choice no longer
+        //    takes it when K is a multiple of 16.
         const int64_t NS = round_up(N, kTileRows) / kTileRows;
         const int64_t KT = round_up(K, kTileK) / kTileK;
         const int64_t g32 = ceil_div(M, 32) * ceil_div(NS, 4);
         const int64_t n2 = ceil_div(NS, 2);
-        const bool narrow16 = KT >= 40 && ceil_div(M, 16) * n2 <= cus;
-        const bool narrow32 = KT >= 40 && ceil_div(M, 32) * n2 <= cus;
+        const bool narrow = KT >= 20;
+        const bool one16 = narrow && ceil_div(M, 16) * NS <= cus;
+        const bool narrow16 = narrow && ceil_div(M, 16) * n2 <= cus;
+        const bool narrow32 = narrow && ceil_div(M, 32) * n2 <= cus;
         int pipe;
-        if (narrow16)
+        if (one16)
+            pipe = 9;
+        else if (narrow16)
             pipe = 8;
         else if (narrow32)
             pipe = 7;
@@ -621,8 +631,7 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         const PipeCfg &c = kPipeCfg[pipe];
         const int64_t mblk = ceil_div(M, c.BM), nblk = ceil_div(NS, int64_t(c.WN) * c.SPW);
         const int mode = gemm_kernel_mode();
-        const bool tiny_long = can_split && KT >= 96 && g32 <= cus / 4 && pipe < 7;
-        if (mode == 1 || (mode == 0 && !tiny_long)) {
+        if (mode != 2) {
             g.pipe = pipe;
             g.BM = c.BM;
             g.MBLK = int(mblk);
@@ -685,7 +694,8 @@ hipError_t launch_gemm(const GemmLaunch &l, hipStream_t stream) {
         case 5: fn = pipe_kernel_fn<5>(); break;
         case 6: fn = pipe_kernel_fn<6>(); break;
         case 7: fn = pipe_kernel_fn<7>(); break;
-        default: fn = pipe_kernel_fn<8>(); break;
+        case 8: fn = pipe_kernel_fn<8>(); break;
+        default: fn = pipe_kernel_fn<9>(); break;
         }
         return hipLaunchKernel(fn, dim3(blocks), dim3(unsigned(64 * c.WM * c.WN * c.KS)), args, 0,
                                stream);

@@ -532,16 +532,16 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
     a.NS = int(Np / kTileRows);
     a.shape = gemm_shape(M, N, K, dev.cus, need > 0);
     // Few rows: the GEMV-style kernel over M activation rows.  Automatic
-    // choice (measured on MI355X, cold weights): M <= 4 up to 49152 weight
-    // tiles (2560 x 6912 at M = 2: 5.1 against 10.3 us for the best MFMA
-    // kernel, at M = 4: 6.6 against 7.8 us; 5120 x 27648 at M = 4: 16.1
-    // against 22.7 us; at 55296 x 5120 the MFMA kernel wins, 15.7 against
-    // 24.9 us at M = 4), and ragged K (not a multiple of 16), where the MFMA
-    // path is the general kernel.  From M = 5 the MFMA kernels win (2560 x
-    // 6912 at M = 8: 7.9 against 10.0 us).
+    // choice (measured on MI355X, cold weights): M <= 2 up to 49152 weight
+    // tiles (2560 x 6912: 5.1 against 6.7 us for the best MFMA kernel;
+    // 5120 x 27648: 10.9 against 14.3 us; at 55296 x 5120 the two tie near
+    // 16 us), and ragged K (not a multiple of 16), where the MFMA path is
+    // the general kernel.  From M = 3 the MFMA kernels with wave groups
+    // splitting K win or tie (5120 x 27648 at M = 4: 14.6 against 16.3 us;
+    // 13824 x 2560 at M = 3: 6.2 against 7.2 us).
     const int mode = gemm_kernel_mode();
     const int64_t wtiles = int64_t(a.NS) * a.KT;
-    const bool few_auto = K % 16 != 0 || (M <= 4 && wtiles <= 49152);
+    const bool few_auto = K % 16 != 0 || (M <= 2 && wtiles <= 49152);
     const bool few = M <= kRowsMaxM && (mode == 3 || (mode == 0 && few_auto));
     if (few) {
         GemvLaunch g;

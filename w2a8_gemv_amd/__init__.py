@@ -23,7 +23,8 @@ __all__ = [
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
     "w2a8_linear_gemv", "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream", "tune_gemm",
-    "DEFAULT_GEMV_STREAM_POLICY",
+    "DEFAULT_GEMV_STREAM_POLICY", "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
+    "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw2a8.so")

@@ -74,9 +74,14 @@ constexpr int64_t kSplitWgs = 12;
 //    Partials are combined with one device-scope atomic per row.
 //    ktw <= krange_tiles always.
 //  * A workgroup splits its range over WK <= 16 waves with runs of about
-//    tiles_per_wave tiles (tiles_per_wave + 2 in a split strip; at most 32:
-//    each lane stages at most four 16-byte activation chunks); their row sums
-//    are combined through LDS.
+//    tiles_per_wave tiles (tiles_per_wave + 2 in a split strip, half of
+//    tiles_per_wave in an unsplit strip when there are no more strips than
+//    CUs; at most 32: each lane stages at most four 16-byte activation
+//    chunks); their row sums are combined through LDS.  On those small grids
+//    most CUs are idle and shorter runs finish sooner (measured on MI355X,
+//    cold: 8 waves of 2-3 tiles against 4 waves of 5-7 tiles take 0.10 to
+//    0.20 us less at 2560 x 2560, 3840 x 2560, 3200 x 3200 and 4800 x 3200;
+//    at 55296 x 5120, 1728 strips, halving the runs costs 2.8 us).
 //  * The load batch U (two in flight per wave) is the smallest of 2, 4, 8
 //    (at most `unroll`) whose two batches cover the run.
 void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll) {
@@ -92,7 +97,8 @@ void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int 
     const int64_t ktw = ceil_div(KT, SG);
     // Runs of a split strip may be a little longer: its extra waves cost an
     // LDS combine on top of the atomic one.
-    int64_t WK = ceil_div(ktw, SG > 1 ? tpw + 2 : tpw);
+    const int64_t run_tiles = SG > 1 ? tpw + 2 : NS <= cus ? std::max<int64_t>(1, tpw / 2) : tpw;
+    int64_t WK = ceil_div(ktw, run_tiles);
     // An unsplit strip with more than two waves: a multiple of four, so the
     // workgroup spreads evenly over the compute unit's four SIMDs (5 or 7
     // waves measured slower than 4 or 8).

@@ -598,12 +598,12 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         //  * K of 20 tiles or more over few strips: workgroups of one strip
         //    with 8 wave groups and 16-row tiles while that grid is at most
         //    one workgroup per CU (2560 x 6912 at M = 8: 6.0 against 8.2 us,
-        //    5120 x 27648 at M = 16: 14.8 against 18.2 us), else workgroups
+        //    5120 x 27648 at M = 8: 14.6 against 18.2 us), else workgroups
         //    of 2 strips, so that the grid doubles, with 8 wave groups and
         //    16-row tiles while that grid is, else 4 groups and 32-row tiles
         //    while that one is (2560 x 6912 at M = 64: 8.0 against 13.1 us,
         //    at M = 128: 9.6 against 12.6 us; 5120 x 27648 at M = 32: 18.6
-        //    against 31 us; 13824 x 2560 at M = 16: 6.2 against 8.2 us).
+        //    against 31 us; 13824 x 2560 at M = 8: 6.1 against 7.2 us).
         //    These also beat the general kernel's split over K across
         //    workgroups on every grid it used to take (at most one 32-row
         //    workgroup per 4 CUs with 96 k-tiles or more: 5120 x 27648 at

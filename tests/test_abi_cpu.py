@@ -424,6 +424,23 @@ def test_gemv_plan_properties():
         w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
 
 
+def test_gemv_default_plans_of_the_measured_shapes():
+    """The default rule's plans (waves per workgroup, workgroups per strip,
+    load batch) on a 256-CU device for the shapes its choices were measured
+    on: twice the waves with half-length runs in unsplit strips while there
+    are no more strips than CUs, 4-wave workgroups above that, and a split
+    over workgroups for strips of 48 k-tiles or more."""
+    assert w2a8.DEFAULT_GEMV_POLICY == (4, 6, 8, 256, 48)
+    want = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
+            (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),
+            (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 12, 4),
+            (5120, 27648): (3, 12, 4), (55296, 5120): (8, 1, 4)}
+    for (N, K), plan in want.items():
+        assert tuple(w2a8.gemv_plan(N, K, 256)) == plan + (0,), (N, K)
+    # The same 80-strip matrix on a 64-CU device has more strips than CUs.
+    assert tuple(w2a8.gemv_plan(2560, 2560, 64)) == (4, 1, 4, 0)
+
+
 def test_binding_refuses_host_tensors_for_device_calls():
     with pytest.raises(ValueError):
         w2a8.quant_act_int8(torch.zeros((1, 16), dtype=torch.bfloat16))

@@ -429,12 +429,15 @@ def test_gemv_default_plans_of_the_measured_shapes():
     load batch) on a 256-CU device for the shapes its choices were measured
     on: twice the waves with half-length runs in unsplit strips while there
     are no more strips than CUs, 4-wave workgroups above that, and a split
-    over workgroups for strips of 48 k-tiles or more."""
+    over workgroups for strips of 48 k-tiles or more, into equal k-ranges
+    where one of the two smaller counts gives them (3200 x 10240: 10 ranges
+    of 8 tiles, not 12 of 7; 2560 x 27648: 12 of 18, not 13 of 17)."""
     assert w2a8.DEFAULT_GEMV_POLICY == (4, 6, 8, 256, 48)
     want = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
             (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),
-            (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 12, 4),
-            (5120, 27648): (3, 12, 4), (55296, 5120): (8, 1, 4)}
+            (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 10, 4),
+            (5120, 27648): (3, 12, 4), (55296, 5120): (8, 1, 4), (2560, 27648): (3, 12, 4),
+            (8192, 8192): (1, 11, 4)}
     for (N, K), plan in want.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == plan + (0,), (N, K)
     # The same 80-strip matrix on a 64-CU device has more strips than CUs.

@@ -62,6 +62,8 @@ struct GemvLaunch {
     int unroll;
     int G;        // streaming kernel: waves in the grid (0: workgroup-split kernel)
     int TQ, TR;   // streaming kernel: NS*KT = TQ*G + TR (wave w starts at w*TQ + min(w, TR))
+    int DXOK = 0; // plain kernel: at most 5 waves per CU in the grid, so activation chunks may
+                  // be loaded directly with the weights (latency-bound grids)
     // Workgroup kernel, set by its launcher so that the kernel divides
     // nothing: KT = KQ*SG + KR (k-range g starts at g*KQ + min(g, KR) and has
     // KQ + (g < KR) tiles), and a range of KQ + i tiles = WQi*WK + WRi (wave

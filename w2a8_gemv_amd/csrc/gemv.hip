@@ -135,6 +135,41 @@ __device__ __forceinline__ void mac_batch(const v4u (&w)[U], const uint8_t *xl, 
     }
 }
 
+// Direct activations: the 16-byte chunk k = 128t + 16kg .. +15 of each tile
+// t of batch b, loaded from global memory next to the tile's weights (all
+// lanes of a row group read the same 128 bytes, one cache line per tile and
+// wave).  Chunks at or past K (K a multiple of 16) load a chunk inside the
+// row and are zeroed where they are used, so no load is conditional.
+template <int U>
+__device__ __forceinline__ void load_x(const int8_t *x, int w0, int last, int b, int kg,
+                                       int nchunk, v4u (&xv)[U]) {
+    const v4u *xp = reinterpret_cast<const v4u *>(x);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        xv[u] = xp[min(min(w0 + b * U + u, last) * (kTileK / 16) + kg, nchunk - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Multiply batch b against its directly loaded activation chunks, and add
+// those chunks' sum to sxl.
+template <int U>
+__device__ __forceinline__ void mac_batch_dx(const v4u (&w)[U], const v4u (&xv)[U], int w0,
+                                             int n, int b, int kg, int K, Acc &acc, int &sxl) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (b * U + u < n) {
+            const int t = w0 + b * U + u;
+            const bool in = t * kTileK + 16 * kg < K;
+            const v4u x = in ? xv[u] : v4u{0u, 0u, 0u, 0u};
+            mac(w[u], x, acc);
+            sxl = dot4(x[0], 0x01010101u, sxl);
+            sxl = dot4(x[1], 0x01010101u, sxl);
+            sxl = dot4(x[2], 0x01010101u, sxl);
+            sxl = dot4(x[3], 0x01010101u, sxl);
+        }
+    }
+}
+
 // FUSED: the activations arrive as one bf16 row (a.xb).  Every workgroup
 // takes the row's largest |x| itself, quantizes its own k-range with the same
 // per-element operations as the quantizer kernel (q8 in common.h) and scale
@@ -143,8 +178,13 @@ __device__ __forceinline__ void mac_batch(const v4u (&w)[U], const uint8_t *xl, 
 // GROUPED: the strip's matrix, outputs and weight scale come from the
 // projection table t (select_proj); the split-k workspace words are indexed
 // by the strip's position in the whole launch.
-template <int U, bool FUSED, bool GROUPED>
+// DX (not FUSED, K a multiple of 16): activation chunks are loaded with each
+// batch of weights straight into registers (load_x) instead of being staged
+// through LDS first, which removes the staging and its wait from the start
+// of every wave.
+template <int U, bool FUSED, bool GROUPED, bool DX>
 __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t) {
+    static_assert(!(FUSED && DX), "the fused kernel quantizes its staged chunks");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -166,9 +206,10 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
     const int nb = (n + U - 1) / U;
     const int kg = lane & 7, rg = lane >> 3;
 
-    // LDS: per-wave activation regions of RUN tiles, then the row partials.
+    // LDS: per-wave activation regions of RUN tiles (not with DX), then the
+    // row partials.
     uint8_t *xl = smem + wv * (a.RUN * kTileK);
-    int *red = reinterpret_cast<int *>(smem + a.WK * a.RUN * kTileK);   // WK*32 ints
+    int *red = reinterpret_cast<int *>(smem + (DX ? 0 : a.WK * a.RUN * kTileK));   // WK*32 ints
 
     const v4u *wt =
         reinterpret_cast<const v4u *>(pj.wp + int64_t(pj.s) * a.KT * kTileWords) + lane;
@@ -210,7 +251,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
                 am[i][1] = p[1];
             }
         }
-    } else {
+    } else if constexpr (!DX) {
 #pragma unroll
         for (int j = 0; j < kXChunks; ++j) {
             const int c = lane + 64 * j;
@@ -219,7 +260,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
                 xr[j] = *reinterpret_cast<const v4u *>(a.x + kbase + 16 * c);
         }
     }
-    if (!FUSED && (a.K & 15) != 0) {
+    if (!FUSED && !DX && (a.K & 15) != 0) {
 #pragma unroll
         for (int j = 0; j < kXChunks; ++j) {
             const int c = lane + 64 * j;
@@ -237,8 +278,12 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
     // 2. Two batches of weight loads in flight (clamped to the run, so the
     //    count of outstanding loads is the same in every wave).
     v4u wa[U], wb[U];
+    v4u xva[DX ? U : 1], xvb[DX ? U : 1];
+    const int xchunks = a.K >> 4;
     load_batch<U>(wt, w0, last, 0, wa);
+    if constexpr (DX) load_x<U>(a.x, w0, last, 0, kg, xchunks, xva);
     load_batch<U>(wt, w0, last, 1, wb);
+    if constexpr (DX) load_x<U>(a.x, w0, last, 1, kg, xchunks, xvb);
 
     // 2b. Fused: the row maximum (chunks beyond the first share and the
     //     values past the last whole chunk after the weight loads), combined
@@ -286,25 +331,45 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
 
     // 3. Stage the run's activations into the wave's LDS region and sum them.
     int sx = 0;
+    if constexpr (!DX) {
 #pragma unroll
-    for (int j = 0; j < kXChunks; ++j) {
-        const int c = lane + 64 * j;
-        if (c < nchunk) *reinterpret_cast<v4u *>(xl + 16 * c) = xr[j];
-        sx = dot4(xr[j][0], 0x01010101u, sx);
-        sx = dot4(xr[j][1], 0x01010101u, sx);
-        sx = dot4(xr[j][2], 0x01010101u, sx);
-        sx = dot4(xr[j][3], 0x01010101u, sx);
+        for (int j = 0; j < kXChunks; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nchunk) *reinterpret_cast<v4u *>(xl + 16 * c) = xr[j];
+            sx = dot4(xr[j][0], 0x01010101u, sx);
+            sx = dot4(xr[j][1], 0x01010101u, sx);
+            sx = dot4(xr[j][2], 0x01010101u, sx);
+            sx = dot4(xr[j][3], 0x01010101u, sx);
+        }
+        sx = sum8(sx);
+        sx += __shfl_xor(sx, 8);
+        sx += __shfl_xor(sx, 16);
+        sx += __shfl_xor(sx, 32);
     }
-    sx = sum8(sx);
-    sx += __shfl_xor(sx, 8);
-    sx += __shfl_xor(sx, 16);
-    sx += __shfl_xor(sx, 32);
 
     // 4. Stream the run: multiply one batch while the next is in flight.
     Acc acc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc.a1[q] = acc.a4[q] = acc.a16[q] = 0;
-    if (n > 0) {
+    if constexpr (DX) {
+        // Each lane sums its own chunks (kg) of the run; the 8 lanes of a
+        // row group together hold every chunk once.
+        int sxl = 0;
+        if (n > 0) {
+            int b = 0;
+            for (; b + 2 < nb; b += 2) {
+                mac_batch_dx<U>(wa, xva, w0, n, b, kg, a.K, acc, sxl);
+                load_batch<U>(wt, w0, last, b + 2, wa);
+                load_x<U>(a.x, w0, last, b + 2, kg, xchunks, xva);
+                mac_batch_dx<U>(wb, xvb, w0, n, b + 1, kg, a.K, acc, sxl);
+                load_batch<U>(wt, w0, last, b + 3, wb);
+                load_x<U>(a.x, w0, last, b + 3, kg, xchunks, xvb);
+            }
+            mac_batch_dx<U>(wa, xva, w0, n, b, kg, a.K, acc, sxl);
+            if (b + 1 < nb) mac_batch_dx<U>(wb, xvb, w0, n, b + 1, kg, a.K, acc, sxl);
+        }
+        sx = sum8(sxl);
+    } else if (n > 0) {
         int b = 0;
         for (; b + 2 < nb; b += 2) {
             mac_batch<U>(wa, xl, w0, w0, n, b, kg, acc);
@@ -353,14 +418,14 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
         store_proj(pj, sa, row, v);
 }
 
-template <int U, bool FUSED>
+template <int U, bool FUSED, bool DX = false>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvLaunch a) {
-    gemv_body<U, FUSED, false>(a, GemvGroups{});
+    gemv_body<U, FUSED, false, DX>(a, GemvGroups{});
 }
 
-template <int U, bool FUSED>
+template <int U, bool FUSED, bool DX = false>
 __global__ __launch_bounds__(1024) void gemv_grouped_kernel(GemvLaunch a, GemvGroups t) {
-    gemv_body<U, FUSED, true>(a, t);
+    gemv_body<U, FUSED, true, DX>(a, t);
 }
 
 
@@ -585,6 +650,23 @@ size_t gemv_lds_bytes(const GemvLaunch &a) {
     return size_t(a.WK) * a.RUN * kTileK + size_t(a.WK) * kTileRows * 4 + 16 * 4;
 }
 
+// Direct activation loads (no LDS staging) for the plain kernel when the grid
+// has at most 5 waves per CU, K is a multiple of 16 and the load batch is at
+// most 4 tiles.  Measured on MI355X (cold, interleaved runs): 0.02-0.07 us
+// less on each of the six sweep shapes of 640 to 1200 waves, but 0.09 us more
+// at 13824 x 2560 (1728 waves), 0.33 us more at 20480 x 3200 (2560) and
+// 1.15 us more at 5120 x 27648 (5760), where the extra 64-lane load
+// instruction per tile costs more than the staging it saves.
+// The chunks also take 2U more registers per lane, which a batch of 8 would
+// push past the budget of 16-wave workgroups.
+static bool gemv_direct_x(const GemvLaunch &a) {
+    return a.DXOK && a.xb == nullptr && (a.K & 15) == 0 && a.unroll <= 4;
+}
+
+static size_t gemv_launch_lds_bytes(const GemvLaunch &a) {
+    return gemv_direct_x(a) ? size_t(a.WK) * kTileRows * 4 : gemv_lds_bytes(a);
+}
+
 hipError_t launch_gemv(const GemvLaunch &la, hipStream_t stream) {
     GemvLaunch a = la;
     a.KQ = a.KT / a.SG;
@@ -596,17 +678,24 @@ hipError_t launch_gemv(const GemvLaunch &la, hipStream_t stream) {
     void *args[] = {&a};
     const void *fn;
     const bool fused = a.xb != nullptr;
+    const bool dx = gemv_direct_x(a);
     switch (a.unroll * 2 + (fused ? 1 : 0)) {
-    case 4: fn = reinterpret_cast<const void *>(&gemv_kernel<2, false>); break;
+    case 4:
+        fn = dx ? reinterpret_cast<const void *>(&gemv_kernel<2, false, true>)
+                : reinterpret_cast<const void *>(&gemv_kernel<2, false>);
+        break;
     case 5: fn = reinterpret_cast<const void *>(&gemv_kernel<2, true>); break;
-    case 8: fn = reinterpret_cast<const void *>(&gemv_kernel<4, false>); break;
+    case 8:
+        fn = dx ? reinterpret_cast<const void *>(&gemv_kernel<4, false, true>)
+                : reinterpret_cast<const void *>(&gemv_kernel<4, false>);
+        break;
     case 9: fn = reinterpret_cast<const void *>(&gemv_kernel<4, true>); break;
     case 17: fn = reinterpret_cast<const void *>(&gemv_kernel<8, true>); break;
     default: fn = reinterpret_cast<const void *>(&gemv_kernel<8, false>); break;
     }
     // x: strip, y: k-range of the strip.
     return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
-                           args, gemv_lds_bytes(a), stream);
+                           args, gemv_launch_lds_bytes(a), stream);
 }
 
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream) {
@@ -625,16 +714,23 @@ hipError_t launch_gemv_grouped(const GemvLaunch &la, const GemvGroups &t, hipStr
     void *args[] = {&a, &tt};
     const void *fn;
     const bool fused = a.xb != nullptr;
+    const bool dx = gemv_direct_x(a);
     switch (a.unroll * 2 + (fused ? 1 : 0)) {
-    case 4: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<2, false>); break;
+    case 4:
+        fn = dx ? reinterpret_cast<const void *>(&gemv_grouped_kernel<2, false, true>)
+                : reinterpret_cast<const void *>(&gemv_grouped_kernel<2, false>);
+        break;
     case 5: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<2, true>); break;
-    case 8: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<4, false>); break;
+    case 8:
+        fn = dx ? reinterpret_cast<const void *>(&gemv_grouped_kernel<4, false, true>)
+                : reinterpret_cast<const void *>(&gemv_grouped_kernel<4, false>);
+        break;
     case 9: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<4, true>); break;
     case 17: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<8, true>); break;
     default: fn = reinterpret_cast<const void *>(&gemv_grouped_kernel<8, false>); break;
     }
     return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
-                           args, gemv_lds_bytes(a), stream);
+                           args, gemv_launch_lds_bytes(a), stream);
 }
 
 }  // namespace w2a8

@@ -364,6 +364,7 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
     gemv_plan_full(a.NS, K, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll, &a.G);
+    a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
     hipError_t e = a.G > 0 ? launch_gemv_stream(a, static_cast<hipStream_t>(stream))
                            : launch_gemv(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
@@ -476,6 +477,7 @@ int grouped_launch(const GemvGroups &t, int64_t ns, int64_t K, const int8_t *x,
     a.G = 0;
     // One plan for the whole launch, as for a matrix of all the strips.
     gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+    a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
     hipError_t e = launch_gemv_grouped(a, t, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }

@@ -78,7 +78,7 @@ def algo_bytes(n, k):
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -18,7 +18,9 @@
 //    case) and sums them on the way (sum_k x, used below); LDS accesses of one
 //    wave are ordered, so this needs no workgroup barrier.  The activation
 //    loads are issued before the weight loads, so staging waits only for
-//    them.
+//    them.  On small grids (at most 5 waves per CU, K a multiple of 16) the
+//    plain kernel skips the staging instead: each lane loads the activation
+//    chunk of each tile together with the tile's weights (load_x).
 //  * Lane l = 8*rg + kg holds rows 4rg..4rg+3 at k = 16kg..16kg+15 of a tile
 //    and reads the matching 16 activation bytes from LDS (a broadcast read).
 //  * Decode without sign handling: code c = w + 1 in {0,1,2}.  For a word,

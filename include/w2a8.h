@@ -9,6 +9,8 @@
  *          §3.1 "BitLinear 层的三元权重逻辑".
  *   [CPU]  "微软BitNet：1-bit量化大模型CPU部署实践",
  *          §2.1 "1.58-bit量化原理", §2.2 "CPU优化设计", §6.3 "模型微调".
+ *   [DEPLOY] "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与
+ *          GPU 运行时优化", section "GPU 运行时优化与低延迟推理管道".
  *   [TEST] "如何编译 BitNet W2A8 CUDA 内核并用 test.py 运行 GEMV 加速测试？",
  *          sections "编译 W2A8 CUDA 内核", "运行 test.py 做 GEMV 基准测试",
  *          "如何判断结果", "限制与注意事项".
@@ -229,8 +231,9 @@ int w2a8_linear_gemv_grouped(int G, const void *const *w_packed, const int64_t *
 
 /* ------------------------------------------------------------------------
  * W2A4 variant: int4 activations.
- * "微软BitNet：1-bit量化大模型CPU部署实践" (its GPU runtime section) names an
- * "a4.8" extension with lower-precision activations, without a formula.
+ * "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与 GPU 运行时优化",
+ * section "GPU 运行时优化与低延迟推理管道", names an "a4.8" extension with
+ * lower-precision activations, without a formula.
  * Reading: the per-token absmax quantizer above with 7 levels per side, and
  * the same exact integer product and fp32 epilogue.
  *

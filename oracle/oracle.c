@@ -11,6 +11,8 @@
  *          §3.1 "BitLinear 层的三元权重逻辑".
  *   [CPU]  "微软BitNet：1-bit量化大模型CPU部署实践",
  *          §2.1 "1.58-bit量化原理", §2.2 "CPU优化设计", §6.3 "模型微调".
+ *   [DEPLOY] "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与
+ *          GPU 运行时优化", section "GPU 运行时优化与低延迟推理管道".
  *   [TEST] "如何编译 BitNet W2A8 CUDA 内核并用 test.py 运行 GEMV 加速测试？",
  *          sections "运行 test.py 做 GEMV 基准测试", "如何判断结果",
  *          "限制与注意事项".
@@ -247,8 +249,9 @@ int oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *w)
 /* ------------------------------------------------------------------------ */
 /* O5. Per-token absmax int4 activation quantization (W2A4 variant).
  *
- * "微软BitNet：1-bit量化大模型CPU部署实践" (its GPU runtime section) names an
- * "a4.8" extension with lower-precision activations and gives no formula.
+ * "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与 GPU 运行时优化",
+ * section "GPU 运行时优化与低延迟推理管道", names an "a4.8" extension with
+ * lower-precision activations and gives no formula.
  * Reading: the O3 quantizer with 4-bit signed codes, 7 levels each side:
  *   a = max_k |x[m][k]|
  *   inv = 7 / a                         (fp32 division)

@@ -99,14 +99,26 @@ def _t_mean_no_abs(W):
     return _tern_generic(W, lambda w: abs(w.astype(np.float64).mean()), np.rint)
 
 
+def _fp32_running_mean_abs(W):
+    # the mean of |W| accumulated in fp32, in row-major order
+    acc = np.float32(0.0)
+    for v in np.abs(np.asarray(W, np.float32)).ravel():
+        acc = np.float32(acc + v)
+    return acc / np.float32(W.size)
+
+
+def _t_fp32_sum(W):
+    return _tern_generic(W, _fp32_running_mean_abs, np.rint)
+
+
 @pytest.mark.parametrize("mut", [_t_no_clamp, _t_half_away, _t_trunc, _t_max_scale,
-                                 _t_mean_no_abs])
+                                 _t_mean_no_abs, _t_fp32_sum])
 def test_ternarize_mutants_fail(mut):
     assert _fails(ternarize_pins, mut)
 
 
 # --------------------------- O3 mutants ------------------------------------
-def _quant_generic(xb, amax_fn, round_fn, qmax=127, lo=-127, per_row=True):
+def _quant_generic(xb, amax_fn, round_fn, qmax=127, lo=-127, per_row=True, divide=False):
     xf = synth.bf16_bits_to_fp32(np.atleast_2d(xb)).astype(np.float32)
     M, K = xf.shape
     q = np.zeros((M, K), np.int8)
@@ -117,8 +129,10 @@ def _quant_generic(xb, amax_fn, round_fn, qmax=127, lo=-127, per_row=True):
         if a == 0:
             continue
         inv = np.float32(qmax) / a
-        q[m] = np.clip(round_fn(xf[m] * inv), lo, 127).astype(np.int8)
         sa[m] = a / np.float32(qmax)
+        # divide: x / sa (the rounded scale) instead of x * inv (its rounded reciprocal)
+        v = (xf[m] / sa[m]) if divide else (xf[m] * inv)
+        q[m] = np.clip(round_fn(v), lo, 127).astype(np.int8)
     return q, sa
 
 
@@ -143,8 +157,12 @@ def _q_half_away(xb):
                           lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5))
 
 
+def _q_divide_by_scale(xb):
+    return _quant_generic(xb, lambda r: np.abs(r).max(), np.rint, divide=True)
+
+
 @pytest.mark.parametrize("mut", [_q_trunc, _q_no_abs, _q_per_tensor, _q_scale_128,
-                                 _q_half_away])
+                                 _q_half_away, _q_divide_by_scale])
 def test_quant_mutants_fail(mut):
     assert _fails(quant_pins, mut)
 

@@ -3,9 +3,9 @@
 //
 // What it computes: the integer product of "如何编译 BitNet W2A8 CUDA 内核并用
 // test.py 运行 GEMV 加速测试？" ("如何判断结果") with the 4-bit activations
-// that "微软BitNet：1-bit量化大模型CPU部署实践" names as its "a4.8"
-// extension; the scale epilogue of "Windows 上跑通 BitNet b1.58：…部署实录"
-// §3.1.
+// that "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与 GPU 运行时优化",
+// section "GPU 运行时优化与低延迟推理管道", names as its "a4.8" extension;
+// the scale epilogue of "Windows 上跑通 BitNet b1.58：…部署实录" §3.1.
 //
 // Same work split, loads, staging, reduction and split-k combine as the
 // int8 workgroup kernel (gemv.hip); what changes:

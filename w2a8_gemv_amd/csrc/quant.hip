@@ -11,9 +11,10 @@
 // One 256-thread workgroup per row: a vectorised max pass, a block max, then
 // a quantize pass that re-reads the row from L2.
 //
-// The int4 variant ("a4.8" activations of "微软BitNet：1-bit量化大模型CPU
-//部署实践", named there without a formula) takes the same steps with 7 in
-// place of 127 and writes the A4I layout (a4.h).
+// The int4 variant (the "a4.8" activations that
+// "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与 GPU 运行时优化",
+// section "GPU 运行时优化与低延迟推理管道", names without a formula) takes the
+// same steps with 7 in place of 127 and writes the A4I layout (a4.h).
 #include "a4.h"
 #include "common.h"
 #include "device.h"

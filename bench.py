@@ -93,6 +93,9 @@ def parse_args():
     ap.add_argument("--steps-per-graph", type=int, default=16,
                     help="consecutive steps captured in one hipGraph (default 16, one "
                          "rotation of the weight copies)")
+    ap.add_argument("--bf16-context", action="store_true",
+                    help="also time the pages' bf16 torch.matmul comparison on the sweep "
+                         "shapes (context only, off by default)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -130,8 +133,7 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
     wf, write = load(write_csv)
     shapes = []
     for n, k in synth.SWEEP_SHAPES:
-        wk, sg, _, g = w2a8.gemv_plan(n, k, cus)
-        assert g == 0, "traffic summary expects the workgroup kernel"
+        wk, sg, _ = w2a8.gemv_plan(n, k, cus)
         grid = (-(-n // 32)) * sg * 64 * wk
         f = sum(fetch[grid]) / len(fetch[grid]) * ff
         w = sum(write[grid]) / len(write[grid]) * wf
@@ -920,7 +922,7 @@ def main():
         out["detail"]["linear_13824x2560"] = linear_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["grouped_decode"] = grouped_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["w2a4"] = a4_extras(torch, w2a8, synth, lib, stream)
-        if per:
+        if per and args.bf16_context:
             out["detail"]["bf16_matmul_context"] = bf16_context(torch, synth, stream, per)
 
     if args.calibrate_copy:

@@ -37,9 +37,13 @@
  * - Layouts: x is [M][K] row-major int8, y is [M][N] row-major.  N, K, M are
  *   element counts (>= 1).  Device pointers to x, y and packed weights must
  *   be 16-byte aligned (W2A8_ERR_ALIGN), scale pointers 4-byte aligned.
- * - Thread safety: the library holds no mutable state besides a per-device
- *   property cache; calls from several host threads are safe.  Two calls in
- *   flight at once must not share a workspace.
+ * - Thread safety: every entry point may be called from several host
+ *   threads at once.  The library's mutable state is a per-device property
+ *   cache and the measurement knobs of w2a8_tuning.h; both are guarded by a
+ *   lock (the batched-product kernel choice is one atomic word), and each
+ *   call plans its launch from one consistent copy of the knobs, taken when
+ *   the call starts.  Two calls in flight at once must not share a
+ *   workspace.
  */
 #ifndef W2A8_H
 #define W2A8_H
@@ -105,7 +109,9 @@ int64_t w2a8_packed_bytes(int64_t N, int64_t K);
 /* Device workspace bytes that w2a8_gemv / w2a8_gemm need for (M, N, K),
  * or -1 if out of range.  For M = 1 it holds one 64-bit word per row, padded
  * to 32 rows (the tile count and partial sum of a row whose k-range is split
- * over several waves); for 2 <= M <= 8, the larger of one such word per
+ * over several workgroups), and is 0 when no launch plan splits a k-range of
+ * that K (with the default knobs: K <= 47*128 = 6016), whatever the device;
+ * the M = 1 entry points then accept a NULL workspace.  For 2 <= M <= 8, the larger of one such word per
  * (row, padded output) and the split-K space below; for M > 8, int32 partial
  * sums and arrival counters of split-K output blocks (0 bytes when M*N is
  * too large for split-K, which is then not used).  The caller allocates it,
@@ -168,7 +174,8 @@ int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q,
  * fp32 [N], or NULL; at least one of y_i32 / y_f32 must be given.  s_a:
  * device, one float (required when y_f32 is given; may be NULL otherwise).
  * s_w: the per-tensor weight scale, by value.  workspace: device, at least
- * w2a8_workspace_bytes(1, N, K) bytes, zeroed before first use (see above).
+ * w2a8_workspace_bytes(1, N, K) bytes, zeroed before first use (see above);
+ * it may be NULL (and ws_bytes anything) when that size is 0.
  * Unlike the reference kernel, which computes only a fixed list of shapes
  * ([TEST] "限制与注意事项"), every N, K within the limits is computed. */
 int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K,
@@ -211,7 +218,7 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
  * (s_a required when any y_f32 entry is given).  The padded rows
  * (sum_g N[g] rounded up to 32 each) must not exceed 2^30.  workspace:
  * device, at least sum_g w2a8_workspace_bytes(1, N[g], K) bytes, zeroed
- * before first use.  Errors: W2A8_ERR_SHAPE for G or an N[g] out of range,
+ * before first use (NULL when that sum is 0).  Errors: W2A8_ERR_SHAPE for G or an N[g] out of range,
  * otherwise as w2a8_gemv. */
 int w2a8_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int64_t K,
                       const int8_t *x, const float *s_a, const float *s_w,

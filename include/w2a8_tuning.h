@@ -2,8 +2,10 @@
  * w2a8_tuning.h — launch-shape knobs of libw2a8.so, for measurement sweeps.
  *
  * Not needed for normal use: the defaults are the measured best on MI355X.
- * The knobs are process-wide (not per device) and are read when a call is
- * made; change them only while no other host thread is calling the library.
+ * The knobs are process-wide (not per device).  Setting them is thread-safe:
+ * each device call takes one consistent copy of the knobs when it starts, so
+ * a call running concurrently with a change uses either all old or all new
+ * values (and every plan computes the same result).
  */
 #ifndef W2A8_TUNING_H
 #define W2A8_TUNING_H
@@ -28,13 +30,6 @@ extern "C" {
 int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_tiles,
                    int split_min_tiles);
 
-/* Streaming GEMV for large matrices: used when the matrix has at least
- * `min_tiles` 1 KiB tiles (0: never, the default) and 16 <= K <= 32768 (all
- * activations fit in LDS).  The grid is CUs * `waves_per_cu` (1..64) long-lived waves, each
- * streaming an equal contiguous share of the tiles with two load batches of
- * `unroll` (2, 4 or 8) tiles in flight.  Returns W2A8_OK or W2A8_ERR_VALUE. */
-int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
-
 /* Batched product kernel (w2a8_gemm): 0 = automatic (default), 1 = the
  * pipelined MFMA kernel whenever K is a multiple of 16 (its configuration
  * still chosen by shape, including the wave-group k-split for small output
@@ -49,13 +44,11 @@ int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll);
 int w2a8_tune_gemm(int kernel);
 
 /* The plan w2a8_gemv would use for (N, K) on a device with `cus` compute
- * units under the current knobs.  Streaming kernel: *stream_waves = grid
- * waves, *unroll = its batch, the other outputs 0.  Otherwise *stream_waves
- * = 0 and waves per workgroup, workgroups per strip and load batch of the
- * workgroup-split kernel.  Returns W2A8_OK, W2A8_ERR_NULL or
- * W2A8_ERR_SHAPE. */
+ * units under the current knobs: waves per workgroup, workgroups per 32-row
+ * strip (more than 1 only when w2a8_workspace_bytes(1, N, K) > 0) and load
+ * batch.  Returns W2A8_OK, W2A8_ERR_NULL or W2A8_ERR_SHAPE. */
 int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
-                   int *unroll, int *stream_waves);
+                   int *unroll);
 
 #ifdef __cplusplus
 }

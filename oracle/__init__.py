@@ -7,6 +7,8 @@ package never imports it.
 
 Functions (parity status in ``oracle.c``):
   gemm_i32(x, w)                 O1  integer product, exact
+  gemm_i32_threads(x, w, t)      O1  the same C function on t host threads, each
+                                     over its own block of weight rows (same result)
   ternarize_absmean(W)           O2  absmean ternarization -> (wq, sw)
   quant_act(x_bf16_bits)         O3  per-token absmax int8 quantization
   epilogue(acc, sa, sw)          O4  fp32 scale epilogue
@@ -80,6 +82,34 @@ def gemm_i32(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     y = np.empty((M, N), dtype=np.int32)
     if _load().oracle_gemm_i32(_ptr(x2), _ptr(w2), M, N, K, _ptr(y)) != 0:
         raise OverflowError("int32 overflow in oracle product")
+    return y[0] if squeeze else y
+
+
+def gemm_i32_threads(x: np.ndarray, w: np.ndarray, threads: int) -> np.ndarray:
+    """gemm_i32 with the output columns (rows of w) split into `threads`
+    contiguous blocks, each computed by the same C function on its own host
+    thread (ctypes releases the GIL during the call).  Every output element is
+    the same int64 sum as in gemm_i32, so the result is identical."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    squeeze = x.ndim == 1
+    x2 = np.ascontiguousarray(np.atleast_2d(x), dtype=np.int8)
+    w2 = np.ascontiguousarray(w, dtype=np.int8)
+    M, K = x2.shape
+    N, K2 = w2.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    threads = max(1, min(int(threads), N))
+    bounds = [N * i // threads for i in range(threads + 1)]
+    y = np.empty((M, N), dtype=np.int32)
+
+    def block(i):
+        n0, n1 = bounds[i], bounds[i + 1]
+        if n1 > n0:
+            y[:, n0:n1] = gemm_i32(x2, w2[n0:n1])
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(block, range(threads)))
     return y[0] if squeeze else y
 
 

@@ -21,7 +21,8 @@ import w2a8_gemv_amd as w2a8
 
 from conftest import ROOT
 
-ST = {"OK": 0, "NULL": 1, "SHAPE": 2, "ALIGN": 3, "VALUE": 4, "BUFSIZE": 5}
+ST = {"OK": 0, "NULL": 1, "SHAPE": 2, "ALIGN": 3, "VALUE": 4, "BUFSIZE": 5, "NODEVICE": 6,
+      "ARCH": 7}
 F = ctypes.c_float
 FAKE = 0x10000          # 16-byte aligned stand-in, never dereferenced
 FAKE_ODD = 0x10004      # 4-byte aligned only
@@ -52,7 +53,7 @@ def test_library_exports_every_declared_symbol():
     expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
-                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemv_stream", "w2a8_tune_gemm",
+                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemm",
                 "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped",
                 "w2a4_act_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv"}
     assert expected.issubset(set(names)), set(names) ^ expected
@@ -82,7 +83,7 @@ def test_size_queries_reject_bad_shapes():
     assert L.w2a8_packed_bytes(5, 0) == -1
     assert L.w2a8_packed_bytes(5, 1048448 + 1) == -1
     assert L.w2a8_workspace_bytes(0, 5, 5) == -1
-    assert L.w2a8_workspace_bytes(1, 5, 5) > 0
+    assert L.w2a8_workspace_bytes(1, 5, 5) == 0 and L.w2a8_workspace_bytes(1, 5, 27648) > 0
 
 
 # ---------------------------------------------------------------------------
@@ -169,8 +170,12 @@ def test_ternarize_worked_examples_and_zero():
 # ---------------------------------------------------------------------------
 # argument validation of the device entry points (rejected before any HIP call)
 # ---------------------------------------------------------------------------
+# K of 64 tiles: the plan may split the k-range, so the workspace is required
+KS = 8192
+
+
 def _gemv(**kw):
-    a = dict(wp=FAKE, x=FAKE, N=64, K=256, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
+    a = dict(wp=FAKE, x=FAKE, N=64, K=KS, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
              wsb=1 << 20)
     a.update(kw)
     return w2a8.lib().w2a8_gemv(a["wp"], a["x"], a["N"], a["K"], a["y"], a["sa"], F(a["sw"]),
@@ -192,7 +197,7 @@ def test_gemv_validation():
     assert _gemv(y=FAKE_ODD) == ST["ALIGN"]
     assert _gemv(yf=FAKE_ODD) == ST["ALIGN"]
     assert _gemv(sa=FAKE + 2) == ST["ALIGN"]
-    assert _gemv(wsb=w2a8.workspace_bytes(1, 64, 256) - 1) == ST["BUFSIZE"]
+    assert _gemv(wsb=w2a8.workspace_bytes(1, 64, KS) - 1) == ST["BUFSIZE"]
 
 
 def _gemm(**kw):
@@ -218,7 +223,7 @@ def test_gemm_validation():
 
 
 def _linear(**kw):
-    a = dict(wp=FAKE, xb=FAKE, N=64, K=256, sw=1.0, yf=FAKE, y=FAKE, ws=FAKE, wsb=1 << 20)
+    a = dict(wp=FAKE, xb=FAKE, N=64, K=KS, sw=1.0, yf=FAKE, y=FAKE, ws=FAKE, wsb=1 << 20)
     a.update(kw)
     return w2a8.lib().w2a8_linear_gemv(a["wp"], a["xb"], a["N"], a["K"], F(a["sw"]), a["yf"],
                                        a["y"], a["ws"], a["wsb"], None)
@@ -234,7 +239,7 @@ def test_linear_gemv_validation():
     assert _linear(xb=FAKE + 2) == ST["ALIGN"]
     assert _linear(yf=FAKE_ODD) == ST["ALIGN"]
     assert _linear(y=FAKE_ODD) == ST["ALIGN"]
-    assert _linear(wsb=w2a8.workspace_bytes(1, 64, 256) - 1) == ST["BUFSIZE"]
+    assert _linear(wsb=w2a8.workspace_bytes(1, 64, KS) - 1) == ST["BUFSIZE"]
 
 
 def _arr(ctype, vals):
@@ -244,7 +249,7 @@ def _arr(ctype, vals):
 def _grouped(linear=False, **kw):
     Ns = kw.pop("Ns", [64, 33, 100])
     G = len(Ns)
-    a = dict(G=G, wp=[FAKE] * G, x=FAKE, K=256, sa=FAKE, sw=[1.0] * G, y=[FAKE] * G,
+    a = dict(G=G, wp=[FAKE] * G, x=FAKE, K=KS, sa=FAKE, sw=[1.0] * G, y=[FAKE] * G,
              yf=[FAKE] * G, ws=FAKE, wsb=1 << 20)
     a.update(kw)
     L = w2a8.lib()
@@ -276,8 +281,9 @@ def test_grouped_validation(linear):
     assert g(yf=[FAKE, FAKE, FAKE_ODD]) == ST["ALIGN"]
     assert g(y=[FAKE_ODD, FAKE, FAKE]) == ST["ALIGN"]
     assert g(x=FAKE + 2) == ST["ALIGN"]
-    need = sum(w2a8.workspace_bytes(1, n, 256) for n in (64, 33, 100))
+    need = sum(w2a8.workspace_bytes(1, n, KS) for n in (64, 33, 100))
     assert g(wsb=need - 1) == ST["BUFSIZE"]
+    assert g(K=256, ws=None, wsb=0) not in (ST["NULL"], ST["ALIGN"], ST["BUFSIZE"])
     if linear:
         assert g(yf=[FAKE, None, FAKE]) == ST["NULL"]          # every fp32 output required
     else:
@@ -324,7 +330,7 @@ def test_w2a4_validation():
     assert L.quant_act_int4(FAKE, 1, 16, FAKE + 8, FAKE, None) == ST["ALIGN"]
 
     def g(**kw):
-        a = dict(wp=FAKE, x=FAKE, N=64, K=256, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
+        a = dict(wp=FAKE, x=FAKE, N=64, K=KS, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE, ws=FAKE,
                  wsb=1 << 20)
         a.update(kw)
         return L.w2a4_gemv(a["wp"], a["x"], a["N"], a["K"], a["y"], a["sa"], F(a["sw"]),
@@ -338,7 +344,7 @@ def test_w2a4_validation():
     assert g(K=1048448 + 1) == ST["SHAPE"]
     assert g(x=FAKE + 8) == ST["ALIGN"]
     assert g(yf=FAKE_ODD) == ST["ALIGN"]
-    assert g(wsb=w2a8.workspace_bytes(1, 64, 256) - 1) == ST["BUFSIZE"]
+    assert g(wsb=w2a8.workspace_bytes(1, 64, KS) - 1) == ST["BUFSIZE"]
 
 
 def test_quant_validation():
@@ -354,12 +360,93 @@ def test_quant_validation():
 
 
 def test_workspace_formula():
-    # GEMV: one 8-byte combining word per padded row, rounded up to 256 bytes
+    # GEMV: one 8-byte combining word per padded row, rounded up to 256 bytes,
+    # when a plan may split the k-range (K >= 48 tiles with the default knobs)
     for N in (1, 31, 32, 2560, 55296):
         Np = -(-N // 32) * 32
-        assert w2a8.workspace_bytes(1, N, 1000) == -(-(8 * Np) // 256) * 256
+        assert w2a8.workspace_bytes(1, N, 6017) == -(-(8 * Np) // 256) * 256
+        assert w2a8.workspace_bytes(1, N, 27648) == -(-(8 * Np) // 256) * 256
+        # no plan splits K <= 47 tiles: no workspace
+        for K in (1, 1000, 2560, 6016):
+            assert w2a8.workspace_bytes(1, N, K) == 0
     # large batched outputs never split K: no workspace needed
     assert w2a8.workspace_bytes(512, 13824, 2560) == 0
+
+
+def test_workspace_rule_matches_the_plans():
+    # w2a8_workspace_bytes(1, N, K) is 0 exactly when no device's plan splits
+    # a strip, under the default knobs and others
+    pols = [w2a8.DEFAULT_GEMV_POLICY, (4, 4, 4, 3, 1), (1, 32, 8, 256, 10 ** 6), (8, 6, 8, 20, 100)]
+    try:
+        for pol in pols:
+            w2a8.tune_gemv(*pol)
+            for N in (1, 2560, 55296):
+                for K in (1, 128, 385, 2560, 6016, 6017, 27648, 40000):
+                    ws = w2a8.workspace_bytes(1, N, K)
+                    splits = [w2a8.gemv_plan(N, K, cus)[1] > 1 for cus in (1, 80, 256, 304)]
+                    if ws == 0:
+                        assert not any(splits), (pol, N, K)
+                    kt = -(-K // 128)
+                    assert (ws > 0) == (kt >= pol[4] or kt > pol[3]), (pol, N, K)
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+def test_gemv_accepts_null_workspace_only_when_unsplit():
+    # Validation order: a NULL workspace is an error only when the k-range
+    # may be split; otherwise validation passes on to the device query
+    # (NODEVICE on this host without a GPU).
+    L = w2a8.lib()
+    nodev = (ST["NODEVICE"], ST["ARCH"], ST["OK"])
+    assert L.w2a8_gemv(FAKE, FAKE, 64, 2560, FAKE, None, 1.0, None, None, 0, None) in nodev
+    assert L.w2a8_gemv(FAKE, FAKE, 64, 27648, FAKE, None, 1.0, None, None, 0, None) == ST["NULL"]
+    assert L.w2a8_linear_gemv(FAKE, FAKE, 64, 2560, 1.0, FAKE, None, None, 0, None) in nodev
+    assert L.w2a8_linear_gemv(FAKE, FAKE, 64, 27648, 1.0, FAKE, None, None, 0, None) == ST["NULL"]
+    assert L.w2a4_gemv(FAKE, FAKE, 64, 2560, FAKE, None, 1.0, None, None, 0, None) in nodev
+    assert L.w2a4_gemv(FAKE, FAKE, 64, 27648, FAKE, None, 1.0, None, None, 0, None) == ST["NULL"]
+
+
+def test_tuning_knobs_are_thread_safe():
+    # Knob changes from one thread while others read plans and sizes: every
+    # plan read must be one of the two policies' plans, never a mix.
+    import threading
+    a, b = w2a8.DEFAULT_GEMV_POLICY, (1, 32, 2, 3, 1)
+    shapes = [(2560, 2560), (5120, 27648), (55296, 5120)]
+    plans = {}
+    try:
+        for pol in (a, b):
+            w2a8.tune_gemv(*pol)
+            for nk in shapes:
+                plans.setdefault(nk, set()).add(tuple(w2a8.gemv_plan(*nk, 256)))
+        stop = threading.Event()
+        bad = []
+
+        def flip():
+            i = 0
+            while not stop.is_set():
+                w2a8.tune_gemv(*(a if i % 2 else b))
+                w2a8.tune_gemm(i % 4)
+                i += 1
+
+        def read():
+            for _ in range(3000):
+                for nk in shapes:
+                    p = tuple(w2a8.gemv_plan(*nk, 256))
+                    if p not in plans[nk]:
+                        bad.append((nk, p))
+        t = threading.Thread(target=flip)
+        t.start()
+        rs = [threading.Thread(target=read) for _ in range(3)]
+        for r in rs:
+            r.start()
+        for r in rs:
+            r.join()
+        stop.set()
+        t.join()
+        assert not bad, bad[:5]
+    finally:
+        w2a8.tune_gemv(*a)
+        w2a8.tune_gemm(0)
 
 
 def test_tuning_knobs_validate():
@@ -369,30 +456,6 @@ def test_tuning_knobs_validate():
             w2a8.tune_gemv(*bad)
     with pytest.raises(w2a8.W2A8Error):
         w2a8.gemv_plan(0, 2560, 256)
-    for bad in [(-1, 4, 4), (1, 0, 4), (1, 65, 4), (1, 4, 3)]:
-        with pytest.raises(w2a8.W2A8Error):
-            w2a8.tune_gemv_stream(*bad)
-
-
-def test_gemv_stream_selection():
-    """The streaming kernel is off by default; when enabled it is chosen only
-    for large matrices whose K fits in LDS."""
-    try:
-        w2a8.tune_gemv_stream(*w2a8.DEFAULT_GEMV_STREAM_POLICY)
-        for N, K in [(55296, 5120), (5120, 27648), (2560, 2560), (1, 16)]:
-            assert w2a8.gemv_plan(N, K, 256)[3] == 0
-        w2a8.tune_gemv_stream(16384, 4, 4)
-        assert w2a8.gemv_plan(55296, 5120, 256)[3] > 0
-        assert w2a8.gemv_plan(5120, 27648, 256)[3] > 0
-        assert w2a8.gemv_plan(2560, 2560, 256)[3] == 0
-        assert w2a8.gemv_plan(4096, 40000, 256)[3] == 0     # K too long for the LDS stage
-        w2a8.tune_gemv_stream(0, 4, 4)
-        assert w2a8.gemv_plan(55296, 5120, 256)[3] == 0
-        w2a8.tune_gemv_stream(1, 4, 4)
-        assert w2a8.gemv_plan(1, 16, 256)[3] == 1
-        assert w2a8.gemv_plan(1, 15, 256)[3] == 0          # K below one 16-byte chunk
-    finally:
-        w2a8.tune_gemv_stream(*w2a8.DEFAULT_GEMV_STREAM_POLICY)
 
 
 def test_gemv_plan_properties():
@@ -405,11 +468,7 @@ def test_gemv_plan_properties():
             for N in (1, 31, 2560, 55296):
                 for K in (1, 127, 128, 2560, 27648, 100000, 1048448):
                     for cus in (1, 80, 256):
-                        wk, sg, u, g = w2a8.gemv_plan(N, K, cus)
-                        if g:   # streaming plan
-                            assert 1 <= g <= max(1, -(-N // 32) * -(-K // 128))
-                            assert 16 <= K and -(-K // 128) * 8 <= 8 * 256   # K staged whole in LDS
-                            continue
+                        wk, sg, u = w2a8.gemv_plan(N, K, cus)
                         kt = -(-K // 128)
                         ktw = -(-kt // sg)
                         run = -(-ktw // wk)
@@ -439,9 +498,9 @@ def test_gemv_default_plans_of_the_measured_shapes():
             (5120, 27648): (3, 12, 4), (55296, 5120): (8, 1, 4), (2560, 27648): (3, 12, 4),
             (8192, 8192): (1, 11, 4)}
     for (N, K), plan in want.items():
-        assert tuple(w2a8.gemv_plan(N, K, 256)) == plan + (0,), (N, K)
+        assert tuple(w2a8.gemv_plan(N, K, 256)) == plan, (N, K)
     # The same 80-strip matrix on a 64-CU device has more strips than CUs.
-    assert tuple(w2a8.gemv_plan(2560, 2560, 64)) == (4, 1, 4, 0)
+    assert tuple(w2a8.gemv_plan(2560, 2560, 64)) == (4, 1, 4)
 
 
 def test_binding_refuses_host_tensors_for_device_calls():

@@ -6,6 +6,8 @@ section "如何判断结果"); here the comparison is with the CPU oracle, on th
 same seeded arrays, at small ragged sizes, at every full workload shape in the
 launch configuration the benchmark times, and under forced k-splits.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -25,7 +27,6 @@ DEFAULT_POLICY = w2a8.DEFAULT_GEMV_POLICY
 def _restore_policy():
     yield
     w2a8.tune_gemv(*DEFAULT_POLICY)
-    w2a8.tune_gemv_stream(*w2a8.DEFAULT_GEMV_STREAM_POLICY)
 
 
 def _case(N, K, seed, sparse=False):
@@ -61,54 +62,18 @@ def test_gemv_forced_splits(policy, N, K):
     np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
 
 
-# Streaming kernel forced onto small matrices: (waves per CU, batch).  Grids
-# from a few waves (each streaming several whole strips) to one wave per tile
-# (every strip split over many waves), ragged N and K.
-STREAM = [(1, 2), (1, 8), (2, 4), (4, 4), (16, 4), (64, 2), (64, 8)]
-
-
-@pytest.mark.parametrize("sp", STREAM)
-@pytest.mark.parametrize("N,K", [(33, 1000), (64, 2560), (200, 3200), (96, 27648), (1000, 130),
-                                 (257, 1000), (100, 300), (7, 21), (5, 16), (2560, 2560),
-                                 (31, 32768)])
-def test_gemv_stream_kernel(sp, N, K):
-    w2a8.tune_gemv_stream(1, *sp)
-    assert w2a8.gemv_plan(N, K, torch.cuda.get_device_properties(0).multi_processor_count)[3] > 0
-    x, w, wp, xd = _case(N, K, seed=3 + N + 7 * K)
-    np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
-
-
-def test_gemv_stream_kernel_declines_k_below_16():
-    """K < 16 (no whole 16-byte activation chunk) stays on the workgroup kernel."""
-    w2a8.tune_gemv_stream(1, 4, 4)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for N, K in [(7, 5), (300, 15), (1, 1)]:
-        assert w2a8.gemv_plan(N, K, cus)[3] == 0
-        x, w, wp, xd = _case(N, K, seed=N + K)
-        np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
-
-
-def test_gemv_stream_kernel_repeat_and_workspace_reset():
-    w2a8.tune_gemv_stream(1, 16, 4)     # every strip split over several waves
-    N, K = 2560, 6912
-    x, w, wp, xd = _case(N, K, seed=17)
-    ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
-    ref = oracle.gemm_i32(x, w)
-    for _ in range(4):
-        np.testing.assert_array_equal(gemv_dev(wp, xd, N, K, workspace=ws), ref)
-        assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
-
-
-def test_gemv_stream_kernel_fp32_epilogue():
-    w2a8.tune_gemv_stream(1, 8, 4)
-    N, K = 4000, 3000
-    x, w, wp, xd = _case(N, K, seed=23)
-    sa = np.array([0.031], np.float32)
-    sw = np.float32(0.0123)
-    yi, yf = gemv_dev(wp, xd, N, K, sa=to_dev(sa), sw=float(sw), want_f32=True)
-    acc = oracle.gemm_i32(x, w)
-    np.testing.assert_array_equal(yi, acc)
-    np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw))
+@pytest.mark.parametrize("N,K", [(33, 1000), (2560, 2560), (100, 6016)])
+def test_gemv_without_workspace_when_unsplit(N, K):
+    """No workspace is needed (nor passed) when no plan splits the k-range."""
+    assert w2a8.workspace_bytes(1, N, K) == 0
+    x, w, wp, xd = _case(N, K, seed=5 + N + K)
+    y = torch.empty(N, dtype=torch.int32, device=dev())
+    rc = w2a8.lib().w2a8_gemv(wp.data_ptr(), xd.data_ptr(), N, K, y.data_ptr(), None,
+                              ctypes.c_float(1.0), None, None, 0,
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), oracle.gemm_i32(x, w))
 
 
 @pytest.mark.parametrize("idx", range(len(synth.SWEEP_SHAPES)))

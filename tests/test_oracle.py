@@ -79,6 +79,17 @@ def test_gemm_pins():
     gemm_pins(oracle.gemm_i32)
 
 
+def test_gemm_threads_equals_gemm():
+    # the threaded caller splits the weight rows into blocks: same result for
+    # more threads than rows, ragged blocks and M > 1
+    rng = np.random.default_rng(99)
+    for M, N, K, t in [(1, 5, 33, 8), (3, 97, 130, 4), (7, 64, 300, 3), (2, 1, 9, 2)]:
+        x = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+        w = rng.integers(-1, 2, size=(N, K), dtype=np.int8)
+        np.testing.assert_array_equal(oracle.gemm_i32_threads(x, w, t), oracle.gemm_i32(x, w))
+    np.testing.assert_array_equal(oracle.gemm_i32_threads(x[0], w, 2), oracle.gemm_i32(x[0], w))
+
+
 def test_gemm_full_sweep_shape_vs_numpy():
     # one full-size workload shape at M = 1 against numpy's int64 matmul
     x, w = synth.gemv_case(2560, 2560, synth.SEED_SMALL)

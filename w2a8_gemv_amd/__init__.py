@@ -22,8 +22,8 @@ __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
-    "w2a8_linear_gemv", "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemv_stream", "tune_gemm",
-    "DEFAULT_GEMV_STREAM_POLICY", "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
+    "w2a8_linear_gemv", "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemm",
+    "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
     "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
 ]
 
@@ -90,9 +90,7 @@ def lib():
         L.w2a8_linear_gemv_grouped.restype = I32
         L.w2a8_tune_gemv.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv.restype = I32
-        L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
-        L.w2a8_tune_gemv_stream.argtypes = [I32, I32, I32]
-        L.w2a8_tune_gemv_stream.restype = I32
+        L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P]
         L.w2a8_tune_gemm.argtypes = [I32]
         L.w2a8_tune_gemm.restype = I32
         L.w2a8_gemv_plan.restype = I32
@@ -305,8 +303,9 @@ def w2a8_linear_gemv(w_packed, x_bf16, N, K, s_w, y_f32, y_i32=None, workspace=N
             raise ValueError("y_i32 must have N elements")
     ws = _ws(workspace_bytes(1, N, K), x_bf16.device, stream, workspace)
     _check(lib().w2a8_linear_gemv(_ptr(w_packed), _ptr(x_bf16), N, K, ctypes.c_float(s_w),
-                                  _ptr(y_f32), _ptr(y_i32), _ptr(ws), ws.numel(),
-                                  _stream_handle(stream)), "w2a8_linear_gemv")
+                                  _ptr(y_f32), _ptr(y_i32), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream_handle(stream)),
+           "w2a8_linear_gemv")
 
 
 # ---------------------------------------------------------------------------
@@ -425,7 +424,8 @@ def w2a8_gemv_grouped(w_packed, x, Ns, K, s_w, y_i32=None, y_f32=None, s_a=None,
     G, wp, n_arr, sw_arr, yi_arr, yf_arr, need = _grouped_args(w_packed, Ns, K, s_w, y_i32, y_f32)
     ws = _ws(need, x.device, stream, workspace)
     _check(lib().w2a8_gemv_grouped(G, wp, n_arr, K, _ptr(x), _ptr(s_a), sw_arr, yi_arr, yf_arr,
-                                   _ptr(ws), ws.numel(), _stream_handle(stream)),
+                                   _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream_handle(stream)),
            "w2a8_gemv_grouped")
 
 
@@ -440,7 +440,8 @@ def w2a8_linear_gemv_grouped(w_packed, x_bf16, Ns, K, s_w, y_f32, y_i32=None, wo
     G, wp, n_arr, sw_arr, yi_arr, yf_arr, need = _grouped_args(w_packed, Ns, K, s_w, y_i32, y_f32)
     ws = _ws(need, x_bf16.device, stream, workspace)
     _check(lib().w2a8_linear_gemv_grouped(G, wp, n_arr, K, _ptr(x_bf16), sw_arr, yf_arr, yi_arr,
-                                          _ptr(ws), ws.numel(), _stream_handle(stream)),
+                                          _ptr(ws), 0 if ws is None else ws.numel(),
+                                          _stream_handle(stream)),
            "w2a8_linear_gemv_grouped")
 
 
@@ -505,13 +506,6 @@ def tune_gemv(wg_per_cu: int, tiles_per_wave: int, unroll: int, krange_tiles: in
                                 split_min_tiles), "w2a8_tune_gemv")
 
 
-DEFAULT_GEMV_STREAM_POLICY = (0, 4, 4)
-
-
-def tune_gemv_stream(min_tiles: int, waves_per_cu: int, unroll: int):
-    _check(lib().w2a8_tune_gemv_stream(min_tiles, waves_per_cu, unroll), "w2a8_tune_gemv_stream")
-
-
 def tune_gemm(kernel: int):
     """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general,
     3 few-row whenever M <= 8."""
@@ -520,8 +514,8 @@ def tune_gemm(kernel: int):
 
 def gemv_plan(N: int, K: int, cus: int):
     """Launch plan of w2a8_gemv: (waves per workgroup, workgroups per strip,
-    load batch, streaming-grid waves); streaming plans are (0, 0, U, G)."""
-    wk, sg, u, g = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib().w2a8_gemv_plan(N, K, cus, ctypes.byref(wk), ctypes.byref(sg), ctypes.byref(u),
-                                ctypes.byref(g)), "w2a8_gemv_plan")
-    return wk.value, sg.value, u.value, g.value
+    load batch)."""
+    wk, sg, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().w2a8_gemv_plan(N, K, cus, ctypes.byref(wk), ctypes.byref(sg), ctypes.byref(u)),
+           "w2a8_gemv_plan")
+    return wk.value, sg.value, u.value

@@ -37,12 +37,17 @@ struct GemvPolicy {
     int unroll;           // largest load batch in tiles (two in flight): 2, 4 or 8
     int krange_tiles;     // at most this many k-tiles per workgroup
     int split_min_tiles;  // split a strip over workgroups only if KT >= this
-    // streaming kernel (large matrices)
-    int stream_min_tiles;     // use it when N*K/4096 tiles >= this (0: never)
-    int stream_waves_per_cu;  // grid of CUs * this long-lived waves
-    int stream_unroll;        // load batch in tiles (two in flight): 2, 4 or 8
 };
-GemvPolicy &gemv_policy();
+// A consistent copy of the current knobs (taken under a lock: every call
+// plans from one snapshot, whatever other host threads set meanwhile).
+GemvPolicy gemv_policy();
+void set_gemv_policy(const GemvPolicy &p);
+// True when a GEMV plan under `p` may split a strip of KT tiles over several
+// workgroups (and so needs the workspace).  Depends on K alone, not on the
+// device.
+inline bool gemv_may_split(int64_t KT, const GemvPolicy &p) {
+    return KT >= p.split_min_tiles || KT > p.krange_tiles;
+}
 
 // GEMV launch arguments (passed to the kernel by value).
 struct GemvLaunch {
@@ -60,8 +65,6 @@ struct GemvLaunch {
     int SG;       // workgroups (k-ranges) per row strip
     int RUN;      // longest run of tiles of one wave (<= 32)
     int unroll;
-    int G;        // streaming kernel: waves in the grid (0: workgroup-split kernel)
-    int TQ, TR;   // streaming kernel: NS*KT = TQ*G + TR (wave w starts at w*TQ + min(w, TR))
     int DXOK = 0; // plain kernel: at most 5 waves per CU in the grid, so activation chunks may
                   // be loaded directly with the weights (latency-bound grids)
     // Workgroup kernel, set by its launcher so that the kernel divides
@@ -126,26 +129,20 @@ __device__ __forceinline__ bool split_add(uint64_t *word, int tiles, int val, in
         kt, v);
 }
 
-// Launch plan for (N, K) on `cus` compute units under the current policy.
-void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll);
+// Launch plan for (N, K) on `cus` compute units under policy `p`.
+void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run,
+               int *unroll);
 size_t gemv_lds_bytes(const GemvLaunch &a);
-// Streaming kernel for large matrices (gemv_stream.hip).
-bool gemv_stream_fits(int64_t K);
-size_t gemv_stream_lds_bytes(const GemvLaunch &a);
-hipError_t launch_gemv_stream(const GemvLaunch &a, hipStream_t stream);
 // Few activation rows (2 <= M <= 8): plan with runs of at most 8 tiles, and
 // the kernel (gemv.hip).  Workspace: 8 bytes per (row, padded output) when
 // strips are split.
-void gemv_rows_plan(int64_t NS, int64_t KT, int64_t M, int cus, int *wk, int *sg, int *run,
-                    int *unroll);
+void gemv_rows_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int64_t M, int cus, int *wk,
+                    int *sg, int *run, int *unroll);
 hipError_t launch_gemv_rows(const GemvLaunch &a, hipStream_t stream);
 constexpr int64_t kRowsMaxM = 8;
 // Fused linear GEMV: quantize the bf16 row in every workgroup, then the
 // workgroup kernel with the fp32 epilogue (gemv.hip).
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream);
-// Full plan: G > 0 selects the streaming kernel (then wk = sg = run = 0).
-void gemv_plan_full(int64_t NS, int64_t K, int cus, int *wk, int *sg, int *run, int *unroll,
-                    int *g);
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
@@ -160,8 +157,10 @@ struct GemmShape {
 GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split);
 // Kernel choice knob (w2a8_tune_gemm): 0 automatic, 1 pipelined kernel
 // whenever K allows it, 2 general kernel always, 3 few-row GEMV-style kernel
-// whenever M <= 8.  Modes 1 and 2 never pick the few-row kernel.
-int &gemm_kernel_mode();
+// whenever M <= 8.  Modes 1 and 2 never pick the few-row kernel.  Read and
+// set atomically.
+int gemm_kernel_mode();
+void set_gemm_kernel_mode(int mode);
 
 // Split-K is only ever used when M * Np <= kGemmSplitMaxOut, which bounds the
 // workspace that w2a8_workspace_bytes reports.

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "common.h"
@@ -49,16 +50,23 @@ int current_device(DeviceInfo *out) {
     return g_dev_status[dev];
 }
 
-int &gemm_kernel_mode() {
-    static int mode = 0;
-    return mode;
+namespace {
+std::atomic<int> g_gemm_mode{0};
+std::mutex g_policy_mu;
+GemvPolicy g_policy = {4, 6, 8, 256, 48};
+}  // namespace
+
+int gemm_kernel_mode() { return g_gemm_mode.load(std::memory_order_relaxed); }
+void set_gemm_kernel_mode(int mode) { g_gemm_mode.store(mode, std::memory_order_relaxed); }
+
+GemvPolicy gemv_policy() {
+    std::lock_guard<std::mutex> lock(g_policy_mu);
+    return g_policy;
 }
 
-GemvPolicy &gemv_policy() {
-    // Streaming kernel off by default (stream_min_tiles 0): on gfx950 the
-    // workgroup kernel is as fast or faster on every measured shape.
-    static GemvPolicy p = {4, 6, 8, 256, 48, 0, 4, 4};
-    return p;
+void set_gemv_policy(const GemvPolicy &p) {
+    std::lock_guard<std::mutex> lock(g_policy_mu);
+    g_policy = p;
 }
 
 // Most workgroups a long strip is split into by default: more only for
@@ -84,10 +92,11 @@ constexpr int64_t kSplitWgs = 12;
 //    at 55296 x 5120, 1728 strips, halving the runs costs 2.8 us).
 //  * The load batch U (two in flight per wave) is the smallest of 2, 4, 8
 //    (at most `unroll`) whose two batches cover the run.
-void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int *unroll) {
-    const GemvPolicy &p = gemv_policy();
+void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run,
+               int *unroll) {
     const int64_t tpw = std::max(1, p.tiles_per_wave);
     int64_t SG = ceil_div(KT, std::max(1, p.krange_tiles));
+    // (SG > 1 only when gemv_may_split(KT, p): the workspace rule relies on it.)
     if (KT >= p.split_min_tiles) {
         SG = std::max(SG, std::min(ceil_div(KT, tpw), kSplitWgs));
         const int64_t want = ceil_div(int64_t(cus) * std::max(1, p.wg_per_cu), NS);
@@ -137,10 +146,10 @@ void gemv_plan(int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run, int 
 // activation chunk per lane per row) and at most 32/MR waves per workgroup
 // (LDS <= 36 KiB for the MR row regions); more workgroups per strip when
 // needed.
-void gemv_rows_plan(int64_t NS, int64_t KT, int64_t M, int cus, int *wk, int *sg, int *run,
-                    int *unroll) {
+void gemv_rows_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int64_t M, int cus, int *wk,
+                    int *sg, int *run, int *unroll) {
     int r = 0;
-    gemv_plan(NS, KT, cus, wk, sg, &r, unroll);
+    gemv_plan(p, NS, KT, cus, wk, sg, &r, unroll);
     const int64_t MR = M <= 2 ? 2 : M <= 4 ? 4 : 8;
     const int64_t wkmax = 32 / MR;
     int64_t SG = *sg, WK = *wk;
@@ -159,27 +168,6 @@ void gemv_rows_plan(int64_t NS, int64_t KT, int64_t M, int cus, int *wk, int *sg
     *sg = int(SG);
     *run = int(R);
     *unroll = R <= 4 ? 2 : 4;
-}
-
-// Large matrices (at least stream_min_tiles tiles, K staged whole in LDS)
-// use the streaming kernel: a grid of CUs * stream_waves_per_cu long-lived
-// waves, each streaming an equal contiguous share of the tiles.
-void gemv_plan_full(int64_t NS, int64_t K, int cus, int *wk, int *sg, int *run, int *unroll,
-                    int *g) {
-    const GemvPolicy &p = gemv_policy();
-    const int64_t KT = ceil_div(K, kTileK);
-    const int64_t T = NS * KT;
-    // (Tile indices are 32-bit in the streaming kernel: T < 2^30 is 1 TiB of weights.)
-    if (p.stream_min_tiles > 0 && T >= p.stream_min_tiles && T < (int64_t(1) << 30) &&
-        gemv_stream_fits(K)) {
-        const int64_t G = std::min<int64_t>(T, int64_t(cus) * p.stream_waves_per_cu);
-        *wk = *sg = *run = 0;
-        *unroll = p.stream_unroll;
-        *g = int(std::max<int64_t>(1, G));
-        return;
-    }
-    *g = 0;
-    gemv_plan(NS, KT, cus, wk, sg, run, unroll);
 }
 
 }  // namespace w2a8
@@ -216,8 +204,9 @@ int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t NS = Np / kTileRows;
     int64_t bytes = 0;
     if (M == 1) {
-        // GEMV: one 64-bit split-k combining word per padded row.
-        bytes = 8 * Np;
+        // GEMV: one 64-bit split-k combining word per padded row, if the
+        // plan may split a strip's k-range at all.
+        if (gemv_may_split(round_up(K, kTileK) / kTileK, gemv_policy())) bytes = 8 * Np;
     } else if (M <= kRowsMaxM) {
         // Few rows: a combining word per (row, padded output), or the general
         // kernel's split-K partials and counters, whichever is larger.
@@ -336,14 +325,18 @@ int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q, fl
 int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32_t *y_i32,
               const float *s_a, float s_w, float *y_f32, void *workspace, int64_t ws_bytes,
               void *stream) {
-    if (!w_packed || !x || !workspace) return W2A8_ERR_NULL;
+    if (!w_packed || !x) return W2A8_ERR_NULL;
     if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
     if (y_f32 && !s_a) return W2A8_ERR_NULL;
     if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    const GemvPolicy pol = gemv_policy();
+    const bool need_ws = gemv_may_split(round_up(K, kTileK) / kTileK, pol);
+    if (need_ws && !workspace) return W2A8_ERR_NULL;
     if (!aligned(w_packed, 16) || !aligned(x, 16) || (y_i32 && !aligned(y_i32, 16)) ||
-        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)) || !aligned(workspace, 16))
+        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)) ||
+        (need_ws && !aligned(workspace, 16)))
         return W2A8_ERR_ALIGN;
-    if (ws_bytes < w2a8_workspace_bytes(1, N, K)) return W2A8_ERR_BUFSIZE;
+    if (need_ws && ws_bytes < 8 * round_up(N, kTileRows)) return W2A8_ERR_BUFSIZE;
     DeviceInfo dev;
     int st = current_device(&dev);
     if (st != W2A8_OK) return st;
@@ -363,10 +356,9 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
-    gemv_plan_full(a.NS, K, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll, &a.G);
+    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
     a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
-    hipError_t e = a.G > 0 ? launch_gemv_stream(a, static_cast<hipStream_t>(stream))
-                           : launch_gemv(a, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 
@@ -375,12 +367,15 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
 int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, int64_t K, float s_w,
                      float *y_f32, int32_t *y_i32, void *workspace, int64_t ws_bytes,
                      void *stream) {
-    if (!w_packed || !x_bf16 || !y_f32 || !workspace) return W2A8_ERR_NULL;
+    if (!w_packed || !x_bf16 || !y_f32) return W2A8_ERR_NULL;
     if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    const GemvPolicy pol = gemv_policy();
+    const bool need_ws = gemv_may_split(round_up(K, kTileK) / kTileK, pol);
+    if (need_ws && !workspace) return W2A8_ERR_NULL;
     if (!aligned(w_packed, 16) || !aligned(x_bf16, 16) || !aligned(y_f32, 16) ||
-        (y_i32 && !aligned(y_i32, 16)) || !aligned(workspace, 16))
+        (y_i32 && !aligned(y_i32, 16)) || (need_ws && !aligned(workspace, 16)))
         return W2A8_ERR_ALIGN;
-    if (ws_bytes < w2a8_workspace_bytes(1, N, K)) return W2A8_ERR_BUFSIZE;
+    if (need_ws && ws_bytes < 8 * round_up(N, kTileRows)) return W2A8_ERR_BUFSIZE;
     DeviceInfo dev;
     int st = current_device(&dev);
     if (st != W2A8_OK) return st;
@@ -400,8 +395,7 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
-    a.G = 0;
-    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
     hipError_t e = launch_gemv_fused(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
@@ -415,9 +409,10 @@ namespace {
 
 // Validates the projection arrays and fills the table; the launch's NS is
 // the total strip count.  `need_f32` makes every y_f32 entry mandatory.
-int grouped_setup(int G, const void *const *w_packed, const int64_t *N, int64_t K,
-                  const float *s_w, int32_t *const *y_i32, float *const *y_f32, bool need_f32,
-                  GemvGroups *t, int64_t *ns_total, int64_t *ws_need, bool *any_f32) {
+int grouped_setup(const GemvPolicy &pol, int G, const void *const *w_packed, const int64_t *N,
+                  int64_t K, const float *s_w, int32_t *const *y_i32, float *const *y_f32,
+                  bool need_f32, GemvGroups *t, int64_t *ns_total, int64_t *ws_need,
+                  bool *any_f32) {
     if (G < 1 || G > kMaxGroups) return W2A8_ERR_SHAPE;
     if (!w_packed || !N || !s_w) return W2A8_ERR_NULL;
     if (need_f32 && !y_f32) return W2A8_ERR_NULL;
@@ -439,7 +434,7 @@ int grouped_setup(int G, const void *const *w_packed, const int64_t *N, int64_t 
         t->y_i32[g] = yi;
         t->y_f32[g] = yf;
         ns += Np / kTileRows;
-        ws += w2a8_workspace_bytes(1, N[g], K);
+        if (gemv_may_split(round_up(K, kTileK) / kTileK, pol)) ws += 8 * Np;
         if (ns * kTileRows > kMaxN) return W2A8_ERR_SHAPE;
     }
     for (int g = G; g < kMaxGroups; ++g) {
@@ -455,8 +450,9 @@ int grouped_setup(int G, const void *const *w_packed, const int64_t *N, int64_t 
     return W2A8_OK;
 }
 
-int grouped_launch(const GemvGroups &t, int64_t ns, int64_t K, const int8_t *x,
-                   const uint16_t *xb, const float *s_a, void *workspace, void *stream) {
+int grouped_launch(const GemvPolicy &pol, const GemvGroups &t, int64_t ns, int64_t K,
+                   const int8_t *x, const uint16_t *xb, const float *s_a, void *workspace,
+                   void *stream) {
     DeviceInfo dev;
     int st = current_device(&dev);
     if (st != W2A8_OK) return st;
@@ -474,9 +470,8 @@ int grouped_launch(const GemvGroups &t, int64_t ns, int64_t K, const int8_t *x,
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(ns);
-    a.G = 0;
     // One plan for the whole launch, as for a matrix of all the strips.
-    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
     a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
     hipError_t e = launch_gemv_grouped(a, t, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
@@ -493,14 +488,16 @@ int w2a8_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int6
     GemvGroups t;
     int64_t ns = 0, need = 0;
     bool any_f32 = false;
-    int st = grouped_setup(G, w_packed, N, K, s_w, y_i32, y_f32, false, &t, &ns, &need, &any_f32);
+    const GemvPolicy pol = gemv_policy();
+    int st = grouped_setup(pol, G, w_packed, N, K, s_w, y_i32, y_f32, false, &t, &ns, &need,
+                           &any_f32);
     if (st != W2A8_OK) return st;
-    if (!x || !workspace) return W2A8_ERR_NULL;
+    if (!x || (need > 0 && !workspace)) return W2A8_ERR_NULL;
     if (any_f32 && !s_a) return W2A8_ERR_NULL;
-    if (!aligned(x, 16) || (s_a && !aligned(s_a, 4)) || !aligned(workspace, 16))
+    if (!aligned(x, 16) || (s_a && !aligned(s_a, 4)) || (need > 0 && !aligned(workspace, 16)))
         return W2A8_ERR_ALIGN;
     if (ws_bytes < need) return W2A8_ERR_BUFSIZE;
-    return grouped_launch(t, ns, K, x, nullptr, s_a, workspace, stream);
+    return grouped_launch(pol, t, ns, K, x, nullptr, s_a, workspace, stream);
 }
 
 int w2a8_linear_gemv_grouped(int G, const void *const *w_packed, const int64_t *N, int64_t K,
@@ -510,12 +507,14 @@ int w2a8_linear_gemv_grouped(int G, const void *const *w_packed, const int64_t *
     GemvGroups t;
     int64_t ns = 0, need = 0;
     bool any_f32 = false;
-    int st = grouped_setup(G, w_packed, N, K, s_w, y_i32, y_f32, true, &t, &ns, &need, &any_f32);
+    const GemvPolicy pol = gemv_policy();
+    int st = grouped_setup(pol, G, w_packed, N, K, s_w, y_i32, y_f32, true, &t, &ns, &need,
+                           &any_f32);
     if (st != W2A8_OK) return st;
-    if (!x_bf16 || !workspace) return W2A8_ERR_NULL;
-    if (!aligned(x_bf16, 16) || !aligned(workspace, 16)) return W2A8_ERR_ALIGN;
+    if (!x_bf16 || (need > 0 && !workspace)) return W2A8_ERR_NULL;
+    if (!aligned(x_bf16, 16) || (need > 0 && !aligned(workspace, 16))) return W2A8_ERR_ALIGN;
     if (ws_bytes < need) return W2A8_ERR_BUFSIZE;
-    return grouped_launch(t, ns, K, nullptr, x_bf16, nullptr, workspace, stream);
+    return grouped_launch(pol, t, ns, K, nullptr, x_bf16, nullptr, workspace, stream);
 }
 
 }  // extern "C"
@@ -586,8 +585,7 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
         g.KT = a.KT;
         g.NS = a.NS;
         g.M = int(M);
-        g.G = 0;
-        gemv_rows_plan(g.NS, g.KT, M, dev.cus, &g.WK, &g.SG, &g.RUN, &g.unroll);
+        gemv_rows_plan(gemv_policy(), g.NS, g.KT, M, dev.cus, &g.WK, &g.SG, &g.RUN, &g.unroll);
         if (g.SG > 1 && !workspace) return W2A8_ERR_NULL;
         hipError_t e = launch_gemv_rows(g, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
@@ -606,40 +604,24 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
         !(unroll == 2 || unroll == 4 || unroll == 8) || krange_tiles < 1 || krange_tiles > 256 ||
         split_min_tiles < 1)
         return W2A8_ERR_VALUE;
-    GemvPolicy &p = gemv_policy();
-    p.wg_per_cu = wg_per_cu;
-    p.tiles_per_wave = tiles_per_wave;
-    p.unroll = unroll;
-    p.krange_tiles = krange_tiles;
-    p.split_min_tiles = split_min_tiles;
+    set_gemv_policy(GemvPolicy{wg_per_cu, tiles_per_wave, unroll, krange_tiles, split_min_tiles});
     return W2A8_OK;
 }
 
 int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
-                   int *unroll, int *stream_waves) {
-    if (!waves_per_wg || !wgs_per_strip || !unroll || !stream_waves) return W2A8_ERR_NULL;
+                   int *unroll) {
+    if (!waves_per_wg || !wgs_per_strip || !unroll) return W2A8_ERR_NULL;
     if (!nk_ok(N, K) || cus < 1) return W2A8_ERR_SHAPE;
     const int64_t NS = round_up(N, kTileRows) / kTileRows;
     const int64_t KT = round_up(K, kTileK) / kTileK;
     int run = 0;
-    gemv_plan_full(NS, K, cus, waves_per_wg, wgs_per_strip, &run, unroll, stream_waves);
+    gemv_plan(gemv_policy(), NS, KT, cus, waves_per_wg, wgs_per_strip, &run, unroll);
     return W2A8_OK;
 }
 
 int w2a8_tune_gemm(int kernel) {
     if (kernel < 0 || kernel > 3) return W2A8_ERR_VALUE;
-    gemm_kernel_mode() = kernel;
-    return W2A8_OK;
-}
-
-int w2a8_tune_gemv_stream(int min_tiles, int waves_per_cu, int unroll) {
-    if (min_tiles < 0 || waves_per_cu < 1 || waves_per_cu > 64 ||
-        !(unroll == 2 || unroll == 4 || unroll == 8))
-        return W2A8_ERR_VALUE;
-    GemvPolicy &p = gemv_policy();
-    p.stream_min_tiles = min_tiles;
-    p.stream_waves_per_cu = waves_per_cu;
-    p.stream_unroll = unroll;
+    set_gemm_kernel_mode(kernel);
     return W2A8_OK;
 }
 

@@ -63,15 +63,19 @@ int quant_act_int4(const uint16_t *x_bf16, int64_t M, int64_t K, uint8_t *x_q4, 
 int w2a4_gemv(const void *w_packed, const uint8_t *x_q4, int64_t N, int64_t K, int32_t *y_i32,
               const float *s_a, float s_w, float *y_f32, void *workspace, int64_t ws_bytes,
               void *stream) {
-    if (!w_packed || !x_q4 || !workspace) return W2A8_ERR_NULL;
+    if (!w_packed || !x_q4) return W2A8_ERR_NULL;
     if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
     if (y_f32 && !s_a) return W2A8_ERR_NULL;
     if (!shape_ok(N, K)) return W2A8_ERR_SHAPE;
+    const GemvPolicy pol = gemv_policy();
+    const bool need_ws = gemv_may_split((K + kTileK - 1) / kTileK, pol);
+    if (need_ws && !workspace) return W2A8_ERR_NULL;
     if (!aligned_to(w_packed, 16) || !aligned_to(x_q4, 16) || (y_i32 && !aligned_to(y_i32, 16)) ||
         (y_f32 && !aligned_to(y_f32, 16)) || (s_a && !aligned_to(s_a, 4)) ||
-        !aligned_to(workspace, 16))
+        (need_ws && !aligned_to(workspace, 16)))
         return W2A8_ERR_ALIGN;
-    if (ws_bytes < w2a8_workspace_bytes(1, N, K)) return W2A8_ERR_BUFSIZE;
+    if (need_ws && ws_bytes < 8 * ((N + kTileRows - 1) / kTileRows * kTileRows))
+        return W2A8_ERR_BUFSIZE;
     DeviceInfo dev;
     int st = current_device(&dev);
     if (st != W2A8_OK) return st;
@@ -91,8 +95,7 @@ int w2a4_gemv(const void *w_packed, const uint8_t *x_q4, int64_t N, int64_t K, i
     a.K = int(K);
     a.KT = int((K + kTileK - 1) / kTileK);
     a.NS = int(Np / kTileRows);
-    a.G = 0;
-    gemv_plan(a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
     hipError_t e = launch_gemv_a4(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }

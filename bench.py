@@ -54,7 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
 # Sources that decide what the GEMV kernel reads and writes: the kernel, its
 # shared helpers and the host-side launch plan.
 GEMV_SRCS = [os.path.join(ROOT, "w2a8_gemv_amd", "csrc", f)
-             for f in ("gemv.hip", "common.h", "device.h", "host.hip")]
+             for f in ("gemv.hip", "gemv_ring.hip", "common.h", "device.h", "host.hip")]
 
 
 def gemv_sources_sha256():
@@ -93,6 +93,11 @@ def parse_args():
     ap.add_argument("--steps-per-graph", type=int, default=16,
                     help="consecutive steps captured in one hipGraph (default 16, one "
                          "rotation of the weight copies)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="sweep the plain-read kernel over load width, loads in flight per "
+                         "wave, waves per CU, non-temporal or plain loads and contiguous or "
+                         "strided chunks, on cold 1 GiB, 71 MB and 35 MB buffers; prints one "
+                         "JSON line with the table and exits")
     ap.add_argument("--bf16-context", action="store_true",
                     help="also time the pages' bf16 torch.matmul comparison on the sweep "
                          "shapes (context only, off by default)")
@@ -125,7 +130,7 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
         factor = CALIB_BYTES / (max(copies) * 1024.0)
         per = {}
         for r in rows:
-            if "gemv_kernel" in r["Kernel_Name"]:
+            if "gemv_kernel" in r["Kernel_Name"] or "gemv_ring_kernel" in r["Kernel_Name"]:
                 per.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]) * 1024.0)
         return factor, per
 
@@ -133,7 +138,7 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
     wf, write = load(write_csv)
     shapes = []
     for n, k in synth.SWEEP_SHAPES:
-        wk, sg, _ = w2a8.gemv_plan(n, k, cus)
+        _, wk, sg, _ = w2a8.gemv_plan(n, k, cus)
         grid = (-(-n // 32)) * sg * 64 * wk
         f = sum(fetch[grid]) / len(fetch[grid]) * ff
         w = sum(write[grid]) / len(write[grid]) * wf
@@ -284,31 +289,101 @@ def kernel_times(torch, lib, shape, reps, stream, rounds=5):
                        rounds)
 
 
-READ_WAVES = (1024, 2048)
+# Plain-read configurations tried as the floor of each matrix: (waves per CU,
+# width in bytes per lane, loads in flight per wave, non-temporal, strided).
+READ_FLOOR_CONFIGS = [(4, 16, 8, 1, 0), (8, 16, 8, 1, 0), (4, 16, 16, 1, 0), (8, 16, 16, 1, 0),
+                      (16, 16, 8, 1, 0), (8, 16, 8, 1, 1), (16, 16, 4, 1, 0)]
 
 
-def read_floor_times(torch, readref, shape, stream, rounds=5):
-    """The same cold rotation read by the pure streaming-read kernel (no
-    arithmetic, no output): per-launch device time of the fastest of a few
-    grid sizes (1024, 2048 and 4 waves per strip), as a floor for the GEMV of
-    that matrix size."""
+def read_floor_times(torch, readref, shape, stream, rounds=5, configs=READ_FLOOR_CONFIGS):
+    """The same cold rotation read by the plain-read kernel (no arithmetic, no
+    output): per-launch device time of the fastest of `configs`, as a floor
+    for the GEMV of that matrix size."""
     if readref is None:
         return None
     nbytes = shape.copies[0].numel()
-    ptrs = [ctypes.c_void_p(c.data_ptr()) for c in shape.copies]
-    out = torch.zeros(1 << 22, dtype=torch.int32, device=shape.x.device)
-    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(shape.x.device).multi_processor_count
     best = None
-    for waves in READ_WAVES + (4 * ((shape.n + 31) // 32),):
-        def launch(j, waves=waves):
-            rc = readref.w2a8_readref_stream(ptrs[j % len(ptrs)], nbytes, waves,
-                                             ctypes.c_void_p(out.data_ptr()), sp)
-            if rc != 0:
-                raise RuntimeError(f"stream read failed with status {rc}")
-        ts = graph_times(torch, launch, max(24, len(ptrs)), stream, rounds)
+    for cfg in configs:
+        ts = read_times(torch, readref, shape.copies, nbytes, cus, cfg, stream, rounds)
         if best is None or sorted(ts)[len(ts) // 2] < sorted(best[1])[len(best[1]) // 2]:
-            best = (waves, ts)
+            best = (cfg, ts)
     return best
+
+
+def read_times(torch, readref, copies, nbytes, cus, cfg, stream, rounds=5, reps=None):
+    """Per-launch device time (us) of the plain read of `nbytes` under `cfg`
+    (waves per CU, width, depth, nt, strided), one launch per copy in a graph
+    (at least 24 launches, or `reps`), so every launch reads a cold copy."""
+    wpc, width, depth, nt, strided = cfg
+    waves = cus * wpc
+    ptrs = [ctypes.c_void_p(c.data_ptr()) for c in copies]
+    out = torch.zeros(max(waves, 1), dtype=torch.int32, device=copies[0].device)
+    op = ctypes.c_void_p(out.data_ptr())
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(j):
+        rc = readref.w2a8_readref_read(ptrs[j % len(ptrs)], nbytes, waves, width, depth, nt,
+                                       strided, op, sp)
+        if rc != 0:
+            raise RuntimeError(f"plain read failed with status {rc}")
+    return graph_times(torch, launch, reps or max(24, len(ptrs)), stream, rounds)
+
+
+READ_CEILING_SIZES = [("1 GiB", 1 << 30), ("55296x5120 packed", 70778880),
+                      ("5120x27648 packed", 35389440)]
+
+
+def read_ceiling(torch, readref, stream, cus):
+    """Sweep of the plain-read kernel on cold buffers of the READ_CEILING_SIZES:
+    every (waves per CU, width, loads in flight, nt, strided) combination,
+    per-launch device time from a graph with one launch per buffer copy
+    (copies >= 700 MB in total, two for 1 GiB).  Also the per-launch time of
+    an empty kernel (the dispatch floor of a graph of launches)."""
+    import numpy as np
+    wpcs = [1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64]
+    out = {"method": "per-launch device time of a graph with one launch per cold copy, median "
+                     "of 5 replays (includes the dispatch gap between graph nodes)",
+           "peak_GBps": PEAK_HBM_GBPS, "cus": cus, "sizes": []}
+    dev = torch.device("cuda", torch.cuda.current_device())
+    ob = torch.zeros(cus * 64, dtype=torch.int32, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    empty = {}
+    for wpc in (1, 4, 16, 64):
+        def el(j, w=cus * wpc):
+            readref.w2a8_readref_empty(w, ctypes.c_void_p(ob.data_ptr()), sp)
+        ts = graph_times(torch, el, 24, stream)
+        empty[wpc] = round(float(np.median(ts)), 3)
+    out["empty_kernel_us_by_waves_per_cu"] = empty
+    for name, nbytes in READ_CEILING_SIZES:
+        slots = max(2, int(-(-ROTATE_BYTES // nbytes)) + 1)
+        copies = [torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32,
+                                device=dev) for _ in range(slots)]
+        torch.cuda.synchronize()
+        rows = []
+        for wpc in wpcs:
+            print(f"# read ceiling {name}: {wpc} waves per CU", file=sys.stderr, flush=True)
+            for width in (16, 8, 4):
+                for depth in (2, 4, 8, 12, 16):
+                    for nt in (1, 0):
+                        for strided in (0, 1):
+                            cfg = (wpc, width, depth, nt, strided)
+                            ts = read_times(torch, readref, copies, nbytes, cus, cfg, stream,
+                                            reps=max(8 if nbytes > (256 << 20) else 24, slots))
+                            med = float(np.median(ts))
+                            rows.append({"waves_per_cu": wpc, "width": width, "depth": depth,
+                                         "nt": nt, "strided": strided, "median_us": round(med, 3),
+                                         "min_us": round(min(ts), 3),
+                                         "GBps": round(nbytes / med / 1e3, 1)})
+        rows.sort(key=lambda r: r["median_us"])
+        best = rows[0]
+        out["sizes"].append({"name": name, "bytes": nbytes, "copies": slots,
+                             "best": best, "best_pct_peak": round(best["GBps"] / PEAK_HBM_GBPS * 100, 1),
+                             "top": rows[:25], "all": rows})
+        print(f"# read ceiling {name}: best {best}", file=sys.stderr, flush=True)
+        del copies
+        torch.cuda.empty_cache()
+    return out
 
 
 def graph_times(torch, launch, reps, stream, rounds=5):
@@ -750,9 +825,11 @@ def load_readref():
     if not os.path.exists(b.READREF_PATH):
         return None
     L = ctypes.CDLL(b.READREF_PATH)
-    L.w2a8_readref_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
-                                      ctypes.c_void_p, ctypes.c_void_p]
-    L.w2a8_readref_stream.restype = ctypes.c_int
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.w2a8_readref_read.argtypes = [P, ctypes.c_int64, I, I, I, I, I, P, P]
+    L.w2a8_readref_read.restype = I
+    L.w2a8_readref_empty.argtypes = [I, P, P]
+    L.w2a8_readref_empty.restype = I
     return L
 
 
@@ -763,9 +840,11 @@ def shape_detail(torch, lib, readref, s, stream):
     p["rotation_copies"] = len(s.copies)
     fl = read_floor_times(torch, readref, s, stream)
     if fl is not None:
-        waves, ts = fl
+        cfg, ts = fl
         med = sorted(ts)[len(ts) // 2]
-        p["read_floor"] = {"median_us": round(med, 3), "waves": waves,
+        p["read_floor"] = {"median_us": round(med, 3),
+                           "config": dict(zip(("waves_per_cu", "width", "depth", "nt", "strided"),
+                                              cfg)),
                            "packed_bytes": s.copies[0].numel(),
                            "gemv_over_floor": round(p["median_us"] / med, 3)}
     return p
@@ -817,6 +896,12 @@ def main():
     cus = props.multi_processor_count
     lib = w2a8.lib()
     stream = torch.cuda.Stream()
+    if args.read_ceiling:
+        rr = load_readref()
+        if rr is None:
+            raise RuntimeError("the plain-read measurement library is not built")
+        print(json.dumps({"read_ceiling": read_ceiling(torch, rr, stream, cus)}), flush=True)
+        return
     if args.gemm_only:
         print(json.dumps({"gemm": gemm_extras(torch, w2a8, synth, lib, stream, cus),
                           "gemm_peak_int8_TOPS": PEAK_INT8_TOPS}), flush=True)
@@ -881,7 +966,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "kernel": "w2a8::gemv_kernel (all launches of the timed region)",
+            "kernel": "w2a8::gemv_ring_kernel (all launches of the timed region)",
             "avg_launch_us": round(dev_us / len(shapes), 3),
             "step_device_us": round(dev_us, 3),
         },
@@ -892,8 +977,9 @@ def main():
                                 "(cold mode); a graph of one launch per copy (at least 24), "
                                 "device time per launch from two events per replay, median "
                                 "of 5 replays (includes the graph's inter-node gaps). "
-                                "read_floor: the pure streaming-read kernel over the same "
-                                "rotation, fastest of 1024, 2048 and 4 waves per strip",
+                                "read_floor: the plain-read kernel over the same rotation, "
+                                "fastest of READ_FLOOR_CONFIGS (waves per CU, bytes per lane, "
+                                "loads in flight, non-temporal, strided)",
             "read_floor_sweep": read_floor_sweep(per),
             "plans": {f"{s.n}x{s.k}": list(w2a8.gemv_plan(s.n, s.k, cus)) for s in shapes},
             "a100_page_us_context": {f"{n}x{k}": v for (n, k), v in A100_US.items()},

@@ -16,7 +16,10 @@
 extern "C" {
 #endif
 
-/* GEMV launch plan (w2a8_gemv).  A 32-row strip with at least
+/* GEMV launch plan of the batch kernel (w2a8_gemv for K not a multiple of
+ * 16; the fused, grouped and W2A4 GEMVs).  The ring kernel's plan uses only
+ * `split_min_tiles` (the shortest strip it splits over workgroups).  A
+ * 32-row strip with at least
  * `split_min_tiles` k-tiles (1 KiB each) is split over workgroups: about one
  * per `tiles_per_wave` tiles, at most 12, and more when there are too few
  * strips to give `wg_per_cu` (1..64) workgroups per compute unit; never more
@@ -29,6 +32,25 @@ extern "C" {
  * out-of-range knobs. */
 int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_tiles,
                    int split_min_tiles);
+
+/* Forced GEMV plan for measurement sweeps (w2a8_gemv only; the fused,
+ * grouped and W2A4 GEMVs keep their automatic plans).  kernel 0 restores the
+ * automatic plan (other arguments ignored).  kernel 1: the batch kernel with
+ * `waves_per_wg` (1..16) waves per workgroup, `wgs_per_strip` (1..4096)
+ * workgroups per 32-row strip (at most one per k-tile) and two load batches
+ * of `depth` (2, 4 or 8) tiles; kernel 2: the ring kernel with `depth` (2, 4,
+ * 6, 8 or 12) tiles in flight per wave; kernel 3: whole strips per wave
+ * (`wgs_per_strip` is then strips per wave; K a multiple of 16); kernel 4:
+ * the ring kernel with the strip's tiles interleaved over its waves (needs
+ * `direct_x`, K a multiple of 16).  `direct_x` (0 or 1) loads each
+ * tile's activations next to its weights instead of staging the wave's run
+ * in LDS (K a multiple of 16; not with batch 8).  w2a8_gemv returns
+ * W2A8_ERR_VALUE for a forced plan whose runs exceed 32 tiles (batch kernel)
+ * or 64 tiles (ring kernel) per wave, or whose activation staging needs more
+ * LDS than a workgroup may allocate on the device.  w2a8_workspace_bytes(1, N, K) counts
+ * a forced split.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int depth,
+                         int direct_x);
 
 /* Batched product kernel (w2a8_gemm): 0 = automatic (default), 1 = the
  * pipelined MFMA kernel whenever K is a multiple of 16 (its configuration
@@ -43,12 +65,15 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
  * pipelined kernel.  Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
 
-/* The plan w2a8_gemv would use for (N, K) on a device with `cus` compute
- * units under the current knobs: waves per workgroup, workgroups per 32-row
- * strip (more than 1 only when w2a8_workspace_bytes(1, N, K) > 0) and load
- * batch.  Returns W2A8_OK, W2A8_ERR_NULL or W2A8_ERR_SHAPE. */
-int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
-                   int *unroll);
+/* The automatic plan w2a8_gemv would use for (N, K) on a device with `cus`
+ * compute units under the current knobs: the kernel (2: the ring kernel, for
+ * K a multiple of 16; 1: the batch kernel, for other K), waves per workgroup,
+ * workgroups per 32-row strip (more than 1 only when
+ * w2a8_workspace_bytes(1, N, K) > 0) and depth (ring: tiles in flight per
+ * wave; batch: load batch).  Returns W2A8_OK, W2A8_ERR_NULL or
+ * W2A8_ERR_SHAPE. */
+int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg,
+                   int *wgs_per_strip, int *depth);
 
 #ifdef __cplusplus
 }

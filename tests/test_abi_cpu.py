@@ -383,7 +383,7 @@ def test_workspace_rule_matches_the_plans():
             for N in (1, 2560, 55296):
                 for K in (1, 128, 385, 2560, 6016, 6017, 27648, 40000):
                     ws = w2a8.workspace_bytes(1, N, K)
-                    splits = [w2a8.gemv_plan(N, K, cus)[1] > 1 for cus in (1, 80, 256, 304)]
+                    splits = [w2a8.gemv_plan(N, K, cus)[2] > 1 for cus in (1, 80, 256, 304)]
                     if ws == 0:
                         assert not any(splits), (pol, N, K)
                     kt = -(-K // 128)
@@ -468,7 +468,16 @@ def test_gemv_plan_properties():
             for N in (1, 31, 2560, 55296):
                 for K in (1, 127, 128, 2560, 27648, 100000, 1048448):
                     for cus in (1, 80, 256):
-                        wk, sg, u = w2a8.gemv_plan(N, K, cus)
+                        kern, wk, sg, u = w2a8.gemv_plan(N, K, cus)
+                        assert kern == (2 if K % 16 == 0 else 1)
+                        if kern == 2:
+                            kt = -(-K // 128)
+                            assert 1 <= sg <= kt and 1 <= wk <= 16 and u in (4, 6, 8)
+                            if sg > 1:
+                                assert kt >= pol[4] and wk == 1
+                            if -(-N // 32) >= 2 * cus:
+                                assert (wk, sg) == (1, 1)
+                            continue
                         kt = -(-K // 128)
                         ktw = -(-kt // sg)
                         run = -(-ktw // wk)
@@ -484,23 +493,33 @@ def test_gemv_plan_properties():
 
 
 def test_gemv_default_plans_of_the_measured_shapes():
-    """The default rule's plans (waves per workgroup, workgroups per strip,
-    load batch) on a 256-CU device for the shapes its choices were measured
-    on: twice the waves with half-length runs in unsplit strips while there
-    are no more strips than CUs, 4-wave workgroups above that, and a split
-    over workgroups for strips of 48 k-tiles or more, into equal k-ranges
-    where one of the two smaller counts gives them (3200 x 10240: 10 ranges
-    of 8 tiles, not 12 of 7; 2560 x 27648: 12 of 18, not 13 of 17)."""
+    """The default plans (kernel, waves per workgroup, workgroups per strip,
+    depth) on a 256-CU device for the shapes the rules were measured on.
+
+    Ring kernel (K a multiple of 16): one wave per whole strip from two
+    strips per CU up; single-wave workgroups with the k-range split to about
+    3.75 waves per CU for strips of 48 tiles or more; 8-wave workgroups
+    otherwise.  Batch kernel (ragged K; the same tile counts as the workload
+    shapes, K one less): twice the waves with half-length runs in unsplit
+    strips while there are no more strips than CUs, 4-wave workgroups above
+    that, and a split over workgroups for strips of 48 k-tiles or more, into
+    equal k-ranges where one of the two smaller counts gives them."""
     assert w2a8.DEFAULT_GEMV_POLICY == (4, 6, 8, 256, 48)
-    want = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
-            (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),
-            (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 10, 4),
-            (5120, 27648): (3, 12, 4), (55296, 5120): (8, 1, 4), (2560, 27648): (3, 12, 4),
-            (8192, 8192): (1, 11, 4)}
-    for (N, K), plan in want.items():
-        assert tuple(w2a8.gemv_plan(N, K, 256)) == plan, (N, K)
+    ring = {(2560, 2560): (8, 1, 4), (3840, 2560): (8, 1, 4), (3200, 3200): (8, 1, 4),
+            (4800, 3200): (8, 1, 4), (13824, 2560): (8, 1, 4), (20480, 3200): (1, 1, 8),
+            (2560, 6912): (1, 12, 4), (3200, 10240): (1, 10, 4), (5120, 27648): (1, 6, 8),
+            (55296, 5120): (1, 1, 4), (6912, 5120): (8, 1, 6), (5120, 3456): (8, 1, 4)}
+    for (N, K), plan in ring.items():
+        assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
+    batch = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
+             (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),
+             (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 10, 4),
+             (5120, 27648): (3, 12, 4), (55296, 5120): (8, 1, 4), (2560, 27648): (3, 12, 4),
+             (8192, 8192): (1, 11, 4)}
+    for (N, K), plan in batch.items():
+        assert tuple(w2a8.gemv_plan(N, K - 1, 256)) == (1,) + plan, (N, K)
     # The same 80-strip matrix on a 64-CU device has more strips than CUs.
-    assert tuple(w2a8.gemv_plan(2560, 2560, 64)) == (4, 1, 4)
+    assert tuple(w2a8.gemv_plan(2560, 2559, 64)) == (1, 4, 1, 4)
 
 
 def test_binding_refuses_host_tensors_for_device_calls():

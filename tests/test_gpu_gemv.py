@@ -27,6 +27,7 @@ DEFAULT_POLICY = w2a8.DEFAULT_GEMV_POLICY
 def _restore_policy():
     yield
     w2a8.tune_gemv(*DEFAULT_POLICY)
+    w2a8.tune_gemv_force(0)
 
 
 def _case(N, K, seed, sparse=False):
@@ -60,6 +61,66 @@ def test_gemv_forced_splits(policy, N, K):
     w2a8.tune_gemv(*policy)
     x, w, wp, xd = _case(N, K, seed=7 + N + K)
     np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
+
+
+# Forced plans: (kernel, waves per workgroup, workgroups per strip, depth,
+# direct activations).  Kernel 2 (ring) at every depth, staged and direct,
+# single-wave and multi-wave workgroups, split and unsplit strips; kernel 1
+# (batch) with its direct-activation path forced on.
+FORCED = [(2, 1, 1, 2, 0), (2, 1, 1, 12, 0), (2, 4, 1, 4, 0), (2, 3, 2, 6, 0), (2, 8, 3, 8, 0),
+          (2, 16, 1, 12, 0), (2, 2, 5, 8, 0), (2, 1, 1, 2, 1), (2, 4, 1, 8, 1), (2, 3, 4, 12, 1),
+          (2, 6, 2, 6, 1), (2, 16, 8, 4, 1), (1, 4, 1, 4, 1), (1, 2, 3, 2, 1),
+          # whole strips per wave (waves per workgroup, strips per wave)
+          (3, 1, 1, 4, 1), (3, 1, 2, 8, 1), (3, 4, 3, 12, 1), (3, 2, 5, 2, 1),
+          # strip tiles interleaved over its waves and workgroups
+          (4, 1, 6, 8, 1), (4, 4, 3, 4, 1), (4, 2, 2, 12, 1), (4, 8, 1, 6, 1), (4, 1, 1, 2, 1),
+          # row slices of 16, 8 and 4 rows per workgroup
+          (5, 1, 1, 4, 1), (5, 3, 2, 8, 1), (6, 1, 1, 12, 1), (6, 2, 3, 6, 1), (7, 1, 1, 8, 1),
+          (7, 4, 1, 4, 1), (7, 1, 5, 12, 1), (7, 16, 2, 6, 1)]
+
+
+@pytest.mark.parametrize("force", FORCED, ids=[".".join(map(str, f)) for f in FORCED])
+@pytest.mark.parametrize("N,K", [(33, 1000), (64, 2560), (200, 3200), (96, 27648), (31, 129),
+                                 (70, 2000), (1, 16)])
+def test_gemv_forced_plans(force, N, K):
+    """Every kernel and ring depth, on ragged N and K (runs past K, empty runs)."""
+    kt = -(-K // 128)
+    sg = min(force[2], kt)
+    if force[0] in (1, 2) and (-(-(-(-kt // sg)) // min(force[1], -(-kt // sg)))
+                               > (64 if force[0] == 2 else 32)):
+        pytest.skip("run longer than the kernel stages")
+    if force[0] >= 3 and K % 16:
+        pytest.skip("kernel needs K a multiple of 16")
+    w2a8.tune_gemv_force(*force)
+    try:
+        x, w, wp, xd = _case(N, K, seed=11 + N + 3 * K)
+        ws = torch.zeros(max(1, w2a8.workspace_bytes(1, N, K)), dtype=torch.uint8, device=dev())
+        ref = oracle.gemm_i32(x, w)
+        for _ in range(2):     # the split path leaves the workspace zeroed
+            np.testing.assert_array_equal(gemv_dev(wp, xd, N, K, workspace=ws), ref)
+            assert int(ws.count_nonzero()) == 0
+        sa = np.array([0.0173], np.float32)
+        yi, yf = gemv_dev(wp, xd, N, K, sa=to_dev(sa), sw=0.031, want_f32=True, workspace=ws)
+        np.testing.assert_array_equal(yf, oracle.epilogue(ref, sa, np.float32(0.031)))
+    finally:
+        w2a8.tune_gemv_force(0)
+
+
+@pytest.mark.parametrize("idx", range(len(synth.LARGE_SHAPES)))
+@pytest.mark.parametrize("force", [(2, 6, 1, 12, 0), (2, 2, 2, 8, 1), (2, 1, 1, 12, 0),
+                                   (3, 1, 2, 12, 1), (3, 4, 1, 4, 1), (4, 1, 6, 8, 1),
+                                   (7, 1, 1, 8, 1), (6, 2, 1, 12, 1), (5, 1, 3, 4, 1)])
+def test_gemv_forced_ring_large_shapes(force, idx):
+    N, K = synth.LARGE_SHAPES[idx]
+    kt = -(-K // 128)
+    if force[0] == 2 and -(-(-(-kt // force[2])) // force[1]) > 64:
+        pytest.skip("run longer than the kernel stages")
+    w2a8.tune_gemv_force(*force)
+    try:
+        x, w, wp, xd = _case(N, K, synth.LARGE_SEEDS[idx], sparse=True)
+        np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
+    finally:
+        w2a8.tune_gemv_force(0)
 
 
 @pytest.mark.parametrize("N,K", [(33, 1000), (2560, 2560), (100, 6016)])
@@ -175,7 +236,7 @@ def test_gemv_f32_only_output():
 def test_gemv_repeat_deterministic_and_workspace_reset():
     N, K = 2560, 6912
     w2a8.tune_gemv(8, 4, 4, 256, 1)   # strips split over workgroups: exercises the atomics
-    assert w2a8.gemv_plan(N, K, torch.cuda.get_device_properties(0).multi_processor_count)[1] > 1
+    assert w2a8.gemv_plan(N, K, torch.cuda.get_device_properties(0).multi_processor_count)[2] > 1
     x, w, wp, xd = _case(N, K, seed=31)
     ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
     ref = oracle.gemm_i32(x, w)

@@ -22,7 +22,8 @@ __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
-    "w2a8_linear_gemv", "tune_gemv", "gemv_plan", "DEFAULT_GEMV_POLICY", "tune_gemm",
+    "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "DEFAULT_GEMV_POLICY",
+    "tune_gemm",
     "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
     "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
 ]
@@ -90,7 +91,9 @@ def lib():
         L.w2a8_linear_gemv_grouped.restype = I32
         L.w2a8_tune_gemv.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv.restype = I32
-        L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P]
+        L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
+        L.w2a8_tune_gemv_force.argtypes = [I32, I32, I32, I32, I32]
+        L.w2a8_tune_gemv_force.restype = I32
         L.w2a8_tune_gemm.argtypes = [I32]
         L.w2a8_tune_gemm.restype = I32
         L.w2a8_gemv_plan.restype = I32
@@ -506,6 +509,13 @@ def tune_gemv(wg_per_cu: int, tiles_per_wave: int, unroll: int, krange_tiles: in
                                 split_min_tiles), "w2a8_tune_gemv")
 
 
+def tune_gemv_force(kernel: int, waves_per_wg: int = 1, wgs_per_strip: int = 1, depth: int = 2,
+                    direct_x: int = 0):
+    """Force a GEMV plan (kernel 1: batch kernel, 2: ring kernel; 0: automatic)."""
+    _check(lib().w2a8_tune_gemv_force(kernel, waves_per_wg, wgs_per_strip, depth, direct_x),
+           "w2a8_tune_gemv_force")
+
+
 def tune_gemm(kernel: int):
     """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general,
     3 few-row whenever M <= 8."""
@@ -513,9 +523,10 @@ def tune_gemm(kernel: int):
 
 
 def gemv_plan(N: int, K: int, cus: int):
-    """Launch plan of w2a8_gemv: (waves per workgroup, workgroups per strip,
-    load batch)."""
-    wk, sg, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib().w2a8_gemv_plan(N, K, cus, ctypes.byref(wk), ctypes.byref(sg), ctypes.byref(u)),
-           "w2a8_gemv_plan")
-    return wk.value, sg.value, u.value
+    """Automatic launch plan of w2a8_gemv: (kernel, waves per workgroup,
+    workgroups per strip, depth); kernel 2 is the ring kernel (K a multiple
+    of 16), 1 the batch kernel."""
+    kern, wk, sg, d = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().w2a8_gemv_plan(N, K, cus, ctypes.byref(kern), ctypes.byref(wk), ctypes.byref(sg),
+                                ctypes.byref(d)), "w2a8_gemv_plan")
+    return kern.value, wk.value, sg.value, d.value

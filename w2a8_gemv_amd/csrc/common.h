@@ -25,6 +25,7 @@ struct DeviceInfo {
     int id;
     int cus;       // compute units
     int xcds;      // accelerator complex dies sharing the dispatch round robin
+    int64_t lds;   // LDS bytes a workgroup may allocate
 };
 
 // Queries (once per device) the current device; checks it is gfx950.
@@ -37,6 +38,11 @@ struct GemvPolicy {
     int unroll;           // largest load batch in tiles (two in flight): 2, 4 or 8
     int krange_tiles;     // at most this many k-tiles per workgroup
     int split_min_tiles;  // split a strip over workgroups only if KT >= this
+    // Forced plan for measurement sweeps (force_kernel 0: automatic plan).
+    // 1: batch kernel with force_wk waves, force_sg workgroups per strip and
+    // load batch force_depth; 2: ring kernel with depth force_depth, direct
+    // activation loads when force_dx.
+    int force_kernel = 0, force_wk = 0, force_sg = 0, force_depth = 0, force_dx = 0;
 };
 // A consistent copy of the current knobs (taken under a lock: every call
 // plans from one snapshot, whatever other host threads set meanwhile).
@@ -46,7 +52,7 @@ void set_gemv_policy(const GemvPolicy &p);
 // workgroups (and so needs the workspace).  Depends on K alone, not on the
 // device.
 inline bool gemv_may_split(int64_t KT, const GemvPolicy &p) {
-    return KT >= p.split_min_tiles || KT > p.krange_tiles;
+    return KT >= p.split_min_tiles || KT > p.krange_tiles || (p.force_kernel && p.force_sg > 1);
 }
 
 // GEMV launch arguments (passed to the kernel by value).
@@ -65,6 +71,7 @@ struct GemvLaunch {
     int SG;       // workgroups (k-ranges) per row strip
     int RUN;      // longest run of tiles of one wave (<= 32)
     int unroll;
+    int TQ = 0, TR = 0;   // ring kernel, interleaved runs: KT = TQ*(SG*WK) + TR
     int DXOK = 0; // plain kernel: at most 5 waves per CU in the grid, so activation chunks may
                   // be loaded directly with the weights (latency-bound grids)
     // Workgroup kernel, set by its launcher so that the kernel divides
@@ -133,6 +140,9 @@ __device__ __forceinline__ bool split_add(uint64_t *word, int tiles, int val, in
 void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, int *sg, int *run,
                int *unroll);
 size_t gemv_lds_bytes(const GemvLaunch &a);
+// Ring-kernel plan of the plain GEMV (K a multiple of 16).
+void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, int *sg,
+                    int *run, int *depth);
 // Few activation rows (2 <= M <= 8): plan with runs of at most 8 tiles, and
 // the kernel (gemv.hip).  Workspace: 8 bytes per (row, padded output) when
 // strips are split.
@@ -144,6 +154,16 @@ constexpr int64_t kRowsMaxM = 8;
 // workgroup kernel with the fp32 epilogue (gemv.hip).
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream);
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
+// Ring-pipelined GEMV (gemv_ring.hip): runs of at most 64 tiles per wave.
+bool gemv_ring_fits(const GemvLaunch &a);
+size_t gemv_ring_lds_bytes(const GemvLaunch &a, bool dx);
+hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, bool dx, bool il, hipStream_t stream);
+// Row slices: 32/slices rows of a strip per workgroup (gemv_ring.hip), K a
+// multiple of 16, slices 2, 4 or 8.
+hipError_t launch_gemv_rows_slice(const GemvLaunch &a, int depth, int slices, hipStream_t stream);
+// Whole strips per wave (gemv_ring.hip), K a multiple of 16.
+hipError_t launch_gemv_strips(const GemvLaunch &a, int depth, int strips_per_wave,
+                              hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
                         hipStream_t stream);

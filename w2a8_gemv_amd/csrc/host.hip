@@ -42,6 +42,7 @@ int current_device(DeviceInfo *out) {
         info.id = dev;
         info.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
         info.xcds = 8;
+        info.lds = int64_t(prop.sharedMemPerBlock);
         g_dev[dev] = info;
         g_dev_status[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? W2A8_OK : W2A8_ERR_ARCH;
         g_dev_known[dev] = true;
@@ -54,6 +55,20 @@ namespace {
 std::atomic<int> g_gemm_mode{0};
 std::mutex g_policy_mu;
 GemvPolicy g_policy = {4, 6, 8, 256, 48};
+
+// The forced plan of the current knobs for a strip of KT tiles, if any
+// (launch fields WK, SG, RUN, unroll); false for the automatic plan.
+bool forced_plan(const GemvPolicy &p, int64_t KT, GemvLaunch *a) {
+    if (!p.force_kernel) return false;
+    const int64_t SG = std::min<int64_t>(p.force_sg, KT);
+    const int64_t ktw = ceil_div(KT, SG);
+    const int64_t WK = std::min<int64_t>(p.force_wk, ktw);
+    a->SG = int(SG);
+    a->WK = int(WK);
+    a->RUN = int(ceil_div(ktw, WK));
+    a->unroll = p.force_depth;
+    return true;
+}
 }  // namespace
 
 int gemm_kernel_mode() { return g_gemm_mode.load(std::memory_order_relaxed); }
@@ -140,6 +155,41 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
     *run = int(R);
     const int u = R <= 4 ? 2 : R <= 8 ? 4 : 8;
     *unroll = std::min(u, p.unroll);
+}
+
+// Ring-kernel plan (K a multiple of 16): plain reads of this device reach
+// their best rate with ~10-12 MB in flight spread over all CUs (about four
+// waves per CU with 8-12 KiB each), and each wave's throughput is bounded by
+// its own ring (loads in flight / memory latency), so the plan aims for
+// roughly a thousand or more evenly loaded waves:
+//  * at least two strips per CU: one single-wave workgroup per whole strip
+//    (no combine at all), ring depth 4 for strips of 32 tiles or more, else 8;
+//  * long strips (KT >= split_min_tiles): single-wave workgroups with the
+//    k-range split so that the grid has about 3.75 waves per CU, combined
+//    with one atomic per row; depth 8 for runs of 24 tiles or more, else 4;
+//  * otherwise: 8-wave workgroups over whole strips, depth 4 (6 for strips of
+//    40 tiles or more).
+// Measured on MI355X (cold, per-launch): within 2% of the best of a sweep of
+// every (waves, splits, depth) on each of the 12 workload shapes; e.g.
+// 55296 x 5120 12.7 us (batch kernel 13.7), 5120 x 27648 8.1 us (8.9),
+// 13824 x 2560 4.0 us (4.3), 2560 x 6912 3.58 us (3.78).
+void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, int *sg,
+                    int *run, int *depth) {
+    int64_t WK = 8, SG = 1, D = KT >= 40 ? 6 : 4;
+    if (NS >= 2 * int64_t(cus)) {
+        WK = 1;
+        D = KT >= 32 ? 4 : 8;
+    } else if (KT >= p.split_min_tiles && KT >= 2) {
+        WK = 1;
+        SG = std::max<int64_t>(2, std::min<int64_t>(KT / 4, (int64_t(cus) * 15 / 4 + NS / 2) / NS));
+        SG = std::min(SG, KT);
+        D = ceil_div(KT, SG) >= 24 ? 8 : 4;
+    }
+    WK = std::min(WK, ceil_div(KT, SG));
+    *wk = int(WK);
+    *sg = int(SG);
+    *run = int(ceil_div(ceil_div(KT, SG), WK));
+    *depth = int(D);
 }
 
 // Few activation rows: the GEMV plan with runs of at most 8 tiles (one
@@ -356,9 +406,41 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
-    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
-    a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
-    hipError_t e = launch_gemv(a, static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (forced_plan(pol, a.KT, &a)) {
+        const int run_max = pol.force_kernel == 1 ? 32 : pol.force_kernel == 2 ? 64 : 1 << 30;
+        if (a.RUN > run_max) return W2A8_ERR_VALUE;
+        if (pol.force_kernel >= 3 && (K & 15) != 0) return W2A8_ERR_VALUE;
+        a.DXOK = pol.force_dx;
+        if (pol.force_kernel == 2 &&
+            int64_t(gemv_ring_lds_bytes(a, pol.force_dx && (K & 15) == 0)) > dev.lds)
+            return W2A8_ERR_VALUE;
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        if (pol.force_kernel == 3) {
+            // whole strips per wave: force_wk waves per workgroup, force_sg
+            // strips per wave
+            a.WK = pol.force_wk;
+            e = (K & 15) != 0 ? hipErrorInvalidValue
+                              : launch_gemv_strips(a, pol.force_depth, pol.force_sg, st);
+        } else if (pol.force_kernel == 1) {
+            e = launch_gemv(a, st);
+        } else if (pol.force_kernel >= 5) {
+            // row slices: 2, 4 or 8 per strip (kernels 5, 6, 7)
+            e = launch_gemv_rows_slice(a, pol.force_depth, 1 << (pol.force_kernel - 4), st);
+        } else {
+            e = launch_gemv_ring(a, pol.force_depth, pol.force_dx != 0, pol.force_kernel == 4, st);
+        }
+    } else if ((K & 15) == 0) {
+        int depth = 4;
+        gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
+        a.unroll = depth;
+        e = launch_gemv_ring(a, depth, true, false, static_cast<hipStream_t>(stream));
+    } else {
+        // ragged K: the batch kernel (activations staged through LDS)
+        gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+        a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
+        e = launch_gemv(a, static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 
@@ -604,18 +686,57 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
         !(unroll == 2 || unroll == 4 || unroll == 8) || krange_tiles < 1 || krange_tiles > 256 ||
         split_min_tiles < 1)
         return W2A8_ERR_VALUE;
-    set_gemv_policy(GemvPolicy{wg_per_cu, tiles_per_wave, unroll, krange_tiles, split_min_tiles});
+    GemvPolicy p = gemv_policy();
+    p.wg_per_cu = wg_per_cu;
+    p.tiles_per_wave = tiles_per_wave;
+    p.unroll = unroll;
+    p.krange_tiles = krange_tiles;
+    p.split_min_tiles = split_min_tiles;
+    set_gemv_policy(p);
     return W2A8_OK;
 }
 
-int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *waves_per_wg, int *wgs_per_strip,
-                   int *unroll) {
-    if (!waves_per_wg || !wgs_per_strip || !unroll) return W2A8_ERR_NULL;
+int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int depth,
+                         int direct_x) {
+    GemvPolicy p = gemv_policy();
+    if (kernel == 0) {
+        p.force_kernel = p.force_wk = p.force_sg = p.force_depth = p.force_dx = 0;
+        set_gemv_policy(p);
+        return W2A8_OK;
+    }
+    if (kernel < 0 || kernel > 7 || waves_per_wg < 1 || waves_per_wg > 16 || wgs_per_strip < 1 ||
+        wgs_per_strip > 4096 || (direct_x != 0 && direct_x != 1))
+        return W2A8_ERR_VALUE;
+    const bool ok = kernel == 1 ? (depth == 2 || depth == 4 || depth == 8)
+                                : (depth == 2 || depth == 4 || depth == 6 || depth == 8 ||
+                                   depth == 12);
+    if (!ok || (kernel == 1 && direct_x && depth == 8) || (kernel >= 4 && !direct_x) ||
+        (kernel >= 5 && depth == 2))
+        return W2A8_ERR_VALUE;
+    p.force_kernel = kernel;
+    p.force_wk = waves_per_wg;
+    p.force_sg = wgs_per_strip;
+    p.force_depth = depth;
+    p.force_dx = direct_x;
+    set_gemv_policy(p);
+    return W2A8_OK;
+}
+
+int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg,
+                   int *wgs_per_strip, int *depth) {
+    if (!kernel || !waves_per_wg || !wgs_per_strip || !depth) return W2A8_ERR_NULL;
     if (!nk_ok(N, K) || cus < 1) return W2A8_ERR_SHAPE;
     const int64_t NS = round_up(N, kTileRows) / kTileRows;
     const int64_t KT = round_up(K, kTileK) / kTileK;
     int run = 0;
-    gemv_plan(gemv_policy(), NS, KT, cus, waves_per_wg, wgs_per_strip, &run, unroll);
+    const GemvPolicy pol = gemv_policy();
+    if (K % 16 == 0) {
+        *kernel = 2;
+        gemv_ring_plan(pol, NS, KT, cus, waves_per_wg, wgs_per_strip, &run, depth);
+    } else {
+        *kernel = 1;
+        gemv_plan(pol, NS, KT, cus, waves_per_wg, wgs_per_strip, &run, depth);
+    }
     return W2A8_OK;
 }
 

@@ -369,28 +369,16 @@ int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q, fl
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 
-// ---------------------------------------------------------------------------
-// a4..a7: GEMV (device)
-// ---------------------------------------------------------------------------
-int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32_t *y_i32,
-              const float *s_a, float s_w, float *y_f32, void *workspace, int64_t ws_bytes,
-              void *stream) {
-    if (!w_packed || !x) return W2A8_ERR_NULL;
-    if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
-    if (y_f32 && !s_a) return W2A8_ERR_NULL;
-    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
-    const GemvPolicy pol = gemv_policy();
-    const bool need_ws = gemv_may_split(round_up(K, kTileK) / kTileK, pol);
-    if (need_ws && !workspace) return W2A8_ERR_NULL;
-    if (!aligned(w_packed, 16) || !aligned(x, 16) || (y_i32 && !aligned(y_i32, 16)) ||
-        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)) ||
-        (need_ws && !aligned(workspace, 16)))
-        return W2A8_ERR_ALIGN;
-    if (need_ws && ws_bytes < 8 * round_up(N, kTileRows)) return W2A8_ERR_BUFSIZE;
-    DeviceInfo dev;
-    int st = current_device(&dev);
-    if (st != W2A8_OK) return st;
+}  // extern "C"
 
+namespace {
+
+// Plans and enqueues one GEMV whose arguments have been validated; `ws` holds
+// the split-k combining words (zero on entry and on exit), or is null when
+// no plan under `pol` splits a strip.
+int gemv_enqueue(const GemvPolicy &pol, const DeviceInfo &dev, const void *w_packed,
+                 const int8_t *x, int64_t N, int64_t K, int32_t *y_i32, const float *s_a,
+                 float s_w, float *y_f32, uint64_t *ws, void *stream) {
     const int64_t Np = round_up(N, kTileRows);
     GemvLaunch a;
     a.wp = static_cast<const uint32_t *>(w_packed);
@@ -401,7 +389,7 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
     a.y_f32 = y_f32;
     a.sa = s_a;
     a.sw = s_w;
-    a.ws_row = static_cast<uint64_t *>(workspace);
+    a.ws_row = ws;
     a.N = int(N);
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
@@ -442,6 +430,36 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
         e = launch_gemv(a, static_cast<hipStream_t>(stream));
     }
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+// ---------------------------------------------------------------------------
+// a4..a7: GEMV (device)
+// ---------------------------------------------------------------------------
+int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32_t *y_i32,
+              const float *s_a, float s_w, float *y_f32, void *workspace, int64_t ws_bytes,
+              void *stream) {
+    if (!w_packed || !x) return W2A8_ERR_NULL;
+    if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
+    if (y_f32 && !s_a) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    const GemvPolicy pol = gemv_policy();
+    const bool need_ws = gemv_may_split(round_up(K, kTileK) / kTileK, pol);
+    if (need_ws && !workspace) return W2A8_ERR_NULL;
+    if (!aligned(w_packed, 16) || !aligned(x, 16) || (y_i32 && !aligned(y_i32, 16)) ||
+        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)) ||
+        (need_ws && !aligned(workspace, 16)))
+        return W2A8_ERR_ALIGN;
+    if (need_ws && ws_bytes < 8 * round_up(N, kTileRows)) return W2A8_ERR_BUFSIZE;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+
+    return gemv_enqueue(pol, dev, w_packed, x, N, K, y_i32, s_a, s_w, y_f32,
+                        static_cast<uint64_t *>(workspace), stream);
 }
 
 // Fused linear layer for one token: quant_act_int8 + w2a8_gemv (fp32

@@ -64,7 +64,8 @@ enum w2a8_status {
     W2A8_ERR_BUFSIZE = 5,   /* a packed or workspace buffer is too small      */
     W2A8_ERR_NODEVICE = 6,  /* no HIP device / device query failed            */
     W2A8_ERR_ARCH = 7,      /* the current device is not gfx950               */
-    W2A8_ERR_LAUNCH = 8     /* the kernel launch was rejected by the runtime  */
+    W2A8_ERR_LAUNCH = 8,    /* the kernel launch was rejected by the runtime  */
+    W2A8_ERR_SCRATCH = 9    /* w2a8_gemv_noalloc: shape beyond its scratch    */
 };
 
 /* Version of the packed weight layout below; stored packed weights are only
@@ -181,6 +182,27 @@ int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q,
 int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K,
               int32_t *y_i32, const float *s_a, float s_w, float *y_f32,
               void *workspace, int64_t ws_bytes, void *stream);
+
+/* Static scratch of w2a8_gemv_noalloc, in bytes (per device). */
+#define W2A8_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+/* w2a8_gemv without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments (minus workspace and ws_bytes), the
+ * same plans and kernels, bit-identical results.  Where w2a8_gemv would use
+ * its workspace (w2a8_workspace_bytes(1, N, K) > 0), this call uses a
+ * static device array of the library of W2A8_NOALLOC_SCRATCH_BYTES bytes per
+ * device (one 64-bit word per padded output row: N up to 131072 rows then),
+ * held until the process ends; larger N is rejected with W2A8_ERR_SCRATCH
+ * before any device work.  The call allocates nothing.  The array is zero
+ * when the library loads and every complete call leaves it zero; the first
+ * call on a device also clears it with a small kernel on `stream` when the
+ * stream is not capturing.  Every call on one device shares the one array:
+ * calls that may overlap on a device (other streams, other host threads)
+ * race and must not be issued. */
+int w2a8_gemv_noalloc(const void *w_packed, const int8_t *x, int64_t N, int64_t K,
+                      int32_t *y_i32, const float *s_a, float s_w, float *y_f32,
+                      void *stream);
 
 /* Whole linear layer for one token, in one launch: the result of
  * quant_act_int8 (M = 1) followed by w2a8_gemv with its fp32 epilogue,

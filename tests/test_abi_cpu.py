@@ -22,7 +22,7 @@ import w2a8_gemv_amd as w2a8
 from conftest import ROOT
 
 ST = {"OK": 0, "NULL": 1, "SHAPE": 2, "ALIGN": 3, "VALUE": 4, "BUFSIZE": 5, "NODEVICE": 6,
-      "ARCH": 7}
+      "ARCH": 7, "SCRATCH": 9}
 F = ctypes.c_float
 FAKE = 0x10000          # 16-byte aligned stand-in, never dereferenced
 FAKE_ODD = 0x10004      # 4-byte aligned only
@@ -41,7 +41,7 @@ def _declared_functions():
 def test_header_status_codes_match_library():
     text = open(os.path.join(ROOT, "include", "w2a8.h")).read()
     codes = dict((k, int(v)) for k, v in re.findall(r"W2A8_(?:ERR_)?(\w+)\s*=\s*(\d+)", text))
-    assert codes["OK"] == 0 and len(codes) == 9
+    assert codes["OK"] == 0 and len(codes) == 10
     L = w2a8.lib()
     for v in codes.values():
         assert L.w2a8_status_str(v) and L.w2a8_status_str(v) != b"unknown status"
@@ -53,7 +53,8 @@ def test_library_exports_every_declared_symbol():
     expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
-                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemm",
+                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemm", "w2a8_tune_gemv_force",
+                "w2a8_gemv_noalloc",
                 "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped",
                 "w2a4_act_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv"}
     assert expected.issubset(set(names)), set(names) ^ expected
@@ -198,6 +199,29 @@ def test_gemv_validation():
     assert _gemv(yf=FAKE_ODD) == ST["ALIGN"]
     assert _gemv(sa=FAKE + 2) == ST["ALIGN"]
     assert _gemv(wsb=w2a8.workspace_bytes(1, 64, KS) - 1) == ST["BUFSIZE"]
+
+
+def test_gemv_noalloc_validation():
+    L = w2a8.lib()
+
+    def g(**kw):
+        a = dict(wp=FAKE, x=FAKE, N=64, K=KS, y=FAKE, sa=FAKE, sw=1.0, yf=FAKE)
+        a.update(kw)
+        return L.w2a8_gemv_noalloc(a["wp"], a["x"], a["N"], a["K"], a["y"], a["sa"], F(a["sw"]),
+                                   a["yf"], None)
+    assert g(wp=None) == ST["NULL"]
+    assert g(x=None) == ST["NULL"]
+    assert g(y=None, yf=None) == ST["NULL"]
+    assert g(sa=None) == ST["NULL"]
+    assert g(N=0) == ST["SHAPE"]
+    assert g(K=1048448 + 1) == ST["SHAPE"]
+    assert g(x=FAKE + 1) == ST["ALIGN"]
+    assert g(yf=FAKE_ODD) == ST["ALIGN"]
+    # scratch: 1 MiB of 8-byte words, one per padded row, needed when K splits
+    assert g(N=131072) not in (ST["SCRATCH"], ST["NULL"], ST["ALIGN"], ST["SHAPE"])
+    assert g(N=131073) == ST["SCRATCH"]
+    assert g(N=131073, K=2560) not in (ST["SCRATCH"], ST["NULL"], ST["ALIGN"], ST["SHAPE"])
+    assert L.w2a8_status_str(ST["SCRATCH"]) != b"unknown status"
 
 
 def _gemm(**kw):

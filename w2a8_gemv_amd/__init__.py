@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
-    "w2a8_gemv", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
+    "w2a8_gemv", "w2a8_gemv_noalloc", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
     "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "DEFAULT_GEMV_POLICY",
     "tune_gemm",
     "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
@@ -73,6 +73,8 @@ def lib():
         L.quant_act_int8.restype = I32
         L.w2a8_gemv.argtypes = [P, P, I64, I64, P, P, F32, P, P, I64, P]
         L.w2a8_gemv.restype = I32
+        L.w2a8_gemv_noalloc.argtypes = [P, P, I64, I64, P, P, F32, P, P]
+        L.w2a8_gemv_noalloc.restype = I32
         L.w2a8_gemm.argtypes = [P, P, I64, I64, I64, P, P, F32, P, P, I64, P]
         L.w2a8_gemm.restype = I32
         L.w2a8_linear_gemv.argtypes = [P, P, I64, I64, F32, P, P, P, I64, P]
@@ -259,6 +261,28 @@ def w2a8_gemv(w_packed, x, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
                            ctypes.c_float(s_w), _ptr(y_f32), _ptr(ws),
                            0 if ws is None else ws.numel(), _stream_handle(stream)),
            "w2a8_gemv")
+
+
+def w2a8_gemv_noalloc(w_packed, x, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
+                      stream=None):
+    """Raw C-ABI call: the GEMV with the library's static scratch instead of a
+    workspace (allocates nothing); returns nothing."""
+    _need(w_packed, "w_packed", torch.uint8, "cuda")
+    _need(x, "x", torch.int8, "cuda")
+    if x.numel() != K:
+        raise ValueError("x must have K elements")
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than packed_bytes(N, K)")
+    for t, nm, dt in ((y_i32, "y_i32", torch.int32), (y_f32, "y_f32", torch.float32)):
+        if t is not None:
+            _need(t, nm, dt, "cuda")
+            if t.numel() != N:
+                raise ValueError(f"{nm} must have N elements")
+    if s_a is not None:
+        _need(s_a, "s_a", torch.float32, "cuda")
+    _check(lib().w2a8_gemv_noalloc(_ptr(w_packed), _ptr(x), N, K, _ptr(y_i32), _ptr(s_a),
+                                   ctypes.c_float(s_w), _ptr(y_f32), _stream_handle(stream)),
+           "w2a8_gemv_noalloc")
 
 
 def w2a8_gemm(w_packed, x, M, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,

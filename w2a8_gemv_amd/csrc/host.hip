@@ -237,6 +237,7 @@ const char *w2a8_status_str(int status) {
     case W2A8_ERR_NODEVICE: return "no HIP device available";
     case W2A8_ERR_ARCH: return "current device is not gfx950";
     case W2A8_ERR_LAUNCH: return "kernel launch failed";
+    case W2A8_ERR_SCRATCH: return "shape needs more than the static scratch of w2a8_gemv_noalloc";
     default: return "unknown status";
     }
 }
@@ -371,6 +372,49 @@ int quant_act_int8(const uint16_t *x_bf16, int64_t M, int64_t K, int8_t *x_q, fl
 
 }  // extern "C"
 
+// Split-k combining words of w2a8_gemv_noalloc: one 64-bit word per padded
+// output row, W2A8_NOALLOC_SCRATCH_BYTES in all, one copy per device for the
+// life of the process.  Zero when the code object loads; every complete call
+// leaves the words it used zero again.  In host code `scratch` names only a
+// host-side stand-in: the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint64_t scratch[W2A8_NOALLOC_SCRATCH_BYTES / 8];
+
+namespace {
+
+std::mutex g_scratch_mu;
+uint64_t *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+__global__ void clear_words_kernel(uint64_t *p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
+
+// The device address of `scratch` on device `dev` (current), taken once per
+// device.  The first call on a device also clears the array with a fill
+// kernel on `stream` (not a memset: callers may be capturing a graph), unless
+// the stream is capturing, in which case the load-time zero stands.
+int scratch_words(int dev, hipStream_t stream, uint64_t **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return W2A8_ERR_LAUNCH;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return W2A8_ERR_LAUNCH;
+        if (cs == hipStreamCaptureStatusNone) {
+            hipLaunchKernelGGL(clear_words_kernel, dim3(64), dim3(256), 0, stream,
+                               static_cast<uint64_t *>(p), int64_t(W2A8_NOALLOC_SCRATCH_BYTES / 8));
+            if (hipGetLastError() != hipSuccess) return W2A8_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = static_cast<uint64_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return W2A8_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // Plans and enqueues one GEMV whose arguments have been validated; `ws` holds
@@ -460,6 +504,32 @@ int w2a8_gemv(const void *w_packed, const int8_t *x, int64_t N, int64_t K, int32
 
     return gemv_enqueue(pol, dev, w_packed, x, N, K, y_i32, s_a, s_w, y_f32,
                         static_cast<uint64_t *>(workspace), stream);
+}
+
+// GEMV with its split-k combining words in the library's static scratch
+// array: no workspace argument and no allocation.
+int w2a8_gemv_noalloc(const void *w_packed, const int8_t *x, int64_t N, int64_t K,
+                      int32_t *y_i32, const float *s_a, float s_w, float *y_f32, void *stream) {
+    if (!w_packed || !x) return W2A8_ERR_NULL;
+    if (!y_i32 && !y_f32) return W2A8_ERR_NULL;
+    if (y_f32 && !s_a) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K)) return W2A8_ERR_SHAPE;
+    const GemvPolicy pol = gemv_policy();
+    const bool need_ws = gemv_may_split(round_up(K, kTileK) / kTileK, pol);
+    if (need_ws && 8 * round_up(N, kTileRows) > W2A8_NOALLOC_SCRATCH_BYTES)
+        return W2A8_ERR_SCRATCH;
+    if (!aligned(w_packed, 16) || !aligned(x, 16) || (y_i32 && !aligned(y_i32, 16)) ||
+        (y_f32 && !aligned(y_f32, 16)) || (s_a && !aligned(s_a, 4)))
+        return W2A8_ERR_ALIGN;
+    DeviceInfo dev;
+    int st = current_device(&dev);
+    if (st != W2A8_OK) return st;
+    uint64_t *ws = nullptr;
+    if (need_ws) {
+        st = scratch_words(dev.id, static_cast<hipStream_t>(stream), &ws);
+        if (st != W2A8_OK) return st;
+    }
+    return gemv_enqueue(pol, dev, w_packed, x, N, K, y_i32, s_a, s_w, y_f32, ws, stream);
 }
 
 // Fused linear layer for one token: quant_act_int8 + w2a8_gemv (fp32

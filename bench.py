@@ -291,8 +291,10 @@ def kernel_times(torch, lib, shape, reps, stream, rounds=5):
 
 # Plain-read configurations tried as the floor of each matrix: (waves per CU,
 # width in bytes per lane, loads in flight per wave, non-temporal, strided).
-READ_FLOOR_CONFIGS = [(4, 16, 8, 1, 0), (8, 16, 8, 1, 0), (4, 16, 16, 1, 0), (8, 16, 16, 1, 0),
-                      (16, 16, 8, 1, 0), (8, 16, 8, 1, 1), (16, 16, 4, 1, 0)]
+# The best configurations of the --read-ceiling sweep on 35 MB and 71 MB
+# (strided and contiguous), and a few neighbours.
+READ_FLOOR_CONFIGS = [(4, 16, 12, 1, 1), (4, 16, 8, 1, 1), (3, 16, 12, 1, 1), (4, 16, 12, 1, 0),
+                      (4, 16, 8, 1, 0), (12, 16, 4, 1, 0), (24, 8, 12, 1, 0), (8, 8, 8, 1, 1)]
 
 
 def read_floor_times(torch, readref, shape, stream, rounds=5, configs=READ_FLOOR_CONFIGS):
@@ -780,14 +782,30 @@ def traffic_summary():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(shapes, seconds=10.0):
-    """The oracle (plain C, one thread) on the same eight GEMVs, repeated for
-    about `seconds`; also checks the GPU's last outputs on sampled rows."""
+def host_cpu_info():
+    """nproc and the CPU model name of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "model_name": model}
+
+
+def cpu_baseline(shapes, seconds=10.0, max_threads=16):
+    """The oracle (plain C) on the same eight GEMVs, repeated for about
+    `seconds` per leg: one thread, then all cores (the same C product on
+    contiguous blocks of weight rows, one host thread each, at most
+    `max_threads`, a one-GPU machine's CPU share).  Also checks the GPU's last
+    outputs on sampled rows."""
     import numpy as np
 
     import oracle
     import synth
-    import w2a8_gemv_amd as w2a8
 
     ws = []
     for s in shapes:
@@ -801,22 +819,36 @@ def cpu_baseline(shapes, seconds=10.0):
         ref = oracle.gemm_i32(s.x_host, w[rows])
         got = s.y.cpu().numpy()[rows]
         ok = ok and bool(np.array_equal(ref, got))
-    del w2a8
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        for s, w in zip(shapes, ws):
-            oracle.gemm_i32(s.x_host, w)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    total = sum(s.nbytes for s in shapes) * reps
-    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the 8 sweep GEMVs in full (int8 weights unpacked), repeated {reps} times "
-                      f"({dt:.1f} s), single thread; GB/s counts the same algorithmic bytes "
-                      f"N*K/4+K+4N per GEMV", "ms_per_sweep": round(dt / reps * 1e3, 3),
-            "gpu_rows_match": ok}
+
+    def leg(threads):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            for s, w in zip(shapes, ws):
+                if threads == 1:
+                    oracle.gemm_i32(s.x_host, w)
+                else:
+                    oracle.gemm_i32_threads(s.x_host, w, threads)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return reps, dt, sum(s.nbytes for s in shapes) * reps / dt / 1e9
+
+    info = host_cpu_info()
+    nthreads = max(1, min(max_threads, info["nproc"] or 1))
+    r1, d1, v1 = leg(1)
+    rn, dn, vn = leg(nthreads)
+    return {"value": round(v1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the 8 sweep GEMVs in full (int8 weights unpacked), repeated {r1} times "
+                      f"({d1:.1f} s), single thread; GB/s counts the same algorithmic bytes "
+                      f"N*K/4+K+4N per GEMV", "ms_per_sweep": round(d1 / r1 * 1e3, 3),
+            "all_cores": {"value": round(vn, 4), "unit": "GB/s", "cores": nthreads,
+                          "sample": f"the same 8 GEMVs, repeated {rn} times ({dn:.1f} s), the "
+                                    f"oracle's C product on {nthreads} host threads, each over "
+                                    f"its own block of weight rows",
+                          "ms_per_sweep": round(dn / rn * 1e3, 3)},
+            "host": info, "gpu_rows_match": ok}
 
 
 def load_readref():
@@ -931,8 +963,14 @@ def main():
     per = []
     for s in ([] if args.no_detail else shapes):
         solo, _ = make_shapes(torch, w2a8, synth, [(s.n, s.k, s.seed, s.sparse)], args.mode, dev)
-        per.append(shape_detail(torch, lib, readref, solo[0], stream))
+        p = shape_detail(torch, lib, readref, solo[0], stream)
         del solo
+        warm, _ = make_shapes(torch, w2a8, synth, [(s.n, s.k, s.seed, s.sparse)], "warm", dev)
+        wt = sorted(kernel_times(torch, lib, warm[0], 24, stream))
+        p["warm_median_us"] = round(wt[len(wt) // 2], 3)
+        p["warm_GBps"] = round(s.nbytes / p["warm_median_us"] / 1e3, 1)
+        del warm
+        per.append(p)
         torch.cuda.empty_cache()
     out = {
         "metric": METRIC,
@@ -975,6 +1013,7 @@ def main():
             "per_shape_kernel_times": per,
             "per_shape_method": "each shape on its own rotation of >= 700 MB of weight copies "
                                 "(cold mode); a graph of one launch per copy (at least 24), "
+                                "warm: 24 launches on one copy (L2 / Infinity Cache resident), "
                                 "device time per launch from two events per replay, median "
                                 "of 5 replays (includes the graph's inter-node gaps). "
                                 "read_floor: the plain-read kernel over the same rotation, "
@@ -1002,6 +1041,24 @@ def main():
                 del shp
                 torch.cuda.empty_cache()
         out["detail"]["large_shapes"] = large
+        # the pass bar: the two largest matrices, cold, against 8 TB/s and against the
+        # best plain read of the same bytes on the same rotation
+        out["largest_shapes_cold"] = [
+            {"nk": f"{p['n']}x{p['k']}", "us": p["median_us"], "GBps": p["GBps"],
+             "pct_peak": p["pct_peak"],
+             "read_floor_us": p.get("read_floor", {}).get("median_us"),
+             "over_read_floor": p.get("read_floor", {}).get("gemv_over_floor")}
+            for p in large if p["mode"] == "cold"]
+        # one GPU's share of each large matrix over 8 GPUs (cold)
+        shard = []
+        for (n, k), seed in zip(synth.SHARD_SHAPES, synth.SHARD_SEEDS):
+            shp, sl = make_shapes(torch, w2a8, synth, [(n, k, seed, True)], "cold", dev)
+            p = shape_detail(torch, lib, readref, shp[0], stream)
+            p.update({"rotation_copies": sl, "plan": list(w2a8.gemv_plan(n, k, cus))})
+            shard.append(p)
+            del shp
+            torch.cuda.empty_cache()
+        out["detail"]["shard_shapes"] = shard
         out["detail"]["device_copy_GBps_read_plus_write"] = round(copy_bandwidth(torch, dev), 1)
         out["detail"]["gemm"] = gemm_extras(torch, w2a8, synth, lib, stream, cus)
         out["detail"]["gemm_peak_int8_TOPS"] = PEAK_INT8_TOPS

@@ -30,6 +30,9 @@ SWEEP_SHAPES = [
 ]
 # The two further shapes the kernel source specialises (same page, "限制与注意事项").
 LARGE_SHAPES = [(5120, 27648), (55296, 5120)]
+# One GPU's share of each large matrix split over 8 GPUs: 55296 rows / 8, and
+# 27648 along K / 8 (same value distribution as the large shapes).
+SHARD_SHAPES = [(6912, 5120), (5120, 3456)]
 # Prefill shapes for the batched product.
 GEMM_SHAPES = [(13824, 2560), (2560, 6912)]
 GEMM_MS = [8, 128, 512]
@@ -139,6 +142,7 @@ def linear_case(m: int, n: int, k: int, seed: int, outlier_p: float = 0.01,
 SEED_SMALL = 1                      # N = K = 2560
 SWEEP_SEEDS = list(range(11, 19))   # one per sweep shape, in order
 LARGE_SEEDS = [21, 22]
+SHARD_SEEDS = [51, 52]
 LINEAR_SEEDS = {1: 31, 128: 32}
 GEMM_SEEDS = {  # shape-major, then M
     (GEMM_SHAPES[0], 8): 41, (GEMM_SHAPES[0], 128): 42, (GEMM_SHAPES[0], 512): 43,

@@ -30,7 +30,12 @@ def _quant_dev(bits):
 
 
 @pytest.mark.parametrize("M,K", [(1, 2560), (128, 2560), (1, 27648), (3, 100), (5, 1),
-                                 (2, 7), (4, 4000), (1, 8), (17, 16)])
+                                 (2, 7), (4, 4000), (1, 8), (17, 16),
+                                 # one wave per row, the row in registers: 1..16 chunks of 8
+                                 # per lane, partial last chunk groups, 1, 2 and 4 rows per
+                                 # workgroup (M against 256 CUs), and K just past the limit
+                                 (1, 8192), (9, 520), (7, 512), (600, 4096), (1100, 1024),
+                                 (33, 8200), (3, 6912), (512, 2560)])
 def test_quant_matches_oracle(M, K):
     xb, _ = synth.linear_case(M, 1, K, seed=M * 7 + K)
     q, sa = _quant_dev(xb)
@@ -51,6 +56,18 @@ def test_quant_worked_examples_and_zero_rows():
     assert q[0].tolist() == [127, -64, 32, 0]
     assert q[2].tolist() == [127, 62, -62, 32]
     assert q[3].tolist() == [0, 0, 0, 0] and sa[3] == 0.0
+
+
+def test_quant_zero_rows_register_path():
+    # zero rows between nonzero ones, K a multiple of 8 (one wave per row)
+    xb, _ = synth.linear_case(6, 1, 48, seed=5)
+    xb[1] = 0
+    xb[4] = 0x8000          # negative zeros
+    q, sa = _quant_dev(xb)
+    oq, osa = oracle.quant_act(xb)
+    np.testing.assert_array_equal(q, oq)
+    np.testing.assert_array_equal(sa, osa)
+    assert np.all(q[1] == 0) and np.all(q[4] == 0) and sa[1] == 0.0 and sa[4] == 0.0
 
 
 def _linear_ref(xb, wq, sw):

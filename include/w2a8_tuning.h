@@ -37,18 +37,16 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
  * grouped and W2A4 GEMVs keep their automatic plans).  kernel 0 restores the
  * automatic plan (other arguments ignored).  kernel 1: the batch kernel with
  * `waves_per_wg` (1..16) waves per workgroup, `wgs_per_strip` (1..4096)
- * workgroups per 32-row strip (at most one per k-tile) and two load batches
- * of `depth` (2, 4 or 8) tiles; kernel 2: the ring kernel with `depth` (2, 4,
- * 6, 8 or 12) tiles in flight per wave; kernel 3: whole strips per wave
- * (`wgs_per_strip` is then strips per wave; K a multiple of 16); kernel 4:
- * the ring kernel with the strip's tiles interleaved over its waves (needs
- * `direct_x`, K a multiple of 16).  `direct_x` (0 or 1) loads each
- * tile's activations next to its weights instead of staging the wave's run
- * in LDS (K a multiple of 16; not with batch 8).  w2a8_gemv returns
- * W2A8_ERR_VALUE for a forced plan whose runs exceed 32 tiles (batch kernel)
- * or 64 tiles (ring kernel) per wave, or whose activation staging needs more
- * LDS than a workgroup may allocate on the device.  w2a8_workspace_bytes(1, N, K) counts
- * a forced split.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+ * workgroups per 32-row strip (at most one per k-tile), two load batches of
+ * `depth` (2, 4 or 8) tiles, and each tile's activations loaded next to its
+ * weights when `direct_x` is 1 (K a multiple of 16; not with batch 8) instead
+ * of staging the wave's run in LDS.  kernel 2: the ring kernel (K a multiple
+ * of 16) with `depth` (2, 4, 6, 8 or 12) tiles in flight per wave; it always
+ * loads activations next to the weights, so `direct_x` must be 1.
+ * w2a8_gemv returns W2A8_ERR_VALUE for a forced batch plan whose runs exceed
+ * 32 tiles per wave, or a forced ring plan on K not a multiple of 16.
+ * w2a8_workspace_bytes(1, N, K) counts a forced split.  Returns W2A8_OK or
+ * W2A8_ERR_VALUE. */
 int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int depth,
                          int direct_x);
 

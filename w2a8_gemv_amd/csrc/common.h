@@ -40,8 +40,8 @@ struct GemvPolicy {
     int split_min_tiles;  // split a strip over workgroups only if KT >= this
     // Forced plan for measurement sweeps (force_kernel 0: automatic plan).
     // 1: batch kernel with force_wk waves, force_sg workgroups per strip and
-    // load batch force_depth; 2: ring kernel with depth force_depth, direct
-    // activation loads when force_dx.
+    // load batch force_depth, direct activation loads when force_dx; 2: ring
+    // kernel with depth force_depth (activations always loaded directly).
     int force_kernel = 0, force_wk = 0, force_sg = 0, force_depth = 0, force_dx = 0;
 };
 // A consistent copy of the current knobs (taken under a lock: every call
@@ -71,7 +71,6 @@ struct GemvLaunch {
     int SG;       // workgroups (k-ranges) per row strip
     int RUN;      // longest run of tiles of one wave (<= 32)
     int unroll;
-    int TQ = 0, TR = 0;   // ring kernel, interleaved runs: KT = TQ*(SG*WK) + TR
     int DXOK = 0; // plain kernel: at most 5 waves per CU in the grid, so activation chunks may
                   // be loaded directly with the weights (latency-bound grids)
     // Workgroup kernel, set by its launcher so that the kernel divides
@@ -154,16 +153,9 @@ constexpr int64_t kRowsMaxM = 8;
 // workgroup kernel with the fp32 epilogue (gemv.hip).
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream);
 hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
-// Ring-pipelined GEMV (gemv_ring.hip): runs of at most 64 tiles per wave.
-bool gemv_ring_fits(const GemvLaunch &a);
-size_t gemv_ring_lds_bytes(const GemvLaunch &a, bool dx);
-hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, bool dx, bool il, hipStream_t stream);
-// Row slices: 32/slices rows of a strip per workgroup (gemv_ring.hip), K a
-// multiple of 16, slices 2, 4 or 8.
-hipError_t launch_gemv_rows_slice(const GemvLaunch &a, int depth, int slices, hipStream_t stream);
-// Whole strips per wave (gemv_ring.hip), K a multiple of 16.
-hipError_t launch_gemv_strips(const GemvLaunch &a, int depth, int strips_per_wave,
-                              hipStream_t stream);
+// Ring-pipelined GEMV (gemv_ring.hip): K a multiple of 16, WK <= 16 waves
+// per workgroup, depth 2, 4, 6, 8 or 12 tiles in flight per wave.
+hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
                         hipStream_t stream);

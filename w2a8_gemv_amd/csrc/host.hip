@@ -440,33 +440,20 @@ int gemv_enqueue(const GemvPolicy &pol, const DeviceInfo &dev, const void *w_pac
     a.NS = int(Np / kTileRows);
     hipError_t e;
     if (forced_plan(pol, a.KT, &a)) {
-        const int run_max = pol.force_kernel == 1 ? 32 : pol.force_kernel == 2 ? 64 : 1 << 30;
-        if (a.RUN > run_max) return W2A8_ERR_VALUE;
-        if (pol.force_kernel >= 3 && (K & 15) != 0) return W2A8_ERR_VALUE;
-        a.DXOK = pol.force_dx;
-        if (pol.force_kernel == 2 &&
-            int64_t(gemv_ring_lds_bytes(a, pol.force_dx && (K & 15) == 0)) > dev.lds)
-            return W2A8_ERR_VALUE;
         const hipStream_t st = static_cast<hipStream_t>(stream);
-        if (pol.force_kernel == 3) {
-            // whole strips per wave: force_wk waves per workgroup, force_sg
-            // strips per wave
-            a.WK = pol.force_wk;
-            e = (K & 15) != 0 ? hipErrorInvalidValue
-                              : launch_gemv_strips(a, pol.force_depth, pol.force_sg, st);
-        } else if (pol.force_kernel == 1) {
+        if (pol.force_kernel == 1) {
+            if (a.RUN > 32) return W2A8_ERR_VALUE;
+            a.DXOK = pol.force_dx;
             e = launch_gemv(a, st);
-        } else if (pol.force_kernel >= 5) {
-            // row slices: 2, 4 or 8 per strip (kernels 5, 6, 7)
-            e = launch_gemv_rows_slice(a, pol.force_depth, 1 << (pol.force_kernel - 4), st);
         } else {
-            e = launch_gemv_ring(a, pol.force_depth, pol.force_dx != 0, pol.force_kernel == 4, st);
+            if ((K & 15) != 0) return W2A8_ERR_VALUE;
+            e = launch_gemv_ring(a, pol.force_depth, st);
         }
     } else if ((K & 15) == 0) {
         int depth = 4;
         gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
         a.unroll = depth;
-        e = launch_gemv_ring(a, depth, true, false, static_cast<hipStream_t>(stream));
+        e = launch_gemv_ring(a, depth, static_cast<hipStream_t>(stream));
     } else {
         // ragged K: the batch kernel (activations staged through LDS)
         gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
@@ -792,15 +779,13 @@ int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int de
         set_gemv_policy(p);
         return W2A8_OK;
     }
-    if (kernel < 0 || kernel > 7 || waves_per_wg < 1 || waves_per_wg > 16 || wgs_per_strip < 1 ||
+    if (kernel < 0 || kernel > 2 || waves_per_wg < 1 || waves_per_wg > 16 || wgs_per_strip < 1 ||
         wgs_per_strip > 4096 || (direct_x != 0 && direct_x != 1))
         return W2A8_ERR_VALUE;
-    const bool ok = kernel == 1 ? (depth == 2 || depth == 4 || depth == 8)
+    const bool ok = kernel == 1 ? (depth == 2 || depth == 4 || depth == 8) && !(direct_x && depth == 8)
                                 : (depth == 2 || depth == 4 || depth == 6 || depth == 8 ||
-                                   depth == 12);
-    if (!ok || (kernel == 1 && direct_x && depth == 8) || (kernel >= 4 && !direct_x) ||
-        (kernel >= 5 && depth == 2))
-        return W2A8_ERR_VALUE;
+                                   depth == 12) && direct_x == 1;
+    if (!ok) return W2A8_ERR_VALUE;
     p.force_kernel = kernel;
     p.force_wk = waves_per_wg;
     p.force_sg = wgs_per_strip;

@@ -60,7 +60,8 @@ enum w2a8_status {
     W2A8_ERR_NULL = 1,      /* a required pointer is NULL                     */
     W2A8_ERR_SHAPE = 2,     /* M, N or K < 1, or above the documented limits  */
     W2A8_ERR_ALIGN = 3,     /* a pointer is not aligned as required           */
-    W2A8_ERR_VALUE = 4,     /* a weight outside {-1,0,1}, or a code 11        */
+    W2A8_ERR_VALUE = 4,     /* a weight outside {-1,0,1}, a code 11, or a
+                               tuning knob / forced plan out of range       */
     W2A8_ERR_BUFSIZE = 5,   /* a packed or workspace buffer is too small      */
     W2A8_ERR_NODEVICE = 6,  /* no HIP device / device query failed            */
     W2A8_ERR_ARCH = 7,      /* the current device is not gfx950               */

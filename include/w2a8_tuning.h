@@ -55,13 +55,24 @@ int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int de
  * still chosen by shape, including the wave-group k-split for small output
  * grids; it never splits K across workgroups), 2 = the general kernel
  * (split-K across workgroups for small outputs) always, 3 = the few-row
- * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8, the
- * automatic choice above that.  The automatic
- * rule, from measurements on MI355X: the few-row kernel for
- * M <= 2 up to 49152 weight tiles and for K not a multiple of 16 (M <= 8);
- * the general kernel for K not a multiple of 16 above that; otherwise the
- * pipelined kernel.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+ * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8, 4 = the
+ * short-batch MFMA ring kernel (the GEMV's weight stream feeding int8 MFMA)
+ * whenever M <= 16 and K is a multiple of 16; other shapes take the
+ * automatic choice.  The automatic rule, from measurements on MI355X: the
+ * few-row kernel for M <= 2 up to 49152 weight tiles and for K not a multiple
+ * of 16 (M <= 8); the ring kernel for the other M <= 8; the general kernel
+ * for K not a multiple of 16 above that; otherwise the pipelined kernel.
+ * Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
+
+/* Forced plan of the short-batch MFMA ring kernel, wherever w2a8_gemm takes
+ * it: `waves_per_wg` (1..16) waves per workgroup splitting a 32-row strip's
+ * k-range, `wgs_per_strip` (1..4096; at most the strip's k-tiles are used)
+ * workgroups per strip, `depth` (2, 4, 6 or 8) tiles in flight per wave.
+ * All three 0 restore the automatic plan.  w2a8_gemm returns W2A8_ERR_VALUE
+ * for a forced plan whose rings need more LDS than a workgroup may allocate
+ * on the device.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+int w2a8_tune_gemm_ring(int waves_per_wg, int wgs_per_strip, int depth);
 
 /* The automatic plan w2a8_gemv would use for (N, K) on a device with `cus`
  * compute units under the current knobs: the kernel (2: the ring kernel, for

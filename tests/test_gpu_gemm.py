@@ -27,6 +27,7 @@ ORACLE_THREADS = max(1, min(16, os.cpu_count() or 1))
 def _restore_gemm_kernel():
     yield
     w2a8.tune_gemm(0)
+    w2a8.tune_gemm_ring(0, 0, 0)
 
 
 def _gemm_dev(wp, xd, M, N, K, sa=None, sw=1.0, want_f32=False):
@@ -167,6 +168,68 @@ def test_gemm_few_rows_fp32_epilogue_and_workspace_reset():
         np.testing.assert_array_equal(yi.cpu().numpy().reshape(M, N), acc)
         np.testing.assert_array_equal(yf.cpu().numpy().reshape(M, N), oracle.epilogue(acc, sa, sw))
         assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
+
+
+# Short-batch MFMA ring kernel (2 <= M <= 16, K a multiple of 16) forced:
+# both activation tile heights (M <= 8 and 9..16), ragged N, k-tile
+# remainders, runs shorter and longer than the ring, split strips.
+RING = [(2, 1, 16), (2, 33, 144), (3, 100, 1040), (5, 64, 2560), (7, 257, 4000), (8, 2560, 6912),
+        (8, 13824, 2560), (9, 31, 272), (12, 200, 10240), (16, 96, 27648), (16, 2560, 2560),
+        (4, 5000, 3200), (11, 640, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", RING)
+def test_gemm_ring_kernel(M, N, K):
+    w2a8.tune_gemm(4)
+    x, w = synth.gemm_case(M, N, K, seed=13 * M + N + 7 * K)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+
+
+@pytest.mark.parametrize("plan", [(1, 1, 2), (1, 7, 8), (4, 3, 4), (8, 1, 6), (16, 2, 2),
+                                  (2, 40, 4), (3, 5, 6), (8, 12, 8)])
+def test_gemm_ring_kernel_plans(plan):
+    """Forced plans: single- and many-wave workgroups, strips split over many
+    workgroups (runs of one tile, empty runs), every depth."""
+    try:
+        w2a8.tune_gemm(4)
+        w2a8.tune_gemm_ring(*plan)
+        for M, N, K in [(4, 200, 3200), (8, 96, 27648), (2, 33, 1008), (16, 64, 6912),
+                        (13, 700, 2560)]:
+            x, w = synth.gemm_case(M, N, K, seed=M + N + K)
+            ws = torch.zeros(max(256, w2a8.workspace_bytes(M, N, K)), dtype=torch.uint8,
+                             device=dev())
+            wp, xd = packed_on_device(w), to_dev(x)
+            lds = plan[0] * plan[2] * 1024 * (2 if M <= 8 else 3)
+            if lds > torch.cuda.get_device_properties(dev()).shared_memory_per_block:
+                # the rings do not fit a workgroup's LDS: refused, nothing launched
+                y = torch.empty(M * N, dtype=torch.int32, device=dev())
+                with pytest.raises(w2a8.W2A8Error):
+                    w2a8.w2a8_gemm(wp, xd, M, N, K, y_i32=y, workspace=ws)
+                continue
+            ref = oracle.gemm_i32(x, w)
+            for _ in range(2):
+                y = torch.empty(M * N, dtype=torch.int32, device=dev())
+                w2a8.w2a8_gemm(wp, xd, M, N, K, y_i32=y, workspace=ws)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(y.cpu().numpy().reshape(M, N), ref)
+                assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
+    finally:
+        w2a8.tune_gemm_ring(0, 0, 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 700, 27648), (15, 333, 3200)])
+def test_gemm_ring_kernel_fp32_epilogue(M, N, K):
+    w2a8.tune_gemm(4)
+    x, w = synth.gemm_case(M, N, K, seed=5 * M + K)
+    rng = np.random.default_rng(8)
+    sa = (rng.random(M, dtype=np.float32) * 0.05 + 1e-3).astype(np.float32)
+    sw = np.float32(0.021)
+    yi, yf = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K, sa=to_dev(sa), sw=float(sw),
+                       want_f32=True)
+    acc = oracle.gemm_i32(x, w)
+    np.testing.assert_array_equal(yi, acc)
+    np.testing.assert_array_equal(yf, oracle.epilogue(acc, sa, sw))
 
 
 @pytest.mark.parametrize("key", list(synth.GEMM_SEEDS.keys()),

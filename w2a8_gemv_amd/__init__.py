@@ -23,7 +23,7 @@ __all__ = [
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemv_noalloc", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
     "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "DEFAULT_GEMV_POLICY",
-    "tune_gemm",
+    "tune_gemm", "tune_gemm_ring",
     "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
     "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
 ]
@@ -98,6 +98,8 @@ def lib():
         L.w2a8_tune_gemv_force.restype = I32
         L.w2a8_tune_gemm.argtypes = [I32]
         L.w2a8_tune_gemm.restype = I32
+        L.w2a8_tune_gemm_ring.argtypes = [I32, I32, I32]
+        L.w2a8_tune_gemm_ring.restype = I32
         L.w2a8_gemv_plan.restype = I32
         if L.w2a8_layout_version() != LAYOUT_VERSION:
             raise RuntimeError("libw2a8.so layout version does not match the binding")
@@ -542,8 +544,13 @@ def tune_gemv_force(kernel: int, waves_per_wg: int = 1, wgs_per_strip: int = 1, 
 
 def tune_gemm(kernel: int):
     """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general,
-    3 few-row whenever M <= 8."""
+    3 few-row whenever M <= 8, 4 short-batch MFMA ring whenever M <= 16 and K allows."""
     _check(lib().w2a8_tune_gemm(kernel), "w2a8_tune_gemm")
+
+
+def tune_gemm_ring(waves_per_wg: int = 0, wgs_per_strip: int = 0, depth: int = 0):
+    """Forced plan of the short-batch MFMA ring kernel (all 0: automatic)."""
+    _check(lib().w2a8_tune_gemm_ring(waves_per_wg, wgs_per_strip, depth), "w2a8_tune_gemm_ring")
 
 
 def gemv_plan(N: int, K: int, cus: int):

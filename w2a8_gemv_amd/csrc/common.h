@@ -149,6 +149,13 @@ void gemv_rows_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int64_t M, int 
                     int *sg, int *run, int *unroll);
 hipError_t launch_gemv_rows(const GemvLaunch &a, hipStream_t stream);
 constexpr int64_t kRowsMaxM = 8;
+// Short batches on MFMA (gemm_ring.hip): 2 <= M <= kRingMaxM, K a multiple
+// of 16, the GEMV's work split (WK waves, SG workgroups per strip; split
+// strips combine per (row, output) like the few-row kernel), depth 2, 4, 6
+// or 8 tiles in flight per wave.  LDS: gemm_ring_lds_bytes per workgroup.
+constexpr int64_t kRingMaxM = 16;
+size_t gemm_ring_lds_bytes(int M, int wk, int depth);
+hipError_t launch_gemm_ring(const GemvLaunch &a, int depth, hipStream_t stream);
 // Fused linear GEMV: quantize the bf16 row in every workgroup, then the
 // workgroup kernel with the fp32 epilogue (gemv.hip).
 hipError_t launch_gemv_fused(const GemvLaunch &a, hipStream_t stream);

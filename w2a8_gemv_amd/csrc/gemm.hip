@@ -35,8 +35,6 @@
 namespace w2a8 {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 constexpr int kXStride = kTileK + 16;  // LDS row stride of the activation tile
 
 struct GemmArgs {
@@ -54,16 +52,6 @@ struct GemmArgs {
     // (k-part p starts at p*KQ + min(p, KR)).
     int KQ, KR;
 };
-
-// Codes {0,1,2} in each byte -> signed weights {-1,0,1}.
-__device__ __forceinline__ int signed_codes(uint32_t c) {
-    return int(__builtin_amdgcn_perm(0u, 0x000100FFu, c));
-}
-
-__device__ __forceinline__ v4i expand_word(uint32_t w) {
-    return v4i{signed_codes(w & 0x03030303u), signed_codes((w >> 2) & 0x03030303u),
-               signed_codes((w >> 4) & 0x03030303u), signed_codes((w >> 6) & 0x03030303u)};
-}
 
 // Load one 16-byte activation chunk (row m, k0..k0+15) with bounds handling.
 __device__ __forceinline__ v4u load_x_chunk(const GemmArgs &a, int m, int k0, bool xvec) {

@@ -53,6 +53,10 @@ int current_device(DeviceInfo *out) {
 
 namespace {
 std::atomic<int> g_gemm_mode{0};
+// Forced plan of the short-batch MFMA ring kernel: waves | depth << 5 |
+// workgroups per strip << 9 (0: automatic), one word so that every call
+// reads a consistent plan.
+std::atomic<uint32_t> g_ring_force{0};
 std::mutex g_policy_mu;
 GemvPolicy g_policy = {4, 6, 8, 256, 48};
 
@@ -192,6 +196,38 @@ void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *w
     *depth = int(D);
 }
 
+// Short-batch MFMA ring kernel plan (measured on MI355X, cold weights, M = 8
+// unless noted; best of a sweep of WK 1..8, SG 1..8, depth 2..6 per shape):
+//  * at least two strips per CU: one wave per strip, depth 4
+//    (55296 x 5120: 15.6 us, pipelined kernel 16.5);
+//  * K under 40 tiles: 4 waves per strip, no split, depth 2 (4 with fewer
+//    strips than CUs) (13824 x 2560: 5.21 us against 6.16; M = 4 5.21
+//    against 6.01; 2560 x 2560: 4.08 against 4.72);
+//  * otherwise 4 waves and 3 workgroups per strip, depth 4 (2 from 128
+//    tiles) (2560 x 6912: 5.10 against 6.31; M = 3 4.99 against 6.20;
+//    5120 x 27648: 11.1 against 14.9; 3200 x 10240: 6.5 against 7.5, where
+//    4 workgroups of depth 2 reach 6.0).
+// The depth is lowered until the workgroup's rings fit the device's LDS.
+void gemm_ring_plan(int64_t NS, int64_t KT, int64_t M, int cus, int64_t lds, int *wk, int *sg,
+                    int *depth) {
+    int64_t WK = 4, SG = 1, D = 4;
+    if (NS >= 2 * int64_t(cus)) {
+        WK = 1;
+    } else if (KT < 40) {
+        D = NS >= cus ? 2 : 4;
+    } else {
+        SG = 3;
+        D = KT >= 128 ? 2 : 4;
+    }
+    WK = std::min(WK, ceil_div(KT, SG));
+    int d = int(D);
+    while (d > 2 && int64_t(gemm_ring_lds_bytes(int(M), int(WK), d)) > lds) d -= 2;
+    while (WK > 1 && int64_t(gemm_ring_lds_bytes(int(M), int(WK), d)) > lds) --WK;
+    *wk = int(WK);
+    *sg = int(SG);
+    *depth = d;
+}
+
 // Few activation rows: the GEMV plan with runs of at most 8 tiles (one
 // activation chunk per lane per row) and at most 32/MR waves per workgroup
 // (LDS <= 36 KiB for the MR row regions); more workgroups per strip when
@@ -232,7 +268,7 @@ const char *w2a8_status_str(int status) {
     case W2A8_ERR_NULL: return "a required pointer is NULL";
     case W2A8_ERR_SHAPE: return "M, N or K out of range";
     case W2A8_ERR_ALIGN: return "a pointer is not aligned as required";
-    case W2A8_ERR_VALUE: return "weight outside {-1,0,1} or invalid 2-bit code";
+    case W2A8_ERR_VALUE: return "value out of range (weight, 2-bit code, or tuning knob/forced plan)";
     case W2A8_ERR_BUFSIZE: return "packed or workspace buffer too small";
     case W2A8_ERR_NODEVICE: return "no HIP device available";
     case W2A8_ERR_ARCH: return "current device is not gfx950";
@@ -258,7 +294,7 @@ int64_t w2a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
         // GEMV: one 64-bit split-k combining word per padded row, if the
         // plan may split a strip's k-range at all.
         if (gemv_may_split(round_up(K, kTileK) / kTileK, gemv_policy())) bytes = 8 * Np;
-    } else if (M <= kRowsMaxM) {
+    } else if (M <= kRingMaxM) {
         // Few rows: a combining word per (row, padded output), or the general
         // kernel's split-K partials and counters, whichever is larger.
         bytes = std::max(8 * M * Np, 4 * M * Np + 4 * ceil_div(M, 16) * ceil_div(NS, 4));
@@ -715,18 +751,21 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
     a.shape = gemm_shape(M, N, K, dev.cus, need > 0);
-    // Few rows: the GEMV-style kernel over M activation rows.  Automatic
-    // choice (measured on MI355X, cold weights): M <= 2 up to 49152 weight
-    // tiles (2560 x 6912: 5.1 against 6.7 us for the best MFMA kernel;
-    // 5120 x 27648: 10.9 against 14.3 us; at 55296 x 5120 the two tie near
-    // 16 us), and ragged K (not a multiple of 16), where the MFMA path is
-    // the general kernel.  From M = 3 the MFMA kernels with wave groups
-    // splitting K win or tie (5120 x 27648 at M = 4: 14.6 against 16.3 us;
-    // 13824 x 2560 at M = 3: 6.2 against 7.2 us).
+    // Few rows.  Automatic choice (measured on MI355X, cold weights): the
+    // dot4 few-row kernel for M <= 2 up to 49152 weight tiles (13824 x 2560
+    // at M = 2: 4.92 against 5.07 us for the MFMA ring kernel; 2560 x 6912:
+    // 5.1 against 6.7 us for the pipelined kernel) and for ragged K (not a
+    // multiple of 16); the MFMA ring kernel for the other M <= 8 (plans
+    // above); the pipelined kernel from M = 9, where the ring kernel's
+    // 16-row activation tiles (a third load per k-tile) were mixed
+    // (13824 x 2560 at M = 16: 6.5 against 6.2 us; 2560 x 6912: 6.0 against
+    // 6.6).
     const int mode = gemm_kernel_mode();
     const int64_t wtiles = int64_t(a.NS) * a.KT;
     const bool few_auto = K % 16 != 0 || (M <= 2 && wtiles <= 49152);
     const bool few = M <= kRowsMaxM && (mode == 3 || (mode == 0 && few_auto));
+    const bool ring = K % 16 == 0 && !few &&
+                      ((mode == 4 && M <= kRingMaxM) || (mode == 0 && M <= kRowsMaxM));
     if (few) {
         GemvLaunch g;
         g.wp = a.wp;
@@ -745,6 +784,35 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
         gemv_rows_plan(gemv_policy(), g.NS, g.KT, M, dev.cus, &g.WK, &g.SG, &g.RUN, &g.unroll);
         if (g.SG > 1 && !workspace) return W2A8_ERR_NULL;
         hipError_t e = launch_gemv_rows(g, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
+    }
+    if (ring) {
+        GemvLaunch g;
+        g.wp = a.wp;
+        g.x = x;
+        g.xb = nullptr;
+        g.y_i32 = y_i32;
+        g.y_f32 = y_f32;
+        g.sa = s_a;
+        g.sw = s_w;
+        g.ws_row = static_cast<uint64_t *>(workspace);
+        g.N = int(N);
+        g.K = int(K);
+        g.KT = a.KT;
+        g.NS = a.NS;
+        g.M = int(M);
+        int depth = 4;
+        const uint32_t f = g_ring_force.load(std::memory_order_relaxed);
+        if (f) {
+            g.WK = int(f & 31);
+            depth = int((f >> 5) & 15);
+            g.SG = int(std::min<int64_t>(f >> 9, a.KT));
+            if (int64_t(gemm_ring_lds_bytes(int(M), g.WK, depth)) > dev.lds) return W2A8_ERR_VALUE;
+        } else {
+            gemm_ring_plan(g.NS, g.KT, M, dev.cus, dev.lds, &g.WK, &g.SG, &depth);
+        }
+        if (g.SG > 1 && !workspace) return W2A8_ERR_NULL;
+        hipError_t e = launch_gemm_ring(g, depth, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
     }
     if (int64_t(a.shape.tiles) + 8 > int64_t(INT32_MAX)) return W2A8_ERR_SHAPE;
@@ -813,8 +881,21 @@ int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg
     return W2A8_OK;
 }
 
+int w2a8_tune_gemm_ring(int waves_per_wg, int wgs_per_strip, int depth) {
+    if (waves_per_wg == 0 && wgs_per_strip == 0 && depth == 0) {
+        g_ring_force.store(0, std::memory_order_relaxed);
+        return W2A8_OK;
+    }
+    if (waves_per_wg < 1 || waves_per_wg > 16 || wgs_per_strip < 1 || wgs_per_strip > 4096 ||
+        !(depth == 2 || depth == 4 || depth == 6 || depth == 8))
+        return W2A8_ERR_VALUE;
+    g_ring_force.store(uint32_t(waves_per_wg) | uint32_t(depth) << 5 | uint32_t(wgs_per_strip) << 9,
+                       std::memory_order_relaxed);
+    return W2A8_OK;
+}
+
 int w2a8_tune_gemm(int kernel) {
-    if (kernel < 0 || kernel > 3) return W2A8_ERR_VALUE;
+    if (kernel < 0 || kernel > 4) return W2A8_ERR_VALUE;
     set_gemm_kernel_mode(kernel);
     return W2A8_OK;
 }

@@ -51,10 +51,11 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, 5.0 POPS
 ROTATE_BYTES = 700e6          # > 256 MB Infinity Cache + 8 x 4 MB L2, with margin
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
-# Sources that decide what the GEMV kernel reads and writes: the kernel, its
-# shared helpers and the host-side launch plan.
+COLDNESS_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_coldness.json")
+# Sources that decide what the GEMV kernel reads and writes: the ring kernel
+# and its launch plan (one file), and the shared helpers and launch struct.
 GEMV_SRCS = [os.path.join(ROOT, "w2a8_gemv_amd", "csrc", f)
-             for f in ("gemv.hip", "gemv_ring.hip", "common.h", "device.h", "host.hip")]
+             for f in ("gemv_ring.hip", "common.h", "device.h")]
 
 
 def gemv_sources_sha256():
@@ -107,10 +108,91 @@ def parse_args():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --steps 4 --warmup 1 --no-extra --no-detail "
                          "--no-cpu-baseline --calibrate-copy` into " + os.path.relpath(TRAFFIC_FILE, ROOT))
+    ap.add_argument("--coldness-summary", nargs=2, metavar=("COLD_CSV", "WARM_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (TCC_HIT_sum TCC_MISS_sum "
+                         "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum) of the traffic command, "
+                         "cold and with --mode warm, into " + os.path.relpath(COLDNESS_FILE, ROOT))
     return ap.parse_args()
 
 
 CALIB_BYTES = 256 << 20
+
+
+def _ring_dispatches(path, counters):
+    """Per (grid threads, workgroup threads) of the ring GEMV dispatches: the
+    mean of each counter; and the largest copy dispatch's values (the
+    256 MiB calibration copy)."""
+    import csv
+    per, copy = {}, {}
+    rows = list(csv.DictReader(open(path)))
+    for r in rows:
+        name, c, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+        if c not in counters:
+            continue
+        if "gemv_ring_kernel" in name:
+            key = (int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            per.setdefault(key, {}).setdefault(c, []).append(v)
+        elif "copyBuffer" in name:
+            copy[c] = max(copy.get(c, 0.0), v)
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in per.items()}, copy
+
+
+def write_coldness_summary(cold_csv, warm_csv, cus=256):
+    """L2 hit/miss and memory-side read requests of the sweep GEMVs, cold and
+    warm.  Requests are converted to bytes with the request count of the
+    256 MiB calibration copy of the same run."""
+    import synth
+    import w2a8_gemv_amd as w2a8
+    names = ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_DRAM_sum")
+    out = {"gemv_sources_sha256": gemv_sources_sha256(), "per_shape": [],
+           "calibration": "bytes per memory-side read request = 256 MiB / the calibration "
+                          "copy's TCC_EA0_RDREQ_DRAM_sum in the same run",
+           "reading": "dram_read_bytes ~ packed bytes in both modes: every weight byte is "
+                      "fetched past L2 on every launch.  The Infinity Cache (MALL) is on the "
+                      "memory side and has no counter here; its coldness rests on the "
+                      "rotation of >= 700 MB of weight copies and on the cold/warm timing gap.",
+           "commands": [
+               "rocprofv3 --pmc " + " ".join(names) + " --output-format csv -d <dir> -o tcc -- "
+               "python -u bench.py --steps 4 --warmup 1 --no-extra --no-detail "
+               "--no-cpu-baseline --calibrate-copy [--mode warm]",
+               "python bench.py --coldness-summary <cold_counter_collection.csv> "
+               "<warm_counter_collection.csv>"]}
+    runs = {}
+    for mode, path in (("cold", cold_csv), ("warm", warm_csv)):
+        per, copy = _ring_dispatches(path, names)
+        runs[mode] = (per, CALIB_BYTES / copy["TCC_EA0_RDREQ_DRAM_sum"])
+        out["bytes_per_request_" + mode] = round(runs[mode][1], 2)
+    for n, k in synth.SWEEP_SHAPES:
+        _, wk, sg, _ = w2a8.gemv_plan(n, k, cus)
+        key = ((-(-n // 32)) * sg * 64 * wk, 64 * wk)
+        packed = -(-n // 32) * 32 * (-(-k // 128)) * 128 // 4
+        row = {"n": n, "k": k, "packed_bytes": packed}
+        for mode, (per, bpr) in runs.items():
+            d = per[key]
+            dram = d["TCC_EA0_RDREQ_DRAM_sum"] * bpr
+            row[mode] = {"l2_hit_rate": round(d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] +
+                                                                  d["TCC_MISS_sum"]), 4),
+                         "dram_read_bytes": round(dram),
+                         "dram_over_packed": round(dram / packed, 4)}
+        out["per_shape"].append(row)
+    os.makedirs(os.path.dirname(COLDNESS_FILE), exist_ok=True)
+    with open(COLDNESS_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
+def coldness_summary():
+    """The committed coldness check, if the GEMV sources are unchanged since."""
+    try:
+        with open(COLDNESS_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemv_sources_sha256") != gemv_sources_sha256():
+        return None
+    return {"dram_over_packed_cold": [r["cold"]["dram_over_packed"] for r in t["per_shape"]],
+            "dram_over_packed_warm": [r["warm"]["dram_over_packed"] for r in t["per_shape"]],
+            "source": os.path.relpath(COLDNESS_FILE, ROOT)}
 
 
 def write_traffic_summary(fetch_csv, write_csv, cus=256):
@@ -130,8 +212,11 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
         factor = CALIB_BYTES / (max(copies) * 1024.0)
         per = {}
         for r in rows:
-            if "gemv_kernel" in r["Kernel_Name"] or "gemv_ring_kernel" in r["Kernel_Name"]:
-                per.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]) * 1024.0)
+            if "gemv_ring_kernel" in r["Kernel_Name"]:
+                # (threads in the grid, threads per workgroup): distinct for
+                # every sweep shape's plan (grid size alone is not)
+                key = (int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+                per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         return factor, per
 
     ff, fetch = load(fetch_csv)
@@ -139,9 +224,9 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
     shapes = []
     for n, k in synth.SWEEP_SHAPES:
         _, wk, sg, _ = w2a8.gemv_plan(n, k, cus)
-        grid = (-(-n // 32)) * sg * 64 * wk
-        f = sum(fetch[grid]) / len(fetch[grid]) * ff
-        w = sum(write[grid]) / len(write[grid]) * wf
+        key = ((-(-n // 32)) * sg * 64 * wk, 64 * wk)
+        f = sum(fetch[key]) / len(fetch[key]) * ff
+        w = sum(write[key]) / len(write[key]) * wf
         shapes.append({"n": n, "k": k, "algorithmic_bytes": algo_bytes(n, k),
                        "fetch_bytes": round(f), "write_bytes": round(w),
                        "ratio": round((f + w) / algo_bytes(n, k), 4)})
@@ -909,6 +994,9 @@ def main():
     if args.traffic_summary:
         print(json.dumps(write_traffic_summary(*args.traffic_summary), indent=1))
         return
+    if args.coldness_summary:
+        print(json.dumps(write_coldness_summary(*args.coldness_summary), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the W2A8 GEMV runs on a single MI355X and has no "
@@ -1020,6 +1108,7 @@ def main():
                                 "fastest of READ_FLOOR_CONFIGS (waves per CU, bytes per lane, "
                                 "loads in flight, non-temporal, strided)",
             "read_floor_sweep": read_floor_sweep(per),
+            "l2_coldness_counters": coldness_summary(),
             "plans": {f"{s.n}x{s.k}": list(w2a8.gemv_plan(s.n, s.k, cus)) for s in shapes},
             "a100_page_us_context": {f"{n}x{k}": v for (n, k), v in A100_US.items()},
         },

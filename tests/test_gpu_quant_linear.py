@@ -31,11 +31,10 @@ def _quant_dev(bits):
 
 @pytest.mark.parametrize("M,K", [(1, 2560), (128, 2560), (1, 27648), (3, 100), (5, 1),
                                  (2, 7), (4, 4000), (1, 8), (17, 16),
-                                 # one wave per row, the row in registers: 1..16 chunks of 8
-                                 # per lane, partial last chunk groups, 1, 2 and 4 rows per
-                                 # workgroup (M against 256 CUs), and K just past the limit
+                                 # one workgroup per row, one chunk of 8 per lane: 1..16
+                                 # waves (the last partly idle), and K just past the limit
                                  (1, 8192), (9, 520), (7, 512), (600, 4096), (1100, 1024),
-                                 (33, 8200), (3, 6912), (512, 2560)])
+                                 (33, 8200), (3, 6912), (512, 2560), (4, 8184), (2, 504)])
 def test_quant_matches_oracle(M, K):
     xb, _ = synth.linear_case(M, 1, K, seed=M * 7 + K)
     q, sa = _quant_dev(xb)
@@ -59,7 +58,7 @@ def test_quant_worked_examples_and_zero_rows():
 
 
 def test_quant_zero_rows_register_path():
-    # zero rows between nonzero ones, K a multiple of 8 (one wave per row)
+    # zero rows between nonzero ones, K a multiple of 8 (one chunk per lane)
     xb, _ = synth.linear_case(6, 1, 48, seed=5)
     xb[1] = 0
     xb[4] = 0x8000          # negative zeros

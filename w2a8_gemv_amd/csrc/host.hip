@@ -161,40 +161,6 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
     *unroll = std::min(u, p.unroll);
 }
 
-// Ring-kernel plan (K a multiple of 16): plain reads of this device reach
-// their best rate with ~10-12 MB in flight spread over all CUs (about four
-// waves per CU with 8-12 KiB each), and each wave's throughput is bounded by
-// its own ring (loads in flight / memory latency), so the plan aims for
-// roughly a thousand or more evenly loaded waves:
-//  * at least two strips per CU: one single-wave workgroup per whole strip
-//    (no combine at all), ring depth 4 for strips of 32 tiles or more, else 8;
-//  * long strips (KT >= split_min_tiles): single-wave workgroups with the
-//    k-range split so that the grid has about 3.75 waves per CU, combined
-//    with one atomic per row; depth 8 for runs of 24 tiles or more, else 4;
-//  * otherwise: 8-wave workgroups over whole strips, depth 4 (6 for strips of
-//    40 tiles or more).
-// Measured on MI355X (cold, per-launch): within 2% of the best of a sweep of
-// every (waves, splits, depth) on each of the 12 workload shapes; e.g.
-// 55296 x 5120 12.7 us (batch kernel 13.7), 5120 x 27648 8.1 us (8.9),
-// 13824 x 2560 4.0 us (4.3), 2560 x 6912 3.58 us (3.78).
-void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, int *sg,
-                    int *run, int *depth) {
-    int64_t WK = 8, SG = 1, D = KT >= 40 ? 6 : 4;
-    if (NS >= 2 * int64_t(cus)) {
-        WK = 1;
-        D = KT >= 32 ? 4 : 8;
-    } else if (KT >= p.split_min_tiles && KT >= 2) {
-        WK = 1;
-        SG = std::max<int64_t>(2, std::min<int64_t>(KT / 4, (int64_t(cus) * 15 / 4 + NS / 2) / NS));
-        SG = std::min(SG, KT);
-        D = ceil_div(KT, SG) >= 24 ? 8 : 4;
-    }
-    WK = std::min(WK, ceil_div(KT, SG));
-    *wk = int(WK);
-    *sg = int(SG);
-    *run = int(ceil_div(ceil_div(KT, SG), WK));
-    *depth = int(D);
-}
 
 // Short-batch MFMA ring kernel plan (measured on MI355X, cold weights, M = 8
 // unless noted; best of a sweep of WK 1..8, SG 1..8, depth 2..6 per shape):

@@ -8,11 +8,11 @@
 // IEEE, the product is not contracted, v_rndne_f32 rounds half to even), so
 // the result is bit-identical to any IEEE implementation of the same steps.
 //
-// K a multiple of 8 up to 8192: one wave per row holding the whole row in
-// registers (one read of the row, a cross-lane maximum, then quantize and
-// store from the same registers).  Other K: one 256-thread workgroup per row,
-// a vectorised max pass, a block max, then a quantize pass that re-reads the
-// row from L2.
+// K a multiple of 8 up to 8192: one workgroup per row, each lane holding one
+// chunk of 8 values in registers (one read of the row, a row maximum across
+// lanes and waves, then quantize and store from the same registers).  Other
+// K: one 256-thread workgroup per row, a vectorised max pass, a block max,
+// then a quantize pass that re-reads the row from L2.
 //
 // The int4 variant (the "a4.8" activations that
 // "使用 BitNet 框架部署 1-bit LLM：三元权重量化、LUT 矩阵乘加速与 GPU 运行时优化",
@@ -80,50 +80,45 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *xb, int M, i
     if (tid == 0) sa[m] = amax / 127.0f;
 }
 
-// One wave per row, the row held in registers (K % 8 == 0, K <= 512*C): each
-// lane loads its C chunks of 8 values at once, the wave takes the row maximum
-// with cross-lane reductions, and the same registers are quantized and
-// stored, so the row is read from memory once.  R rows (waves) per
-// workgroup.  Same per-element operations (q8) as quant_kernel.
-template <int C>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t *xb, int M, int K,
-                                                         int8_t *xq, float *sa) {
-    const int lane = int(threadIdx.x) & 63;
-    const int m = int(blockIdx.x) * (int(blockDim.x) >> 6) + (int(threadIdx.x) >> 6);
-    if (m >= M) return;
+// One workgroup per row, one 8-value chunk per lane (K % 8 == 0, K <= 8192):
+// W = ceil(K/512) waves load the row once, take the maximum (within each
+// wave by lane exchanges, then across the waves through LDS), and quantize
+// and store the chunk held in registers.  Same per-element operations (q8)
+// as quant_kernel.
+__global__ __launch_bounds__(1024) void quant_rows_kernel(const uint16_t *xb, int M, int K,
+                                                          int8_t *xq, float *sa) {
+    const int tid = int(threadIdx.x);
+    const int m = int(blockIdx.x);
+    const int c = tid;                            // this lane's chunk of 8 values
+    const int nc = K >> 3;
     const v4u *r8 = reinterpret_cast<const v4u *>(xb + int64_t(m) * K);
     v2u *o8 = reinterpret_cast<v2u *>(xq + int64_t(m) * K);
-    const int nc = K >> 3;
-    v4u v[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const int c = lane + 64 * j;
-        v[j] = c < nc ? r8[c] : v4u{0u, 0u, 0u, 0u};
-    }
+    const v4u v = c < nc ? r8[c] : v4u{0u, 0u, 0u, 0u};
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < C; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(v[j][i])), fabsf(hi_bf16(v[j][i]))));
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(v[i])), fabsf(hi_bf16(v[i]))));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;   // a zero row quantizes to 0
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const int c = lane + 64 * j;
-        if (c < nc) {
-            uint32_t o[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t a = v[j][2 * h], b = v[j][2 * h + 1];
-                o[h] = q8(lo_bf16(a), inv) | (q8(hi_bf16(a), inv) << 8) |
-                       (q8(lo_bf16(b), inv) << 16) | (q8(hi_bf16(b), inv) << 24);
-            }
-            o8[c] = v2u{o[0], o[1]};
-        }
+    __shared__ float red[16];
+    const int nw = int(blockDim.x) >> 6;
+    if (nw > 1) {
+        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        __syncthreads();
+        amax = red[0];
+        for (int w = 1; w < nw; ++w) amax = fmaxf(amax, red[w]);
     }
-    if (lane == 0) sa[m] = amax / 127.0f;
+    const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;   // a zero row quantizes to 0
+    if (c < nc) {
+        uint32_t o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t a = v[2 * h], b = v[2 * h + 1];
+            o[h] = q8(lo_bf16(a), inv) | (q8(hi_bf16(a), inv) << 8) |
+                   (q8(lo_bf16(b), inv) << 16) | (q8(hi_bf16(b), inv) << 24);
+        }
+        o8[c] = v2u{o[0], o[1]};
+    }
+    if (tid == 0) sa[m] = amax / 127.0f;
 }
 
 // Row maximum of |x| over a workgroup of 256 threads.
@@ -217,26 +212,16 @@ hipError_t launch_quant_a4(const uint16_t *xb, int M, int K, uint8_t *xq4, float
                            dim3(256), args, 0, stream);
 }
 
-// Register-resident rows for K % 8 == 0 and K <= 8192 (C = 1..16 chunks of 8
-// per lane); one wave per row, and workgroups of 2 or 4 rows only once M
-// gives every CU that many (fewer, larger workgroups dispatch faster; smaller
-// ones spread a short batch over more CUs).  Other K: one 256-thread
+// K % 8 == 0 and K <= 8192: one workgroup of ceil(K/512) waves per row, one
+// chunk of 8 values per lane (quant_rows_kernel).  Other K: one 256-thread
 // workgroup per row, two passes (quant_kernel).
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
                         hipStream_t stream) {
     void *args[] = {const_cast<uint16_t **>(&xb), &M, &K, &xq, &sa};
     if ((K & 7) == 0 && K <= 8192) {
-        DeviceInfo dev;
-        const int cus = current_device(&dev) == W2A8_OK ? dev.cus : 256;
-        const int rows = M >= 4 * cus ? 4 : M >= 2 * cus ? 2 : 1;
-        const int need = (K / 8 + 63) / 64;
-        const void *fn = need <= 1   ? reinterpret_cast<const void *>(&quant_rows_kernel<1>)
-                         : need <= 2 ? reinterpret_cast<const void *>(&quant_rows_kernel<2>)
-                         : need <= 4 ? reinterpret_cast<const void *>(&quant_rows_kernel<4>)
-                         : need <= 8 ? reinterpret_cast<const void *>(&quant_rows_kernel<8>)
-                                     : reinterpret_cast<const void *>(&quant_rows_kernel<16>);
-        return hipLaunchKernel(fn, dim3(unsigned((M + rows - 1) / rows)), dim3(unsigned(64 * rows)),
-                               args, 0, stream);
+        const int waves = (K / 8 + 63) / 64;
+        return hipLaunchKernel(reinterpret_cast<const void *>(&quant_rows_kernel),
+                               dim3(unsigned(M)), dim3(unsigned(64 * waves)), args, 0, stream);
     }
     return hipLaunchKernel(reinterpret_cast<const void *>(&quant_kernel), dim3(unsigned(M)),
                            dim3(256), args, 0, stream);

@@ -23,8 +23,9 @@ inline int64_t a4_row_bytes(int64_t K) { return (K + kA4Granule - 1) / kA4Granul
 
 hipError_t launch_quant_a4(const uint16_t *xb, int M, int K, uint8_t *xq4, float *sa,
                            hipStream_t stream);
-// The workgroup GEMV of gemv.hip with int4 activations (a.x points at the
-// A4I row); same plan, layout, reduction and workspace.
-hipError_t launch_gemv_a4(const GemvLaunch &a, hipStream_t stream);
+// The ring GEMV of gemv_ring.hip with int4 activations (a.x points at the
+// A4I row; any K); same plan (gemv_ring_plan), layout, reduction and
+// workspace.  depth: 2, 4, 6, 8 or 12 tiles in flight per wave.
+hipError_t launch_gemv_a4(const GemvLaunch &a, int depth, hipStream_t stream);
 
 }  // namespace w2a8

@@ -7,16 +7,20 @@
 // section "GPU 运行时优化与低延迟推理管道", names as its "a4.8" extension;
 // the scale epilogue of "Windows 上跑通 BitNet b1.58：…部署实录" §3.1.
 //
-// Same work split, loads, staging, reduction and split-k combine as the
-// int8 workgroup kernel (gemv.hip); what changes:
-//  * a tile's activations are 64 bytes (128 nibbles) and a lane reads its
-//    chunk as 8 bytes from the wave's LDS region;
+// Same work split, weight stream, reduction and split-k combine as the int8
+// ring kernel (gemv_ring.hip): each wave keeps a ring of D weight tiles in
+// flight and loads each tile's activation chunk next to it.  What changes:
+//  * a tile's activations are 64 bytes (128 nibbles): a lane loads its
+//    chunk as 8 bytes;
 //  * decode: for each weight word, w & 0x33333333 and (w >> 2) & 0x33333333
 //    put the codes c = w + 1 of 8 values each into nibbles, in the same
 //    positions as their activations in the chunk's two words, so two
 //    v_dot8_i32_i4 give sum c*x over 16 weights: 5 VALU per 16 weights
 //    (the int8 kernel needs 9), one accumulator per row;
-//  * sum_k x (for sum w*x = sum c*x - sum x) is v_dot8 against 0x11111111.
+//  * sum_k x (for sum w*x = sum c*x - sum x) is v_dot8 against 0x11111111;
+//  * A4I rows are zero-padded to 32 values, so any K takes this kernel:
+//    values past K inside the row are zeros, and only chunks past the padded
+//    row are clamped to a chunk inside it and counted as zero.
 #include "a4.h"
 #include "device.h"
 
@@ -25,10 +29,6 @@ namespace {
 
 
 constexpr int kA4TileBytes = kTileK / 2;   // activation bytes per k-tile (64)
-// Activation granules (16 bytes, 2 chunks) staged per lane: runs of at most
-// 32 tiles = 128 granules.
-constexpr int kA4Granules = 2;
-
 
 __device__ __forceinline__ void mac_a4(const v4u w, const v2u xv, int (&acc)[4]) {
 #pragma unroll
@@ -39,22 +39,9 @@ __device__ __forceinline__ void mac_a4(const v4u w, const v2u xv, int (&acc)[4])
     }
 }
 
-template <int U>
-__device__ __forceinline__ void mac_batch(const v4u (&w)[U], const uint8_t *xl, int n, int b,
-                                          int kg, int (&acc)[4]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (b * U + u < n) {
-            const v2u xv =
-                *reinterpret_cast<const v2u *>(xl + (b * U + u) * kA4TileBytes + 8 * kg);
-            mac_a4(w[u], xv, acc);
-        }
-    }
-}
-
-template <int U>
+template <int D>
 __global__ __launch_bounds__(1024) void gemv_a4_kernel(GemvLaunch a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int red[16 * kTileRows];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -64,74 +51,63 @@ __global__ __launch_bounds__(1024) void gemv_a4_kernel(GemvLaunch a) {
     const int kt0 = g * a.KQ + min(g, a.KR);
     const int ntile = a.KQ + (big ? 1 : 0);
     const int wq = big ? a.WQ1 : a.WQ0, wr = big ? a.WR1 : a.WR0;
+    // Tiles of this wave: w0 .. w0+n-1; loads past the run re-read its last
+    // tile (an empty run: a tile of this strip).
     const int w0 = kt0 + wv * wq + min(wv, wr);
     const int n = wq + (wv < wr ? 1 : 0);
-    const int w1 = w0 + n;
-    const int nb = (n + U - 1) / U;
     const int kg = lane & 7, rg = lane >> 3;
+    const int last = min(max(w0, w0 + n - 1), a.KT - 1);
+    const v4u *sbase = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords);
+    // Activation chunks of 8 bytes: chunk c = 8t + kg of the padded row.
+    const v2u *xp = reinterpret_cast<const v2u *>(a.x);
+    const int xlast = (a.K + kA4Granule - 1) / kA4Granule * 2 - 1;   // 2 chunks per granule
 
-    // LDS: per-wave activation regions of RUN tiles, then the row partials.
-    uint8_t *xl = smem + wv * (a.RUN * kA4TileBytes);
-    int *red = reinterpret_cast<int *>(smem + a.WK * a.RUN * kA4TileBytes);
-
-    const v4u *wt = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords) + lane;
-    const int last = min(max(w0, w1 - 1), a.KT - 1);
-
-    // 1. The run's activation granules that exist in the padded row, loaded
-    //    before the weights (granules past the row read as zero).
-    const uint8_t *xg = reinterpret_cast<const uint8_t *>(a.x);
-    const int gbase = w0 * (kTileK / kA4Granule);
-    const int ngran = n * (kTileK / kA4Granule);
-    const int grow = (a.K + kA4Granule - 1) / kA4Granule;
-    v4u xr[kA4Granules];
+    // 1. Fill the ring: tiles w0 .. w0+D-1 (clamped to `last`) and their
+    //    activation chunks.
+    v4u r[D];
+    v2u xq[D];
 #pragma unroll
-    for (int j = 0; j < kA4Granules; ++j) {
-        const int c = lane + 64 * j;
-        xr[j] = v4u{0u, 0u, 0u, 0u};
-        if (c < ngran && gbase + c < grow)
-            xr[j] = *reinterpret_cast<const v4u *>(xg + 16 * (gbase + c));
+    for (int j = 0; j < D; ++j) {
+        const int t = min(w0 + j, last);
+        r[j] = __builtin_nontemporal_load(sbase + t * (kTileBytes / 16) + lane);
+        xq[j] = xp[min(t * 8 + kg, xlast)];
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 2. Two batches of weight loads in flight (clamped to the run).
-    v4u wa[U], wb[U];
-    load_batch<U>(wt, w0, last, 0, wa);
-    load_batch<U>(wt, w0, last, 1, wb);
-
-    // 3. Stage the run's activations and sum them.
-    int sx = 0;
-#pragma unroll
-    for (int j = 0; j < kA4Granules; ++j) {
-        const int c = lane + 64 * j;
-        if (c < ngran) *reinterpret_cast<v4u *>(xl + 16 * c) = xr[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sx = dot8(xr[j][e], 0x11111111u, sx);
-    }
-    sx = sum8(sx);
-    sx += __shfl_xor(sx, 8);
-    sx += __shfl_xor(sx, 16);
-    sx += __shfl_xor(sx, 32);
-
-    // 4. Stream the run: multiply one batch while the next is in flight.
+    // 2. Stream: consume tile i of the run, reload its slot with tile i + D.
     int acc[4] = {0, 0, 0, 0};
-    if (n > 0) {
-        int b = 0;
-        for (; b + 2 < nb; b += 2) {
-            mac_batch<U>(wa, xl, n, b, kg, acc);
-            load_batch<U>(wt, w0, last, b + 2, wa);
-            mac_batch<U>(wb, xl, n, b + 1, kg, acc);
-            load_batch<U>(wt, w0, last, b + 3, wb);
-        }
-        mac_batch<U>(wa, xl, n, b, kg, acc);
-        if (b + 1 < nb) mac_batch<U>(wb, xl, n, b + 1, kg, acc);
-    }
-
-    // 5. Reduce over the 8 lanes of a row group, then over the waves.
-    int r[4];
+    int sxl = 0;
+    int i = 0;
+    for (; i + D < n; i += D) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = sum8(acc[q]);
-    const int mine = (kg == 0 ? r[0] : kg == 1 ? r[1] : kg == 2 ? r[2] : r[3]) - sx;
-    int tot = 0;
-    int r32;
+        for (int j = 0; j < D; ++j) {
+            const bool in = (w0 + i + j) * 8 + kg <= xlast;
+            const v2u xv = in ? xq[j] : v2u{0u, 0u};
+            sxl = dot8(xv[0], 0x11111111u, dot8(xv[1], 0x11111111u, sxl));
+            mac_a4(r[j], xv, acc);
+            const int t = min(w0 + i + D + j, last);
+            r[j] = __builtin_nontemporal_load(sbase + t * (kTileBytes / 16) + lane);
+            xq[j] = xp[min(t * 8 + kg, xlast)];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        if (i + j < n) {
+            const bool in = (w0 + i + j) * 8 + kg <= xlast;
+            const v2u xv = in ? xq[j] : v2u{0u, 0u};
+            sxl = dot8(xv[0], 0x11111111u, dot8(xv[1], 0x11111111u, sxl));
+            mac_a4(r[j], xv, acc);
+        }
+    }
+    const int sx = sum8(sxl);
+
+    // 3. Reduce over the 8 lanes of a row group, then over the waves.
+    int rr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rr[q] = sum8(acc[q]);
+    const int mine = (kg == 0 ? rr[0] : kg == 1 ? rr[1] : kg == 2 ? rr[2] : rr[3]) - sx;
+    int tot = 0, r32;
     bool owner;
     if (a.WK == 1) {
         tot = mine;
@@ -157,7 +133,8 @@ __global__ __launch_bounds__(1024) void gemv_a4_kernel(GemvLaunch a) {
 
 }  // namespace
 
-hipError_t launch_gemv_a4(const GemvLaunch &la, hipStream_t stream) {
+hipError_t launch_gemv_a4(const GemvLaunch &la, int depth, hipStream_t stream) {
+    if (la.WK < 1 || la.WK > 16) return hipErrorInvalidValue;
     GemvLaunch a = la;
     a.KQ = a.KT / a.SG;
     a.KR = a.KT % a.SG;
@@ -166,12 +143,17 @@ hipError_t launch_gemv_a4(const GemvLaunch &la, hipStream_t stream) {
     a.WQ1 = (a.KQ + 1) / a.WK;
     a.WR1 = (a.KQ + 1) % a.WK;
     void *args[] = {&a};
-    const void *fn = a.unroll == 2   ? reinterpret_cast<const void *>(&gemv_a4_kernel<2>)
-                     : a.unroll == 4 ? reinterpret_cast<const void *>(&gemv_a4_kernel<4>)
-                                     : reinterpret_cast<const void *>(&gemv_a4_kernel<8>);
-    const size_t lds = size_t(a.WK) * a.RUN * kA4TileBytes + size_t(a.WK) * kTileRows * 4;
+    const void *fn;
+    switch (depth) {
+    case 2: fn = reinterpret_cast<const void *>(&gemv_a4_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&gemv_a4_kernel<4>); break;
+    case 6: fn = reinterpret_cast<const void *>(&gemv_a4_kernel<6>); break;
+    case 8: fn = reinterpret_cast<const void *>(&gemv_a4_kernel<8>); break;
+    case 12: fn = reinterpret_cast<const void *>(&gemv_a4_kernel<12>); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
-                           args, lds, stream);
+                           args, 0, stream);
 }
 
 }  // namespace w2a8

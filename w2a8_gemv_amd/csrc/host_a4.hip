@@ -95,8 +95,10 @@ int w2a4_gemv(const void *w_packed, const uint8_t *x_q4, int64_t N, int64_t K, i
     a.K = int(K);
     a.KT = int((K + kTileK - 1) / kTileK);
     a.NS = int(Np / kTileRows);
-    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
-    hipError_t e = launch_gemv_a4(a, static_cast<hipStream_t>(stream));
+    int depth = 4;
+    gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
+    a.unroll = depth;
+    hipError_t e = launch_gemv_a4(a, depth, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 

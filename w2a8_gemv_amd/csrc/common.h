@@ -93,6 +93,9 @@ struct GemvGroups {
     float *y_f32[kMaxGroups];
 };
 hipError_t launch_gemv_grouped(const GemvLaunch &a, const GemvGroups &t, hipStream_t stream);
+// The ring kernel over several projections (K a multiple of 16; gemv_ring.hip).
+hipError_t launch_gemv_ring_grouped(const GemvLaunch &a, const GemvGroups &t, int depth,
+                                    hipStream_t stream);
 
 // Activation quantization, per element (shared by the quantizer kernel and
 // the fused linear GEMV so both produce the same codes): bf16 halves of a

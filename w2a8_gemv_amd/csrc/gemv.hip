@@ -60,45 +60,6 @@ __device__ __forceinline__ void mac(const v4u w, const v4u xv, Acc &acc) {
     }
 }
 
-// The projection a strip belongs to.  Plain launch: the launch's own matrix
-// and outputs.  Grouped launch (several projections sharing the activation
-// row and K): strips are numbered across the projections in order and
-// projection i owns strips [begin[i], begin[i+1]); begin is increasing and
-// padded with INT32_MAX, so the choice is a chain of uniform selects over
-// values already in the kernel arguments, with no dependent load.
-struct Proj {
-    const uint32_t *wp;
-    int32_t *y_i32;
-    float *y_f32;
-    float sw;
-    int N;
-    int s;   // strip index within the projection
-};
-
-template <bool GROUPED>
-__device__ __forceinline__ Proj select_proj(const GemvLaunch &a, const GemvGroups &t, int s) {
-    Proj p{a.wp, a.y_i32, a.y_f32, a.sw, a.N, s};
-    if constexpr (GROUPED) {
-        // The last projection that begins at or before s owns it.
-#pragma unroll
-        for (int i = 0; i < kMaxGroups; ++i) {
-            const bool hit = s >= t.begin[i];
-            p.wp = hit ? t.wp[i] : p.wp;
-            p.y_i32 = hit ? t.y_i32[i] : p.y_i32;
-            p.y_f32 = hit ? t.y_f32[i] : p.y_f32;
-            p.sw = hit ? t.sw[i] : p.sw;
-            p.N = hit ? t.N[i] : p.N;
-            p.s = hit ? s - t.begin[i] : p.s;
-        }
-    }
-    return p;
-}
-
-__device__ __forceinline__ void store_proj(const Proj &p, float sa, int row, int v) {
-    if (p.y_i32) p.y_i32[row] = v;
-    if (p.y_f32) p.y_f32[row] = (float(v) * sa) * p.sw;
-}
-
 // Largest |x| of bf16 words (8 values per v4u... 2 per word).
 __device__ __forceinline__ float absmax_words(const v4u v, float m) {
 #pragma unroll

@@ -50,14 +50,18 @@ __device__ __forceinline__ int xsum16(const v4u x, int s) {
     return dot4(x[3], 0x01010101u, s);
 }
 
-template <int D>
-__global__ __launch_bounds__(1024) void gemv_ring_kernel(GemvLaunch a) {
+// GROUPED: the strip's matrix, outputs and weight scale come from the
+// projection table (strips numbered across the projections); the split-k
+// combining words are indexed by the strip's position in the whole launch.
+template <int D, bool GROUPED>
+__device__ __forceinline__ void ring_body(const GemvLaunch &a, const GemvGroups &tab) {
     __shared__ int red[16 * kTileRows];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = int(blockIdx.x);
     const int g = int(blockIdx.y);
+    const Proj pj = select_proj<GROUPED>(a, tab, s);
     const bool big = g < a.KR;
     const int kt0 = g * a.KQ + min(g, a.KR);
     const int ntile = a.KQ + (big ? 1 : 0);
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(1024) void gemv_ring_kernel(GemvLaunch a) {
     // Last tile a load may touch: the run's last tile (or, for an empty run,
     // a tile of this strip).
     const int last = min(max(w0, w0 + n - 1), a.KT - 1);
-    const v4u *sbase = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords);
+    const v4u *sbase = reinterpret_cast<const v4u *>(pj.wp + int64_t(pj.s) * a.KT * kTileWords);
 
     // 1. Fill the ring: tiles w0 .. w0+D-1 (clamped to `last`) and their
     //    activation chunks.
@@ -134,14 +138,23 @@ __global__ __launch_bounds__(1024) void gemv_ring_kernel(GemvLaunch a) {
         if (owner)
             for (int w = 0; w < a.WK; ++w) tot += red[w * kTileRows + tid];
     }
-    const int row = s * kTileRows + r32;
-    const float sa = a.y_f32 ? a.sa[0] : 0.0f;
+    const int row = pj.s * kTileRows + r32;
+    const float sa = pj.y_f32 ? a.sa[0] : 0.0f;
     int v = tot;
-    if (a.SG > 1 && !(owner && split_add(a.ws_row + row, ntile, tot, a.KT, &v))) return;
-    if (owner && row < a.N) {
-        if (a.y_i32) a.y_i32[row] = v;
-        if (a.y_f32) a.y_f32[row] = (float(v) * sa) * a.sw;
-    }
+    if (a.SG > 1 &&
+        !(owner && split_add(a.ws_row + s * kTileRows + r32, ntile, tot, a.KT, &v)))
+        return;
+    if (owner && row < pj.N) store_proj(pj, sa, row, v);
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void gemv_ring_kernel(GemvLaunch a) {
+    ring_body<D, false>(a, GemvGroups{});
+}
+
+template <int D>
+__global__ __launch_bounds__(1024) void gemv_ring_grouped_kernel(GemvLaunch a, GemvGroups t) {
+    ring_body<D, true>(a, t);
 }
 
 }  // namespace
@@ -181,7 +194,10 @@ void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *w
     *depth = int(D);
 }
 
-hipError_t launch_gemv_ring(const GemvLaunch &la, int depth, hipStream_t stream) {
+namespace {
+
+template <bool GROUPED>
+hipError_t launch_ring(const GemvLaunch &la, const GemvGroups *t, int depth, hipStream_t stream) {
     if ((la.K & 15) != 0 || la.WK < 1 || la.WK > 16) return hipErrorInvalidValue;
     GemvLaunch a = la;
     a.KQ = a.KT / a.SG;
@@ -190,18 +206,34 @@ hipError_t launch_gemv_ring(const GemvLaunch &la, int depth, hipStream_t stream)
     a.WR0 = a.KQ % a.WK;
     a.WQ1 = (a.KQ + 1) / a.WK;
     a.WR1 = (a.KQ + 1) % a.WK;
-    void *args[] = {&a};
+    GemvGroups tt = t ? *t : GemvGroups{};
+    void *args[] = {&a, &tt};
     const void *fn;
+#define W2A8_RING(DD)                                                                      \
+    fn = GROUPED ? reinterpret_cast<const void *>(&gemv_ring_grouped_kernel<DD>)           \
+                 : reinterpret_cast<const void *>(&gemv_ring_kernel<DD>)
     switch (depth) {
-    case 2: fn = reinterpret_cast<const void *>(&gemv_ring_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void *>(&gemv_ring_kernel<4>); break;
-    case 6: fn = reinterpret_cast<const void *>(&gemv_ring_kernel<6>); break;
-    case 8: fn = reinterpret_cast<const void *>(&gemv_ring_kernel<8>); break;
-    case 12: fn = reinterpret_cast<const void *>(&gemv_ring_kernel<12>); break;
+    case 2: W2A8_RING(2); break;
+    case 4: W2A8_RING(4); break;
+    case 6: W2A8_RING(6); break;
+    case 8: W2A8_RING(8); break;
+    case 12: W2A8_RING(12); break;
     default: return hipErrorInvalidValue;
     }
+#undef W2A8_RING
     return hipLaunchKernel(fn, dim3(unsigned(a.NS), unsigned(a.SG)), dim3(unsigned(64 * a.WK)),
                            args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, hipStream_t stream) {
+    return launch_ring<false>(a, nullptr, depth, stream);
+}
+
+hipError_t launch_gemv_ring_grouped(const GemvLaunch &a, const GemvGroups &t, int depth,
+                                    hipStream_t stream) {
+    return launch_ring<true>(a, &t, depth, stream);
 }
 
 }  // namespace w2a8

@@ -629,10 +629,20 @@ int grouped_launch(const GemvPolicy &pol, const GemvGroups &t, int64_t ns, int64
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(ns);
-    // One plan for the whole launch, as for a matrix of all the strips.
-    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
-    a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
-    hipError_t e = launch_gemv_grouped(a, t, static_cast<hipStream_t>(stream));
+    // One plan for the whole launch, as for a matrix of all the strips: the
+    // ring kernel for int8 rows with K a multiple of 16, else the workgroup
+    // kernel (which also quantizes a bf16 row in every workgroup).
+    hipError_t e;
+    if (!xb && (K & 15) == 0) {
+        int depth = 4;
+        gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
+        a.unroll = depth;
+        e = launch_gemv_ring_grouped(a, t, depth, static_cast<hipStream_t>(stream));
+    } else {
+        gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+        a.DXOK = int64_t(a.NS) * a.SG * a.WK <= 5 * int64_t(dev.cus);
+        e = launch_gemv_grouped(a, t, static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 

@@ -28,8 +28,6 @@ namespace w2a8 {
 namespace {
 
 
-constexpr int kA4TileBytes = kTileK / 2;   // activation bytes per k-tile (64)
-
 __device__ __forceinline__ void mac_a4(const v4u w, const v2u xv, int (&acc)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

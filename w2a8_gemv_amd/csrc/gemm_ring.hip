@@ -191,37 +191,51 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
     wait_vm<0>();
 
     // Outputs.  acc[j][e] of lane l is element (m, c) of the strip's
-    // [MR x 32] output tile with m = 4(l/16) + e, c = 16j + l%16.  The tile is
-    // exchanged through LDS (the wave's own ring, or with WK waves a shared
-    // area once every wave has passed the first barrier) and summed over the
-    // waves in store order: instruction i covers rows 2i (lanes 0..31) and
-    // 2i + 1 (lanes 32..63), one whole 128-byte row segment each, so no store
-    // writes part of a line.  With WK waves, wave w finishes the instructions
-    // i with i % WK == w.
-    int *red = reinterpret_cast<int *>(a.WK > 1 ? smem : ring);
-    const int wsel = a.WK > 1 ? wv : 0;
-    if (a.WK > 1) __syncthreads();
+    // [MR x 32] output tile with m = 4(l/16) + e, c = 16j + l%16.  Each wave
+    // writes its tile to the start of its own ring (its loads have all
+    // landed, and no other wave touches that ring), so one barrier suffices
+    // before the waves read one another's tiles.  The sums are finished in
+    // store order: instruction i covers rows 2i (lanes 0..31) and 2i + 1
+    // (lanes 32..63), one whole 128-byte row segment each, so no store writes
+    // part of a line; with WK waves, wave w finishes the instructions i with
+    // i % WK == w.
+    {
+        int *mine = reinterpret_cast<int *>(ring);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) red[(wsel * 8 + p) * 64 + lane] = acc[p >> 2][p & 3];
+        for (int p = 0; p < 8; ++p) mine[p * 64 + lane] = acc[p >> 2][p & 3];
+    }
     if (a.WK > 1) __syncthreads();
     constexpr int NI = MR / 2;
     const int c = lane & 31;
     const int Np = a.NS * kTileRows;
     const int row = s * kTileRows + c;
-    // (every wave reads all NI positions of every wave's tile, NI reads in
-    // flight per step, and keeps the sums it owns)
+    // the instructions this wave finishes, as a bit mask (no division)
+    uint32_t own = 0;
+    for (int i = wv; i < NI; i += a.WK) own |= 1u << i;
+    const int *red = reinterpret_cast<const int *>(smem);
+    constexpr int kRingInts = D * SLOT / 4;        // ints from one wave's ring to the next
     int val[NI], at[NI];
     bool st[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int m = 2 * i + (lane >> 5);
-        st[i] = (a.WK == 1 || i % a.WK == wv) && m < a.M;
+        st[i] = ((own >> i) & 1u) && m < a.M;
         at[i] = (4 * (c >> 4) + (m & 3)) * 64 + 16 * (m >> 2) + (c & 15);
         val[i] = 0;
     }
-    for (int w = 0; w < a.WK; ++w) {
+    // Sums over the waves' tiles, four waves per step with all their reads in
+    // flight (reads past the last wave re-read it and count as zero).
+    for (int w = 0; w < a.WK; w += 4) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) val[i] += red[w * 512 + at[i]];
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = w + u < a.WK;
+            const int wu = ok ? w + u : a.WK - 1;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int t = red[wu * kRingInts + at[i]];
+                val[i] += ok ? t : 0;
+            }
+        }
     }
     // Every scale load and split-strip atomic is issued before any store, so
     // no wait for a returning value falls between stores (each such wait

@@ -163,16 +163,17 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
 
 
 // Short-batch MFMA ring kernel plan (measured on MI355X, cold weights, M = 8
-// unless noted; best of a sweep of WK 1..8, SG 1..8, depth 2..6 per shape):
+// unless noted; best of a sweep of WK 1..16, SG 1..8, depth 2..8 per shape,
+// pipelined kernel in brackets where measured):
 //  * at least two strips per CU: one wave per strip, depth 4
-//    (55296 x 5120: 15.6 us, pipelined kernel 16.5);
+//    (55296 x 5120: 15.9 us [16.5]);
 //  * K under 40 tiles: 4 waves per strip, no split, depth 2 (4 with fewer
-//    strips than CUs) (13824 x 2560: 5.21 us against 6.16; M = 4 5.21
-//    against 6.01; 2560 x 2560: 4.08 against 4.72);
+//    strips than CUs) (13824 x 2560: 5.06 us [6.16], M = 4 5.04;
+//    2560 x 2560: 3.89);
+//  * K of 64 to 127 tiles: 4 waves and 4 workgroups per strip, depth 2
+//    (3200 x 10240: 5.77 against 6.29 with 3 workgroups of depth 4);
 //  * otherwise 4 waves and 3 workgroups per strip, depth 4 (2 from 128
-//    tiles) (2560 x 6912: 5.10 against 6.31; M = 3 4.99 against 6.20;
-//    5120 x 27648: 11.1 against 14.9; 3200 x 10240: 6.5 against 7.5, where
-//    4 workgroups of depth 2 reach 6.0).
+//    tiles) (2560 x 6912: 4.86 [6.31], M = 4 4.81; 5120 x 27648: 11.2).
 // The depth is lowered until the workgroup's rings fit the device's LDS.
 void gemm_ring_plan(int64_t NS, int64_t KT, int64_t M, int cus, int64_t lds, int *wk, int *sg,
                     int *depth) {
@@ -181,6 +182,9 @@ void gemm_ring_plan(int64_t NS, int64_t KT, int64_t M, int cus, int64_t lds, int
         WK = 1;
     } else if (KT < 40) {
         D = NS >= cus ? 2 : 4;
+    } else if (KT >= 64 && KT < 128) {
+        SG = 4;
+        D = 2;
     } else {
         SG = 3;
         D = KT >= 128 ? 2 : 4;

@@ -99,6 +99,13 @@ def parse_args():
                          "wave, waves per CU, non-temporal or plain loads and contiguous or "
                          "strided chunks, on cold 1 GiB, 71 MB and 35 MB buffers; prints one "
                          "JSON line with the table and exits")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="launch an empty kernel over 1 to 1024 workgroups and the int8 "
+                         "quantizer at M = 1 to 256 (K = 2560), eagerly (kernel-trace runs) "
+                         "and graph-timed; prints one JSON line and exits")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="median, mean and minimum duration per (kernel, grid, workgroup) "
+                         "of a rocprofv3 --kernel-trace CSV; prints one JSON line and exits")
     ap.add_argument("--bf16-context", action="store_true",
                     help="also time the pages' bf16 torch.matmul comparison on the sweep "
                          "shapes (context only, off by default)")
@@ -495,6 +502,75 @@ def graph_times(torch, launch, reps, stream, rounds=5):
         if r:
             out.append(e0.elapsed_time(e1) * 1e3 / reps)
     return out
+
+
+LAUNCH_FLOOR_WGS = [1, 2, 4, 8, 16, 32, 128, 1024]
+LAUNCH_FLOOR_QUANT_M = [1, 2, 8, 32, 128, 256]
+
+
+def launch_floor(torch, w2a8, readref, stream, reps=50):
+    """The fixed cost of a launch against the workgroups it spreads over the
+    dies: an empty kernel (4 waves per workgroup, no memory access) over
+    LAUNCH_FLOOR_WGS workgroups, and the int8 quantizer (one workgroup per
+    row) at LAUNCH_FLOOR_QUANT_M rows of K = 2560.  Each is launched `reps`
+    times eagerly with a synchronisation after each (so a kernel trace sees
+    them one by one), then graph-timed (median per launch)."""
+    import numpy as np
+    dev = torch.device("cuda", torch.cuda.current_device())
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ob = torch.zeros(4 * max(LAUNCH_FLOOR_WGS), dtype=torch.int32, device=dev)
+    out = {"method": "eager launches one by one (for the kernel trace), then the median "
+                     "per-launch time of a graph of 24 launches over 5 replays",
+           "empty_kernel": {}, "quant_act_int8_K2560": {}}
+
+    def run(fn):
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                fn(0)
+            torch.cuda.synchronize()
+        return round(float(np.median(graph_times(torch, fn, 24, stream))), 3)
+
+    for wgs in LAUNCH_FLOOR_WGS:
+        def el(j, w=4 * wgs):
+            rc = readref.w2a8_readref_empty(w, ctypes.c_void_p(ob.data_ptr()), sp)
+            if rc != 0:
+                raise RuntimeError(f"empty kernel launch failed ({rc})")
+        out["empty_kernel"][str(wgs)] = run(el)
+    K = 2560
+    for m in LAUNCH_FLOOR_QUANT_M:
+        xb = torch.randn(m, K, device=dev).to(torch.bfloat16)
+        xq = torch.empty(m, K, dtype=torch.int8, device=dev)
+        sa = torch.empty(m, dtype=torch.float32, device=dev)
+
+        def ql(j, xb=xb, xq=xq, sa=sa):
+            w2a8.quant_act_int8(xb, xq, sa)
+        out["quant_act_int8_K2560"][str(m)] = run(ql)
+    return out
+
+
+def trace_summary(path):
+    """Per (kernel, grid threads, workgroup threads) of a rocprofv3 kernel
+    trace: launches and the median, mean and minimum duration (us)."""
+    import csv
+    import numpy as np
+    def size(r, name):
+        if name in r:
+            return int(r[name])
+        return int(r[name + "_X"]) * int(r[name + "_Y"]) * int(r[name + "_Z"])
+
+    per = {}
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], size(r, "Grid_Size"), size(r, "Workgroup_Size"))
+        per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = []
+    for (name, grid, wg), d in sorted(per.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        d = np.asarray(d)
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].split(" ")[-1]
+        rows.append({"kernel": short[-60:], "grid": grid, "workgroup": wg,
+                     "workgroups": grid // max(wg, 1), "launches": int(d.size),
+                     "median_us": round(float(np.median(d)), 3),
+                     "mean_us": round(float(d.mean()), 3), "min_us": round(float(d.min()), 3)})
+    return rows
 
 
 def rotation(torch, wp, nbytes):
@@ -979,14 +1055,17 @@ def read_floor_sweep(per):
 
 
 def summarize_times(s, d):
+    """Per-launch times of one shape: GB/s and % of peak follow the median,
+    as the reported time does; GBps_of_mean is the rate of the mean."""
     import numpy as np
     d = np.asarray(d, dtype=np.float64)
     return {"n": s.n, "k": s.k, "bytes": s.nbytes, "mean_us": round(float(d.mean()), 3),
             "median_us": round(float(np.median(d)), 3),
             "p10_us": round(float(np.percentile(d, 10)), 3),
             "p90_us": round(float(np.percentile(d, 90)), 3),
-            "GBps": round(s.nbytes / float(d.mean()) / 1e3, 1),
-            "pct_peak": round(100 * s.nbytes / float(d.mean()) / 1e3 / PEAK_HBM_GBPS, 1)}
+            "GBps": round(s.nbytes / float(np.median(d)) / 1e3, 1),
+            "pct_peak": round(100 * s.nbytes / float(np.median(d)) / 1e3 / PEAK_HBM_GBPS, 1),
+            "GBps_of_mean": round(s.nbytes / float(d.mean()) / 1e3, 1)}
 
 
 def main():
@@ -996,6 +1075,9 @@ def main():
         return
     if args.coldness_summary:
         print(json.dumps(write_coldness_summary(*args.coldness_summary), indent=1))
+        return
+    if args.trace_summary:
+        print(json.dumps({"trace_summary": trace_summary(args.trace_summary)}))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1021,6 +1103,12 @@ def main():
         if rr is None:
             raise RuntimeError("the plain-read measurement library is not built")
         print(json.dumps({"read_ceiling": read_ceiling(torch, rr, stream, cus)}), flush=True)
+        return
+    if args.launch_floor:
+        rr = load_readref()
+        if rr is None:
+            raise RuntimeError("the plain-read measurement library is not built")
+        print(json.dumps({"launch_floor": launch_floor(torch, w2a8, rr, stream)}), flush=True)
         return
     if args.gemm_only:
         print(json.dumps({"gemm": gemm_extras(torch, w2a8, synth, lib, stream, cus),

@@ -60,8 +60,10 @@ int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int de
  * whenever M <= 16 and K is a multiple of 16; other shapes take the
  * automatic choice.  The automatic rule, from measurements on MI355X: the
  * few-row kernel for M <= 2 up to 49152 weight tiles and for K not a multiple
- * of 16 (M <= 8); the ring kernel for the other M <= 8; the general kernel
- * for K not a multiple of 16 above that; otherwise the pipelined kernel.
+ * of 16 (M <= 8); the ring kernel for the other M <= 8, and for
+ * 9 <= M <= 16 with fewer than 3 weight strips (of 32 rows) per compute
+ * unit; the general kernel for K not a multiple of 16 above that; otherwise
+ * the pipelined kernel.
  * Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
 

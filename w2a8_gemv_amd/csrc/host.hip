@@ -163,13 +163,15 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
 
 
 // Short-batch MFMA ring kernel plan (measured on MI355X, cold weights, M = 8
-// unless noted; best of a sweep of WK 1..16, SG 1..8, depth 2..8 per shape,
+// unless noted; best of sweeps of WK 1..16, SG 1..8, depth 2..8 per shape,
 // pipelined kernel in brackets where measured):
-//  * at least two strips per CU: one wave per strip, depth 4
+//  * at least four strips per CU: one wave per strip, depth 4
 //    (55296 x 5120: 15.9 us [16.5]);
-//  * K under 40 tiles: 4 waves per strip, no split, depth 2 (4 with fewer
-//    strips than CUs) (13824 x 2560: 5.06 us [6.16], M = 4 5.04;
-//    2560 x 2560: 3.89);
+//  * K under 40 tiles, or at least 3/4 of a strip per CU: 4 waves per strip,
+//    no split, depth 2 (4 with fewer strips than CUs) (13824 x 2560:
+//    5.06 us [6.16], M = 4 5.04; 20480 x 3200: 6.44, where one wave per
+//    strip took 7.90; 6912 x 5120: 5.14, where 3 workgroups per strip took
+//    6.04; 2560 x 2560: 3.89; 5120 x 3456: 4.39);
 //  * K of 64 to 127 tiles: 4 waves and 4 workgroups per strip, depth 2
 //    (3200 x 10240: 5.77 against 6.29 with 3 workgroups of depth 4);
 //  * otherwise 4 waves and 3 workgroups per strip, depth 4 (2 from 128
@@ -178,9 +180,9 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
 void gemm_ring_plan(int64_t NS, int64_t KT, int64_t M, int cus, int64_t lds, int *wk, int *sg,
                     int *depth) {
     int64_t WK = 4, SG = 1, D = 4;
-    if (NS >= 2 * int64_t(cus)) {
+    if (NS >= 4 * int64_t(cus)) {
         WK = 1;
-    } else if (KT < 40) {
+    } else if (KT < 40 || 4 * NS >= 3 * int64_t(cus)) {
         D = NS >= cus ? 2 : 4;
     } else if (KT >= 64 && KT < 128) {
         SG = 4;
@@ -736,16 +738,19 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
     // at M = 2: 4.92 against 5.07 us for the MFMA ring kernel; 2560 x 6912:
     // 5.1 against 6.7 us for the pipelined kernel) and for ragged K (not a
     // multiple of 16); the MFMA ring kernel for the other M <= 8 (plans
-    // above); the pipelined kernel from M = 9, where the ring kernel's
-    // 16-row activation tiles (a third load per k-tile) were mixed
-    // (13824 x 2560 at M = 16: 6.5 against 6.2 us; 2560 x 6912: 6.0 against
-    // 6.6).
+    // above), and for 9 <= M <= 16 with fewer than 3 strips per CU (M = 16
+    // against the pipelined kernel: 2560 x 6912 5.89 against 6.61 us,
+    // 5120 x 27648 13.4 against 15.6, 3200 x 10240 7.24 against 8.06,
+    // 6912 x 5120 6.01 against 6.24, 20480 x 3200 8.20 against 8.45; with
+    // more strips the pipelined kernel wins: 27648 x 5120 10.8 against 13.6,
+    // 55296 x 5120 17.1 against 18.8); the pipelined kernel above that.
     const int mode = gemm_kernel_mode();
     const int64_t wtiles = int64_t(a.NS) * a.KT;
     const bool few_auto = K % 16 != 0 || (M <= 2 && wtiles <= 49152);
     const bool few = M <= kRowsMaxM && (mode == 3 || (mode == 0 && few_auto));
+    const bool ring_auto = M <= kRowsMaxM || (M <= kRingMaxM && a.NS < 3 * int64_t(dev.cus));
     const bool ring = K % 16 == 0 && !few &&
-                      ((mode == 4 && M <= kRingMaxM) || (mode == 0 && M <= kRowsMaxM));
+                      ((mode == 4 && M <= kRingMaxM) || (mode == 0 && ring_auto));
     if (few) {
         GemvLaunch g;
         g.wp = a.wp;

@@ -103,9 +103,14 @@ def parse_args():
                     help="launch an empty kernel over 1 to 1024 workgroups and the int8 "
                          "quantizer at M = 1 to 256 (K = 2560), eagerly (kernel-trace runs) "
                          "and graph-timed; prints one JSON line and exits")
-    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
-                    help="median, mean and minimum duration per (kernel, grid, workgroup) "
-                         "of a rocprofv3 --kernel-trace CSV; prints one JSON line and exits")
+    ap.add_argument("--trace-summary", nargs="+", metavar="ARG",
+                    help="KERNEL_TRACE_CSV [grid|kernel]: median, mean and minimum duration "
+                         "per (kernel, grid, workgroup), or per kernel with its registers and "
+                         "LDS, of a rocprofv3 --kernel-trace CSV; prints one JSON line and exits")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("TRACE_CSV", "A_CSV", "B_CSV"),
+                    help="batched-product counters per launch shape from a kernel trace and "
+                         "the two --pmc passes of `bench.py --gemm-only` (see "
+                         "gemm_counter_summary); prints one JSON line and exits")
     ap.add_argument("--bf16-context", action="store_true",
                     help="also time the pages' bf16 torch.matmul comparison on the sweep "
                          "shapes (context only, off by default)")
@@ -548,28 +553,110 @@ def launch_floor(torch, w2a8, readref, stream, reps=50):
     return out
 
 
-def trace_summary(path):
-    """Per (kernel, grid threads, workgroup threads) of a rocprofv3 kernel
-    trace: launches and the median, mean and minimum duration (us)."""
+def _short_kernel_name(name):
+    """A kernel's name without its namespace noise and argument list."""
+    name = name.replace("(anonymous namespace)::", "").replace("w2a8::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _dispatch_size(r, name):
+    if name in r:
+        return int(r[name])
+    return int(r[name + "_X"]) * int(r[name + "_Y"]) * int(r[name + "_Z"])
+
+
+def trace_summary(path, by="grid"):
+    """Dispatches of a rocprofv3 kernel trace, per (kernel, grid threads,
+    workgroup threads) (by="grid") or per kernel (by="kernel", with its
+    registers and LDS): launches and the median, mean and minimum duration
+    (us)."""
     import csv
     import numpy as np
-    def size(r, name):
-        if name in r:
-            return int(r[name])
-        return int(r[name + "_X"]) * int(r[name + "_Y"]) * int(r[name + "_Z"])
-
-    per = {}
+    per, info = {}, {}
     for r in csv.DictReader(open(path)):
-        key = (r["Kernel_Name"], size(r, "Grid_Size"), size(r, "Workgroup_Size"))
+        name = _short_kernel_name(r["Kernel_Name"])
+        key = (name, _dispatch_size(r, "Grid_Size"), _dispatch_size(r, "Workgroup_Size"))
+        if by == "kernel":
+            key = (name,)
+            info.setdefault(name, {"vgpr": int(r["VGPR_Count"]),
+                                   "agpr": int(r.get("Accum_VGPR_Count", 0) or 0),
+                                   "lds_bytes": int(r["LDS_Block_Size"]),
+                                   "workgroup": _dispatch_size(r, "Workgroup_Size")})
         per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     rows = []
-    for (name, grid, wg), d in sorted(per.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+    for key, d in per.items():
         d = np.asarray(d)
-        short = name.replace("(anonymous namespace)::", "").split("(")[0].split(" ")[-1]
-        rows.append({"kernel": short[-60:], "grid": grid, "workgroup": wg,
-                     "workgroups": grid // max(wg, 1), "launches": int(d.size),
-                     "median_us": round(float(np.median(d)), 3),
-                     "mean_us": round(float(d.mean()), 3), "min_us": round(float(d.min()), 3)})
+        row = {"kernel": key[0][:70]}
+        if by == "kernel":
+            row.update(info[key[0]])
+        else:
+            row.update({"grid": key[1], "workgroup": key[2], "workgroups": key[1] // max(key[2], 1)})
+        row.update({"launches": int(d.size), "median_us": round(float(np.median(d)), 3),
+                    "mean_us": round(float(d.mean()), 3), "min_us": round(float(d.min()), 3)})
+        rows.append(row)
+    if by == "kernel":
+        rows.sort(key=lambda r: -r["launches"] * r["mean_us"])
+    else:
+        rows.sort(key=lambda r: (r["kernel"], r["grid"]))
+    return rows
+
+
+def gemm_counter_summary(trace_csv, a_csv, b_csv, simds=1024, ghz=2.4):
+    """Batched-product counters per launch shape from three rocprofv3 runs of
+    `bench.py --gemm-only`: a kernel trace (durations) and two --pmc passes,
+    (a) SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES
+    SQ_INSTS_VALU_MFMA_I8 SQ_INSTS_VALU SQ_INSTS_LDS SQ_ACTIVE_INST_VALU and
+    (b) SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_ANY
+    SQ_ACTIVE_INST_ANY SQ_INSTS_SALU GRBM_GUI_ACTIVE GRBM_COUNT.  Counters are
+    averaged over the dispatches of a (kernel, grid, workgroup); MFMA busy is
+    SQ_VALU_MFMA_BUSY_CYCLES over all SIMD-cycles of the median duration."""
+    import csv
+    import numpy as np
+    dur = {}
+    for r in csv.DictReader(open(trace_csv)):
+        key = (_short_kernel_name(r["Kernel_Name"]), _dispatch_size(r, "Grid_Size"),
+               _dispatch_size(r, "Workgroup_Size"))
+        dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counters(path):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            key = (_short_kernel_name(r["Kernel_Name"]), _dispatch_size(r, "Grid_Size"),
+                   _dispatch_size(r, "Workgroup_Size"))
+            out.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        return out
+    ca, cb = counters(a_csv), counters(b_csv)
+    rows = []
+    for key, c in ca.items():
+        if "gemm" not in key[0] or key not in cb:
+            continue
+        mean = {n: float(np.mean(v)) for n, v in list(c.items()) + list(cb[key].items())}
+        mf = mean.get("SQ_INSTS_VALU_MFMA_I8", 0.0)
+        if mf <= 0:
+            continue
+        med = float(np.median(dur[key])) if key in dur else None
+        rows.append({"kernel": key[0], "grid": key[1], "workgroup": key[2],
+                     "median_us": round(med, 3) if med else None,
+                     "mfma": round(mf), "mfma_busy": round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                                           (simds * med * ghz * 1e3), 4) if med else None,
+                     "busy_cycles_per_mfma": round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / mf, 2),
+                     "other_valu_per_mfma": round((mean["SQ_INSTS_VALU"] - mf) / mf, 2),
+                     "lds_per_mfma": round(mean["SQ_INSTS_LDS"] / mf, 2),
+                     "salu_per_mfma": round(mean["SQ_INSTS_SALU"] / mf, 2),
+                     "lds_bank_conflicts": round(mean["SQ_LDS_BANK_CONFLICT"]),
+                     "waves": round(mean["SQ_WAVES"])})
+    rows.sort(key=lambda r: r["mfma"])
     return rows
 
 
@@ -1077,7 +1164,11 @@ def main():
         print(json.dumps(write_coldness_summary(*args.coldness_summary), indent=1))
         return
     if args.trace_summary:
-        print(json.dumps({"trace_summary": trace_summary(args.trace_summary)}))
+        by = args.trace_summary[1] if len(args.trace_summary) > 1 else "grid"
+        print(json.dumps({"trace_summary": trace_summary(args.trace_summary[0], by)}))
+        return
+    if args.counter_summary:
+        print(json.dumps({"gemm_counters": gemm_counter_summary(*args.counter_summary)}))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

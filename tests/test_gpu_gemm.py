@@ -186,6 +186,24 @@ def test_gemm_ring_kernel(M, N, K):
     np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
 
 
+# The automatic choice for short batches, one shape per branch of the
+# short-batch plan rule on a 256-CU device (strips = ceil(N/32), k-tiles =
+# ceil(K/128)): one wave per strip from 1024 strips; 4 waves per strip for
+# K under 40 tiles or from 192 strips; 4 workgroups per strip for 64-127
+# k-tiles; 3 otherwise; and for 9 <= M <= 16 the pipelined kernel from 768
+# strips (the first of each pair below) against the ring kernel just under.
+AUTO_SHORT = [(4, 32800, 256), (8, 20000, 3200), (8, 6900, 5120), (9, 3100, 10000),
+              (12, 2500, 6900), (16, 5000, 16400), (12, 24570, 384), (12, 24500, 384),
+              (16, 24600, 640), (16, 24530, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", AUTO_SHORT)
+def test_gemm_automatic_short_batches(M, N, K):
+    x, w = synth.gemm_case(M, N, K, seed=3 * M + N + K)
+    y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+    np.testing.assert_array_equal(y, oracle.gemm_i32_threads(x, w, ORACLE_THREADS))
+
+
 @pytest.mark.parametrize("plan", [(1, 1, 2), (1, 7, 8), (4, 3, 4), (8, 1, 6), (16, 2, 2),
                                   (2, 40, 4), (3, 5, 6), (8, 12, 8)])
 def test_gemm_ring_kernel_plans(plan):

@@ -113,9 +113,9 @@ int64_t w2a8_packed_bytes(int64_t N, int64_t K);
  * to 32 rows (the tile count and partial sum of a row whose k-range is split
  * over several workgroups), and is 0 when no launch plan splits a k-range of
  * that K (with the default knobs: K <= 47*128 = 6016), whatever the device;
- * the M = 1 entry points then accept a NULL workspace.  For 2 <= M <= 16,
+ * the M = 1 entry points then accept a NULL workspace.  For 2 <= M <= 32,
  * the larger of one such word per (row, padded output) and the split-K
- * space below; for M > 16, int32 partial sums and arrival counters of
+ * space below; for M > 32, int32 partial sums and arrival counters of
  * split-K output blocks (0 bytes when M*N is too large for split-K, which is
  * then not used).  The caller allocates it,
  * zeroes it ONCE before its first use, and may then reuse it for any call

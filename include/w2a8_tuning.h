@@ -57,13 +57,14 @@ int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int de
  * (split-K across workgroups for small outputs) always, 3 = the few-row
  * kernel (GEMV-style, dot4 on decoded weights) whenever M <= 8, 4 = the
  * short-batch MFMA ring kernel (the GEMV's weight stream feeding int8 MFMA)
- * whenever M <= 16 and K is a multiple of 16; other shapes take the
+ * whenever M <= 32 and K is a multiple of 16; other shapes take the
  * automatic choice.  The automatic rule, from measurements on MI355X: the
  * few-row kernel for M <= 2 up to 49152 weight tiles and for K not a multiple
- * of 16 (M <= 8); the ring kernel for the other M <= 8, and for
- * 9 <= M <= 16 with fewer than 3 weight strips (of 32 rows) per compute
- * unit; the general kernel for K not a multiple of 16 above that; otherwise
- * the pipelined kernel.
+ * of 16 (M <= 8); the ring kernel for the other M <= 8, for 9 <= M <= 16
+ * with fewer than 3 weight strips (of 32 rows) per compute unit, and for
+ * 17 <= M <= 32 with K of at least 192 tiles of 128 over fewer strips than
+ * compute units; the general kernel for K not a multiple of 16 above that;
+ * otherwise the pipelined kernel.
  * Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
 

@@ -170,12 +170,13 @@ def test_gemm_few_rows_fp32_epilogue_and_workspace_reset():
         assert int(ws.count_nonzero()) == 0, "workspace not left zeroed"
 
 
-# Short-batch MFMA ring kernel (2 <= M <= 16, K a multiple of 16) forced:
+# Short-batch MFMA ring kernel (2 <= M <= 32, K a multiple of 16) forced:
 # both activation tile heights (M <= 8 and 9..16), ragged N, k-tile
 # remainders, runs shorter and longer than the ring, split strips.
 RING = [(2, 1, 16), (2, 33, 144), (3, 100, 1040), (5, 64, 2560), (7, 257, 4000), (8, 2560, 6912),
         (8, 13824, 2560), (9, 31, 272), (12, 200, 10240), (16, 96, 27648), (16, 2560, 2560),
-        (4, 5000, 3200), (11, 640, 128)]
+        (4, 5000, 3200), (11, 640, 128), (17, 300, 2560), (24, 2560, 6912), (32, 700, 10240),
+        (32, 13824, 2560), (20, 64, 27648), (29, 100, 1040), (31, 33, 144)]
 
 
 @pytest.mark.parametrize("M,N,K", RING)
@@ -190,11 +191,14 @@ def test_gemm_ring_kernel(M, N, K):
 # short-batch plan rule on a 256-CU device (strips = ceil(N/32), k-tiles =
 # ceil(K/128)): one wave per strip from 1024 strips; 4 waves per strip for
 # K under 40 tiles or from 192 strips; 4 workgroups per strip for 64-127
-# k-tiles; 3 otherwise; and for 9 <= M <= 16 the pipelined kernel from 768
-# strips (the first of each pair below) against the ring kernel just under.
+# k-tiles; 3 otherwise; for 9 <= M <= 16 the pipelined kernel from 768
+# strips (the first of each pair below) against the ring kernel just under;
+# for 17 <= M <= 32 the ring kernel (32-row tiles) only from 192 k-tiles
+# under 256 strips (the last four: ring, ring, pipelined, pipelined).
 AUTO_SHORT = [(4, 32800, 256), (8, 20000, 3200), (8, 6900, 5120), (9, 3100, 10000),
               (12, 2500, 6900), (16, 5000, 16400), (12, 24570, 384), (12, 24500, 384),
-              (16, 24600, 640), (16, 24530, 640)]
+              (16, 24600, 640), (16, 24530, 640), (20, 3000, 24576), (32, 8160, 24600),
+              (24, 8200, 24600), (20, 3000, 24448)]
 
 
 @pytest.mark.parametrize("M,N,K", AUTO_SHORT)
@@ -213,12 +217,12 @@ def test_gemm_ring_kernel_plans(plan):
         w2a8.tune_gemm(4)
         w2a8.tune_gemm_ring(*plan)
         for M, N, K in [(4, 200, 3200), (8, 96, 27648), (2, 33, 1008), (16, 64, 6912),
-                        (13, 700, 2560)]:
+                        (13, 700, 2560), (32, 200, 3200), (24, 96, 27648)]:
             x, w = synth.gemm_case(M, N, K, seed=M + N + K)
             ws = torch.zeros(max(256, w2a8.workspace_bytes(M, N, K)), dtype=torch.uint8,
                              device=dev())
             wp, xd = packed_on_device(w), to_dev(x)
-            lds = plan[0] * plan[2] * 1024 * (2 if M <= 8 else 3)
+            lds = plan[0] * plan[2] * 1024 * (2 if M <= 8 else 3 if M <= 16 else 5)
             if lds > torch.cuda.get_device_properties(dev()).shared_memory_per_block:
                 # the rings do not fit a workgroup's LDS: refused, nothing launched
                 y = torch.empty(M * N, dtype=torch.int32, device=dev())

@@ -544,7 +544,7 @@ def tune_gemv_force(kernel: int, waves_per_wg: int = 1, wgs_per_strip: int = 1, 
 
 def tune_gemm(kernel: int):
     """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general,
-    3 few-row whenever M <= 8, 4 short-batch MFMA ring whenever M <= 16 and K allows."""
+    3 few-row whenever M <= 8, 4 short-batch MFMA ring whenever M <= 32 and K allows."""
     _check(lib().w2a8_tune_gemm(kernel), "w2a8_tune_gemm")
 
 

@@ -155,8 +155,11 @@ constexpr int64_t kRowsMaxM = 8;
 // Short batches on MFMA (gemm_ring.hip): 2 <= M <= kRingMaxM, K a multiple
 // of 16, the GEMV's work split (WK waves, SG workgroups per strip; split
 // strips combine per (row, output) like the few-row kernel), depth 2, 4, 6
-// or 8 tiles in flight per wave.  LDS: gemm_ring_lds_bytes per workgroup.
-constexpr int64_t kRingMaxM = 16;
+// or 8 tiles in flight per wave, activation tiles of 8, 16 or 32 rows.  LDS:
+// gemm_ring_lds_bytes per workgroup.  The automatic choice takes it up to
+// kRingAutoMaxM rows, and up to kRingMaxM rows on very long strips.
+constexpr int64_t kRingMaxM = 32;
+constexpr int64_t kRingAutoMaxM = 16;
 size_t gemm_ring_lds_bytes(int M, int wk, int depth);
 hipError_t launch_gemm_ring(const GemvLaunch &a, int depth, hipStream_t stream);
 // Fused linear GEMV: quantize the bf16 row in every workgroup, then the

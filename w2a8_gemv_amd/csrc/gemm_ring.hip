@@ -1,4 +1,4 @@
-// W2A8 batched product for short batches (2 <= M <= 16, K a multiple of 16)
+// W2A8 batched product for short batches (2 <= M <= 32, K a multiple of 16)
 // on gfx950: the GEMV's ring-pipelined weight stream feeding int8 MFMA.
 //
 // What it computes: the exact integer product of the GEMV
@@ -13,16 +13,17 @@
 // contiguous run.  Each wave keeps a ring of D tiles in flight; a tile
 // arrives by direct global->LDS loads (global_load_lds_dwordx4, 1 KiB per
 // instruction) into the wave's own ring slot: the packed weight tile, and
-// the tile's [8 or 16 rows x 128 k] activations.  The slot is read back in
-// MFMA operand order, so no barrier is needed anywhere in the stream.
+// the tile's [8, 16 or 32 rows x 128 k] activations.  The slot is read back
+// in MFMA operand order, so no barrier is needed anywhere in the stream.
 //
-// Per tile a wave issues 2 (M <= 8) or 3 load instructions, reads 4 weight
-// words and 2 activation fragments per lane from LDS, expands the words into
-// signed bytes, and issues 4 v_mfma_i32_16x16x64_i8: A = 16 activation rows
-// x 64 k, B = 64 k x 16 weight rows (two 16-row blocks j of the strip, two
-// k-halves h of the tile).  Lane l supplies row l % 16 and the 16 bytes of
-// k-group l / 16 of each operand.  With M <= 8 the activation rows 8..15 of
-// A repeat rows 0..7; their outputs are discarded.
+// Per tile a wave issues 2, 3 or 5 load instructions (M up to 8, 16, 32),
+// reads 4 weight words and 2 activation fragments per 16-row block per lane
+// from LDS, expands the words into signed bytes once, and issues 4
+// v_mfma_i32_16x16x64_i8 per 16-row block: A = 16 activation rows x 64 k,
+// B = 64 k x 16 weight rows (two 16-row blocks j of the strip, two k-halves
+// h of the tile).  Lane l supplies row l % 16 and the 16 bytes of k-group
+// l / 16 of each operand.  With M <= 8 the activation rows 8..15 of A repeat
+// rows 0..7; their outputs are discarded.
 #include "device.h"
 
 namespace w2a8 {
@@ -68,16 +69,18 @@ __device__ __forceinline__ void ring_issue(uint8_t *slot, int t, const int8_t *w
 
 // The tile in `slot` (its loads have landed): read its operands, then, once
 // the reads are done, reissue the slot with tile `refill` (REFILL), then
-// the 4 MFMAs.
-template <int XL, bool REFILL>
-__device__ __forceinline__ void ring_consume(uint8_t *slot, int refill, const int (&aoff)[2],
+// the 4*MB MFMAs (each expanded weight word serves the MB row blocks).
+template <int XL, int MB, bool REFILL>
+__device__ __forceinline__ void ring_consume(uint8_t *slot, int refill, const int (&aoff)[MB][2],
                                              const int (&boff)[2][2], const int8_t *wsrc,
-                                             const int8_t *const *xsrc, int klast, v4i (&acc)[2]) {
+                                             const int8_t *const *xsrc, int klast,
+                                             v4i (&acc)[MB][2]) {
     uint32_t bw[2][2];
-    v4i av[2];
+    v4i av[MB][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        av[h] = *reinterpret_cast<const v4i *>(slot + aoff[h]);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) av[b][h] = *reinterpret_cast<const v4i *>(slot + aoff[b][h]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) bw[j][h] = *reinterpret_cast<const uint32_t *>(slot + boff[j][h]);
     }
@@ -89,14 +92,18 @@ __device__ __forceinline__ void ring_consume(uint8_t *slot, int refill, const in
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[h], expand_word(bw[j][h]), acc[j], 0,
-                                                            0, 0);
+        for (int j = 0; j < 2; ++j) {
+            const v4i e = expand_word(bw[j][h]);
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[b][h], e, acc[b][j], 0, 0, 0);
+        }
 }
 
 template <int D, int MR>
 __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
     constexpr int XL = MR / 8;                     // activation loads per tile
+    constexpr int MB = MR <= 16 ? 1 : MR / 16;     // 16-row blocks of A per tile
     constexpr int LPT = 1 + XL;                    // load instructions per tile
     constexpr int SLOT = kTileBytes * LPT;         // LDS bytes per ring slot
     static_assert(D <= 8, "drain waits cover at most 8 tiles");
@@ -139,9 +146,9 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
 
     // Operand offsets within a slot.  B: block j (rows 16j + l%16 of the
     // strip), k-half h (k-group kg = 4h + l/16): word r&3 of lane slot
-    // 8(r>>2) + kg, stored at the permuted position.  A: row l%16, chunk
-    // 4h + l/16 (M <= 8: row l%8).
-    int boff[2][2], aoff[2];
+    // 8(r>>2) + kg, stored at the permuted position.  A, block b: row
+    // 16b + l%16, chunk 4h + l/16 (M <= 8: row l%8).
+    int boff[2][2], aoff[MB][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -153,13 +160,17 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
             boff[j][h] = (pos * 4 + (r & 3)) * 4;
         }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = lane & (MR - 1);
-        const int c = 4 * h + (lane >> 4);
-        aoff[h] = kTileBytes * (1 + (r >> 3)) + (8 * (r & 7) + (c ^ (r & 7))) * 16;
-    }
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = MR == 8 ? (lane & 7) : 16 * b + (lane & 15);
+            const int c = 4 * h + (lane >> 4);
+            aoff[b][h] = kTileBytes * (1 + (r >> 3)) + (8 * (r & 7) + (c ^ (r & 7))) * 16;
+        }
 
-    v4i acc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+    v4i acc[MB][2];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[b][0] = acc[b][1] = v4i{0, 0, 0, 0};
 
     // Fill the ring: tiles w0 .. w0+D-1 (clamped to `last`).
 #pragma unroll
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
         for (int j = 0; j < D; ++j) {
             wait_vm<(D - 1) * LPT>();
             __asm__ volatile("" ::: "memory");
-            ring_consume<XL, true>(ring + j * SLOT, min(w0 + i + D + j, last), aoff, boff, wsrc,
+            ring_consume<XL, MB, true>(ring + j * SLOT, min(w0 + i + D + j, last), aoff, boff, wsrc,
                                    xsrc, klast, acc);
         }
     }
@@ -184,14 +195,14 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
         if (i + j < n) {
             wait_vm_tiles<LPT>(D - 1 - j);
             __asm__ volatile("" ::: "memory");
-            ring_consume<XL, false>(ring + j * SLOT, -1, aoff, boff, wsrc, xsrc, klast, acc);
+            ring_consume<XL, MB, false>(ring + j * SLOT, -1, aoff, boff, wsrc, xsrc, klast, acc);
         }
     }
     // Loads issued for a run shorter than the ring may still be writing LDS.
     wait_vm<0>();
 
-    // Outputs.  acc[j][e] of lane l is element (m, c) of the strip's
-    // [MR x 32] output tile with m = 4(l/16) + e, c = 16j + l%16.  Each wave
+    // Outputs.  acc[b][j][e] of lane l is element (m, c) of the strip's
+    // [MR x 32] output tile with m = 16b + 4(l/16) + e, c = 16j + l%16.  Each wave
     // writes its tile to the start of its own ring (its loads have all
     // landed, and no other wave touches that ring), so one barrier suffices
     // before the waves read one another's tiles.  The sums are finished in
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
     {
         int *mine = reinterpret_cast<int *>(ring);
 #pragma unroll
-        for (int p = 0; p < 8; ++p) mine[p * 64 + lane] = acc[p >> 2][p & 3];
+        for (int p = 0; p < 8 * MB; ++p) mine[p * 64 + lane] = acc[p >> 3][(p >> 2) & 1][p & 3];
     }
     if (a.WK > 1) __syncthreads();
     constexpr int NI = MR / 2;
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
     for (int i = 0; i < NI; ++i) {
         const int m = 2 * i + (lane >> 5);
         st[i] = ((own >> i) & 1u) && m < a.M;
-        at[i] = (4 * (c >> 4) + (m & 3)) * 64 + 16 * (m >> 2) + (c & 15);
+        at[i] = ((2 * (m >> 4) + (c >> 4)) * 4 + (m & 3)) * 64 + 16 * ((m >> 2) & 3) + (c & 15);
         val[i] = 0;
     }
     // Sums over the waves' tiles, four waves per step with all their reads in
@@ -289,8 +300,8 @@ __global__ __launch_bounds__(1024) void gemm_ring_kernel(GemvLaunch a) {
 
 size_t gemm_ring_lds_bytes(int M, int wk, int depth) {
     // the waves' slots (at least 4 KiB per wave: they also hold the output
-    // exchange of 2 KiB per wave)
-    const int mr = M <= 8 ? 8 : 16;
+    // exchange of 2 KiB per 16 rows per wave)
+    const int mr = M <= 8 ? 8 : M <= 16 ? 16 : 32;
     return size_t(wk) * depth * kTileBytes * (1 + mr / 8);
 }
 
@@ -304,12 +315,13 @@ hipError_t launch_gemm_ring(const GemvLaunch &la, int depth, hipStream_t stream)
     a.WR0 = a.KQ % a.WK;
     a.WQ1 = (a.KQ + 1) / a.WK;
     a.WR1 = (a.KQ + 1) % a.WK;
-    const bool m8 = a.M <= 8;
+    const int mr = a.M <= 8 ? 8 : a.M <= 16 ? 16 : 32;
     void *args[] = {&a};
     const void *fn;
 #define W2A8_GRING(DD)                                                                   \
-    fn = m8 ? reinterpret_cast<const void *>(&gemm_ring_kernel<DD, 8>)                   \
-            : reinterpret_cast<const void *>(&gemm_ring_kernel<DD, 16>)
+    fn = mr == 8    ? reinterpret_cast<const void *>(&gemm_ring_kernel<DD, 8>)           \
+         : mr == 16 ? reinterpret_cast<const void *>(&gemm_ring_kernel<DD, 16>)          \
+                    : reinterpret_cast<const void *>(&gemm_ring_kernel<DD, 32>)
     switch (depth) {
     case 2: W2A8_GRING(2); break;
     case 4: W2A8_GRING(4); break;

@@ -743,12 +743,19 @@ int w2a8_gemm(const void *w_packed, const int8_t *x, int64_t M, int64_t N, int64
     // 5120 x 27648 13.4 against 15.6, 3200 x 10240 7.24 against 8.06,
     // 6912 x 5120 6.01 against 6.24, 20480 x 3200 8.20 against 8.45; with
     // more strips the pipelined kernel wins: 27648 x 5120 10.8 against 13.6,
-    // 55296 x 5120 17.1 against 18.8); the pipelined kernel above that.
+    // 55296 x 5120 17.1 against 18.8); for 17 <= M <= 32 (32-row tiles) only
+    // on strips of 192 tiles or more over fewer strips than CUs, where the
+    // pipelined kernel reads the weights once per 16-row block (M = 20:
+    // 5120 x 27648 16.6 against 19.1 us, 2560 x 27648 12.2 against 14.0; it
+    // lost at 112 and 128 tiles: 4096 x 16384 12.0 against 10.0); the
+    // pipelined kernel above that.
     const int mode = gemm_kernel_mode();
     const int64_t wtiles = int64_t(a.NS) * a.KT;
     const bool few_auto = K % 16 != 0 || (M <= 2 && wtiles <= 49152);
     const bool few = M <= kRowsMaxM && (mode == 3 || (mode == 0 && few_auto));
-    const bool ring_auto = M <= kRowsMaxM || (M <= kRingMaxM && a.NS < 3 * int64_t(dev.cus));
+    const bool ring_auto = M <= kRowsMaxM ||
+                           (M <= kRingAutoMaxM && a.NS < 3 * int64_t(dev.cus)) ||
+                           (M <= kRingMaxM && a.KT >= 192 && a.NS < int64_t(dev.cus));
     const bool ring = K % 16 == 0 && !few &&
                       ((mode == 4 && M <= kRingMaxM) || (mode == 0 && ring_auto));
     if (few) {

@@ -38,11 +38,36 @@ __device__ __forceinline__ v4i expand_word(uint32_t w) {
 
 // Sum over the 8 lanes of a row group (lanes 8j..8j+7) with DPP moves:
 // xor 1 and xor 2 inside quads, then the mirrored half-row (lane i <-> 7-i).
+// Maximum of a non-negative float over the 64 lanes of a wave, returned
+// wave-uniform: four DPP steps inside each row of 16 lanes, then the four
+// row maxima read into scalar registers.  Non-negative floats order like
+// their bit patterns read as integers.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    int b = __float_as_int(v);
+    b = max(b, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x124, 0xF, 0xF, false));  // row_ror:4
+    b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false));  // row_ror:8
+    const int r0 = __builtin_amdgcn_readlane(b, 0), r1 = __builtin_amdgcn_readlane(b, 16);
+    const int r2 = __builtin_amdgcn_readlane(b, 32), r3 = __builtin_amdgcn_readlane(b, 48);
+    return __int_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 __device__ __forceinline__ int sum8(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
     v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
     v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
     return v;
+}
+
+// Sum over the 64 lanes of a wave, returned wave-uniform: sum8 and one more
+// DPP step give each row of 16 lanes its sum, then the four row sums are
+// read into scalar registers.
+__device__ __forceinline__ int wave_sum(int v) {
+    v = sum8(v);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
 // Loads of batch b of a wave's run of 1 KiB weight tiles (tiles w0 + b*U + u,

@@ -264,13 +264,24 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
         if (tid == 0)
             for (int k = 16 * nfull; k < a.K; ++k)
                 amax = fmaxf(amax, fabsf(__uint_as_float(uint32_t(a.xb[k]) << 16)));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        float *fred = reinterpret_cast<float *>(red + a.WK * kTileRows);   // WK floats
+        amax = wave_max_nonneg(amax);
+        // across the waves: each writes its maximum, the unused entries of
+        // the 16 are zeroed, and every lane reads all 16 with four 16-byte
+        // reads
+        float *fred = reinterpret_cast<float *>(red + a.WK * kTileRows);   // 16 floats
         if (lane == 0) fred[wv] = amax;
+        if (tid >= a.WK && tid < 16) fred[tid] = 0.0f;
         __syncthreads();
-        amax = 0.0f;
-        for (int w = 0; w < a.WK; ++w) amax = fmaxf(amax, fred[w]);
+        {
+            const v4u *r4 = reinterpret_cast<const v4u *>(fred);
+            const v4u q0 = r4[0], q1 = r4[1], q2 = r4[2], q3 = r4[3];
+            float m4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m4[i] = fmaxf(fmaxf(__uint_as_float(q0[i]), __uint_as_float(q1[i])),
+                              fmaxf(__uint_as_float(q2[i]), __uint_as_float(q3[i])));
+            amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        }
         // The quantizer's scale and reciprocal; a zero row quantizes to 0.
         sa = amax / 127.0f;
         const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
@@ -304,10 +315,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
             sx = dot4(xr[j][2], 0x01010101u, sx);
             sx = dot4(xr[j][3], 0x01010101u, sx);
         }
-        sx = sum8(sx);
-        sx += __shfl_xor(sx, 8);
-        sx += __shfl_xor(sx, 16);
-        sx += __shfl_xor(sx, 32);
+        sx = wave_sum(sx);
     }
 
     // 4. Stream the run: multiply one batch while the next is in flight.
@@ -511,11 +519,7 @@ void gemv_rows_kernel(GemvLaunch a) {
         t = dot4(xr[m][1], 0x01010101u, t);
         t = dot4(xr[m][2], 0x01010101u, t);
         t = dot4(xr[m][3], 0x01010101u, t);
-        t = sum8(t);
-        t += __shfl_xor(t, 8);
-        t += __shfl_xor(t, 16);
-        t += __shfl_xor(t, 32);
-        sx[m] = t;
+        sx[m] = wave_sum(t);
     }
 
     // 4. Stream the run.

@@ -47,8 +47,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *xb, int M, i
     } else {
         for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf(lo_bf16(row[k])));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = wave_max_nonneg(amax);
     __shared__ float red[4];
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
@@ -97,15 +96,24 @@ __global__ __launch_bounds__(1024) void quant_rows_kernel(const uint16_t *xb, in
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(v[i])), fabsf(hi_bf16(v[i]))));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    __shared__ float red[16];
+    amax = wave_max_nonneg(amax);
+    // across the waves: each writes its maximum, wave 0 zeroes the unused
+    // entries, and every lane reads all 16 with four 16-byte reads
+    __shared__ __attribute__((aligned(16))) float red[16];
     const int nw = int(blockDim.x) >> 6;
     if (nw > 1) {
-        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        const int lane = tid & 63;
+        if (lane == 0) red[tid >> 6] = amax;
+        if (tid >= nw && tid < 16) red[tid] = 0.0f;
         __syncthreads();
-        amax = red[0];
-        for (int w = 1; w < nw; ++w) amax = fmaxf(amax, red[w]);
+        const v4u *r4 = reinterpret_cast<const v4u *>(red);
+        const v4u q0 = r4[0], q1 = r4[1], q2 = r4[2], q3 = r4[3];
+        float m4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m4[i] = fmaxf(fmaxf(__uint_as_float(q0[i]), __uint_as_float(q1[i])),
+                          fmaxf(__uint_as_float(q2[i]), __uint_as_float(q3[i])));
+        amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     }
     const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;   // a zero row quantizes to 0
     if (c < nc) {
@@ -136,8 +144,7 @@ __device__ __forceinline__ float row_absmax(const uint16_t *row, int K, bool vec
     } else {
         for (int k = tid; k < K; k += 256) amax = fmaxf(amax, fabsf(lo_bf16(row[k])));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = wave_max_nonneg(amax);
     __shared__ float red[4];
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();

@@ -26,14 +26,22 @@ def _bf16_dev(bits: np.ndarray) -> torch.Tensor:
     return to_dev(bits.astype(np.uint16)).view(torch.bfloat16)
 
 
+# K % 16 == 0 up to 8192 takes the one-read kernel (an odd number of 16-value
+# chunks leaves the last granule's second half to the lane after the last);
+# other K the two-pass kernel.
 @pytest.mark.parametrize("M,K", [(1, 1), (1, 7), (1, 15), (1, 16), (1, 31), (2, 33), (3, 100),
-                                 (1, 2560), (4, 4000), (1, 27648), (17, 64)])
+                                 (1, 2560), (4, 4000), (1, 27648), (17, 64), (3, 48),
+                                 (2, 8192), (5, 8176), (1, 8208), (128, 2560)])
 def test_quant_int4_matches_oracle(M, K):
     xb, _ = synth.linear_case(M, 1, K, seed=3 * M + K)
-    xq4, sa = w2a8.quant_act_int4(_bf16_dev(xb))
+    nbytes = w2a8.act4_bytes(M, K)
+    out = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device=dev())
+    xq4, sa = w2a8.quant_act_int4(_bf16_dev(xb), x_q4=out)
     torch.cuda.synchronize()
     q, osa = oracle.quant_act_a4(xb)
-    np.testing.assert_array_equal(xq4.cpu().numpy(), oracle.pack_act4(q))
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[:nbytes], oracle.pack_act4(q))
+    assert (got[nbytes:] == 0xA5).all(), "write past the end of the A4I rows"
     np.testing.assert_array_equal(sa.cpu().numpy(), osa)
 
 

@@ -210,11 +210,79 @@ __global__ __launch_bounds__(256) void quant_a4_kernel(const uint16_t *xb, int M
     if (tid == 0) sa[m] = amax / 7.0f;
 }
 
+// K % 16 == 0 and K <= 8192: one workgroup per row, one 16-value chunk per
+// lane, as quant_rows_kernel: the row is read once, its maximum taken within
+// each wave (DPP) and across the waves (LDS), and each lane quantizes the
+// chunk it holds into its 8 bytes of the A4I row.  With an odd number of
+// chunks the lane after the last writes the zero half of the last granule.
+// Same per-element operations (q4) as quant_a4_kernel.
+__global__ __launch_bounds__(1024) void quant_a4_rows_kernel(const uint16_t *xb, int M, int K,
+                                                             uint8_t *xq4, float *sa) {
+    const int tid = int(threadIdx.x);
+    const int m = int(blockIdx.x);
+    const int nc = K >> 4;                        // 16-value chunks of the row
+    const int G = (K + 31) / 32;                  // 32-value granules (16 bytes each)
+    const v4u *r8 = reinterpret_cast<const v4u *>(xb + int64_t(m) * K);
+    v2u *o8 = reinterpret_cast<v2u *>(xq4 + int64_t(m) * G * 16);
+    v4u a = v4u{0u, 0u, 0u, 0u}, b = v4u{0u, 0u, 0u, 0u};
+    if (tid < nc) {
+        a = r8[2 * tid];
+        b = r8[2 * tid + 1];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(a[j])), fabsf(hi_bf16(a[j]))));
+        amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(b[j])), fabsf(hi_bf16(b[j]))));
+    }
+    amax = wave_max_nonneg(amax);
+    __shared__ __attribute__((aligned(16))) float red[16];
+    const int nw = int(blockDim.x) >> 6;
+    if (nw > 1) {
+        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        if (tid >= nw && tid < 16) red[tid] = 0.0f;
+        __syncthreads();
+        const v4u *r4 = reinterpret_cast<const v4u *>(red);
+        const v4u q0 = r4[0], q1 = r4[1], q2 = r4[2], q3 = r4[3];
+        float m4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m4[i] = fmaxf(fmaxf(__uint_as_float(q0[i]), __uint_as_float(q1[i])),
+                          fmaxf(__uint_as_float(q2[i]), __uint_as_float(q3[i])));
+        amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    }
+    const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+    if (tid < nc) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = lo_bf16(a[j]);
+            v[2 * j + 1] = hi_bf16(a[j]);
+            v[8 + 2 * j] = lo_bf16(b[j]);
+            v[8 + 2 * j + 1] = hi_bf16(b[j]);
+        }
+        uint32_t w0, w1;
+        chunk_a4(v, inv, w0, w1);
+        o8[tid] = v2u{w0, w1};
+    } else if (tid == nc && (nc & 1)) {
+        o8[tid] = v2u{0u, 0u};
+    }
+    if (tid == 0) sa[m] = amax / 7.0f;
+}
+
 }  // namespace
 
+// K % 16 == 0 and K <= 8192: one workgroup of ceil((chunks + 1) / 64) waves
+// per row, one 16-value chunk per lane (quant_a4_rows_kernel).  Other K: one
+// 256-thread workgroup per row, two passes (quant_a4_kernel).
 hipError_t launch_quant_a4(const uint16_t *xb, int M, int K, uint8_t *xq4, float *sa,
                            hipStream_t stream) {
     void *args[] = {const_cast<uint16_t **>(&xb), &M, &K, &xq4, &sa};
+    if ((K & 15) == 0 && K <= 8192) {
+        const int waves = (K / 16 + 1 + 63) / 64;
+        return hipLaunchKernel(reinterpret_cast<const void *>(&quant_a4_rows_kernel),
+                               dim3(unsigned(M)), dim3(unsigned(64 * waves)), args, 0, stream);
+    }
     return hipLaunchKernel(reinterpret_cast<const void *>(&quant_a4_kernel), dim3(unsigned(M)),
                            dim3(256), args, 0, stream);
 }

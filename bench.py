@@ -867,7 +867,8 @@ def a4_extras(torch, w2a8, synth, lib, stream):
     """W2A4 variant (int4 activations): per sweep shape and large shape, cold,
     the W2A4 GEMV and the W2A8 GEMV over the same rotation of weight copies
     (one launch per copy per graph), and the whole int4 layer at 13824 x 2560
-    (quant_act_int4 + w2a4_gemv with the fp32 epilogue)."""
+    (quant_act_int4 + w2a4_gemv with the fp32 epilogue, then w2a4_linear_gemv
+    in one launch)."""
     import numpy as np
     vp, F = ctypes.c_void_p, ctypes.c_float
     sp = vp(stream.cuda_stream)
@@ -932,7 +933,20 @@ def a4_extras(torch, w2a8, synth, lib, stream):
     tl = graph_times(torch, layer, max(12, len(ptrs)), stream)
     out["linear_13824x2560_layer_us"] = round(sorted(tl)[len(tl) // 2], 3)
     out["linear"] = "quant_act_int4 + w2a4_gemv with fp32 epilogue, two launches"
-    del copies, ptrs, wp, xd, x4, sa, yf, ws
+    yfu = torch.empty(n, dtype=torch.float32, device=stream.device)
+
+    def fused(j):
+        rc = lib.w2a4_linear_gemv(ptrs[j % len(ptrs)], vp(xd.data_ptr()), n, k, F(float(sw)),
+                                  vp(yfu.data_ptr()), None, vp(ws.data_ptr()), ws.numel(), sp)
+        if rc != 0:
+            raise RuntimeError(f"w2a4_linear_gemv failed with status {rc}")
+    tf = graph_times(torch, fused, max(12, len(ptrs)), stream)
+    stream.synchronize()
+    if not torch.equal(yf, yfu):
+        raise RuntimeError("w2a4_linear_gemv differs from quant_act_int4 + w2a4_gemv")
+    out["linear_13824x2560_fused_us"] = round(sorted(tf)[len(tf) // 2], 3)
+    out["fused"] = "w2a4_linear_gemv: the same layer in one launch (bit-identical, checked)"
+    del copies, ptrs, wp, xd, x4, sa, yf, yfu, ws
     torch.cuda.empty_cache()
     return out
 

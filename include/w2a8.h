@@ -306,6 +306,19 @@ int w2a4_gemv(const void *w_packed, const uint8_t *x_q4, int64_t N, int64_t K,
               int32_t *y_i32, const float *s_a, float s_w, float *y_f32,
               void *workspace, int64_t ws_bytes, void *stream);
 
+/* W2A4 linear layer for one token, in one launch: the result of
+ * quant_act_int4 (M = 1) followed by w2a4_gemv with its fp32 epilogue,
+ * bit-identical to that pair.  Every workgroup takes the row maximum and
+ * quantizes the part of the row its waves consume into LDS, so the int4 row
+ * never goes through memory.
+ * x_bf16: device, bf16 [K] bit patterns, 16-byte aligned.  y_f32: device,
+ * fp32 [N] (required).  y_i32: device, int32 [N] of the integer product, or
+ * NULL.  w_packed, N, K, s_w, workspace, ws_bytes, stream: as w2a4_gemv
+ * (same workspace size). */
+int w2a4_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, int64_t K,
+                     float s_w, float *y_f32, int32_t *y_i32, void *workspace,
+                     int64_t ws_bytes, void *stream);
+
 /* W2A8 batched product, M >= 1 (prefill).
  * [TEST] "限制与注意事项": the reference handles only M == 1; this entry
  * computes the same product for M token rows:

@@ -7,6 +7,7 @@ with exactly one invalid argument, which the library rejects before it makes
 any HIP call (the fake pointers below are never dereferenced).
 """
 import ctypes
+import functools
 import glob
 import os
 import re
@@ -247,14 +248,16 @@ def test_gemm_validation():
     assert _gemm(wsb=w2a8.workspace_bytes(8, 64, 256) - 1) == ST["BUFSIZE"]
 
 
-def _linear(**kw):
+def _linear(entry="w2a8_linear_gemv", **kw):
     a = dict(wp=FAKE, xb=FAKE, N=64, K=KS, sw=1.0, yf=FAKE, y=FAKE, ws=FAKE, wsb=1 << 20)
     a.update(kw)
-    return w2a8.lib().w2a8_linear_gemv(a["wp"], a["xb"], a["N"], a["K"], F(a["sw"]), a["yf"],
-                                       a["y"], a["ws"], a["wsb"], None)
+    return getattr(w2a8.lib(), entry)(a["wp"], a["xb"], a["N"], a["K"], F(a["sw"]), a["yf"],
+                                      a["y"], a["ws"], a["wsb"], None)
 
 
-def test_linear_gemv_validation():
+@pytest.mark.parametrize("entry", ["w2a8_linear_gemv", "w2a4_linear_gemv"])
+def test_linear_gemv_validation(entry):
+    _linear = functools.partial(globals()["_linear"], entry)
     assert _linear(wp=None) == ST["NULL"]
     assert _linear(xb=None) == ST["NULL"]
     assert _linear(yf=None) == ST["NULL"]          # the fp32 output is required

@@ -149,3 +149,119 @@ def test_linear_a4_layer(N, K):
     q, sa = oracle.quant_act_a4(xb)
     ref = oracle.epilogue(oracle.gemm_i32(q, wq), sa, sw)
     np.testing.assert_array_equal(y.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# fused int4 linear layer (w2a4_linear_gemv): bit-identical to the oracle's
+# int4 quantizer, integer product and epilogue, and to the two-launch path
+# ---------------------------------------------------------------------------
+def _fused_a4(xb, wq, N, K, sw, workspace=None):
+    wp = packed_on_device(wq)
+    yf = guarded(N, torch.float32)
+    yi = guarded(N, torch.int32)
+    w2a8.w2a4_linear_gemv(wp, _bf16_dev(xb.reshape(-1)), N, K, float(sw), yf[:N],
+                          y_i32=yi[:N], workspace=workspace)
+    torch.cuda.synchronize()
+    check_guard(yf, N)
+    check_guard(yi, N)
+    return yf[:N].cpu().numpy(), yi[:N].cpu().numpy()
+
+
+def _a4_ref(xb, wq, sw):
+    q, sa = oracle.quant_act_a4(xb.reshape(1, -1))
+    acc = oracle.gemm_i32(q, wq)
+    return oracle.epilogue(acc, sa, sw)[0], acc[0]
+
+
+# K < 8 and K % 8 != 0 (the row maximum's scalar tail), K % 16 != 0 (the last
+# chunk of a run read value by value), K % 32 != 0 (padding), strips split over
+# workgroups (K = 27648, 10240), per-wave runs and shared k-ranges (one wave
+# per strip; 2600 x 6912 and 16448 x 9000 leave the last workgroup with strips
+# past N).
+FUSED_A4_SHAPES = [(5, 1), (33, 7), (64, 15), (300, 16), (97, 100), (129, 129), (2, 130),
+                   (40, 4000), (1000, 2560), (2560, 6912), (2600, 6912), (3200, 10240),
+                   (5120, 27648), (96, 27648), (700, 8195), (13824, 2560), (55296, 5120)]
+
+
+@pytest.mark.parametrize("N,K", FUSED_A4_SHAPES)
+def test_w2a4_linear_gemv_matches_oracle(N, K):
+    xb, _ = synth.linear_case(1, 1, K, seed=N + 5 * K)
+    _, wq = synth.gemv_case(N, K, seed=N + K, sparse=N % 2 == 1)
+    sw = np.float32(0.0137)
+    yf, yi = _fused_a4(xb, wq, N, K, sw)
+    ref, acc = _a4_ref(xb, wq, sw)
+    np.testing.assert_array_equal(yi, acc)
+    np.testing.assert_array_equal(yf, ref)
+
+
+def test_w2a4_linear_gemv_zero_and_single_value_rows():
+    N, K = 300, 1000
+    _, wq = synth.gemv_case(N, K, seed=4)
+    for row in (np.zeros(K, np.float32), np.eye(1, K, 517, dtype=np.float32)[0] * -3.5,
+                np.full(K, 2.0, np.float32)):
+        xb = synth.fp32_to_bf16_bits(row.reshape(1, K))
+        yf, yi = _fused_a4(xb, wq, N, K, np.float32(0.5))
+        ref, acc = _a4_ref(xb, wq, np.float32(0.5))
+        np.testing.assert_array_equal(yi, acc)
+        np.testing.assert_array_equal(yf, ref)
+
+
+# Runs longer than the fused kernel's LDS regions hold (64 tiles): more waves
+# (unsplit long strips: 600 tiles; one wave per strip on 514 strips: 71
+# tiles), and more workgroups per strip beyond 1024 tiles.
+@pytest.mark.parametrize("policy,N,K", [((1, 32, 8, 256, 10 ** 6), 64, 76800),
+                                        ((1, 32, 8, 256, 10 ** 6), 40, 140000),
+                                        (None, 16448, 9000)])
+def test_w2a4_linear_gemv_long_runs(policy, N, K):
+    try:
+        if policy is not None:
+            w2a8.tune_gemv(*policy)
+        xb, _ = synth.linear_case(1, 1, K, seed=K)
+        _, wq = synth.gemv_case(N, K, seed=N)
+        yf, yi = _fused_a4(xb, wq, N, K, np.float32(0.02))
+        ref, acc = _a4_ref(xb, wq, np.float32(0.02))
+        np.testing.assert_array_equal(yi, acc)
+        np.testing.assert_array_equal(yf, ref)
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+@pytest.mark.parametrize("policy", [(1, 32, 8, 256, 10 ** 6), (64, 1, 8, 256, 1),
+                                    (2, 2, 8, 7, 1), (16, 32, 4, 1, 1)])
+def test_w2a4_linear_gemv_forced_splits(policy):
+    try:
+        w2a8.tune_gemv(*policy)
+        for N, K in [(200, 3200), (96, 27648), (33, 1000)]:
+            xb, _ = synth.linear_case(1, 1, K, seed=K + 1)
+            _, wq = synth.gemv_case(N, K, seed=N + 1)
+            yf, yi = _fused_a4(xb, wq, N, K, np.float32(0.02))
+            ref, acc = _a4_ref(xb, wq, np.float32(0.02))
+            np.testing.assert_array_equal(yi, acc)
+            np.testing.assert_array_equal(yf, ref)
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+def test_w2a4_linear_gemv_workspace_left_zeroed():
+    N, K = 500, 27648
+    xb, _ = synth.linear_case(1, 1, K, seed=12)
+    _, wq = synth.gemv_case(N, K, seed=13)
+    ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
+    ref, acc = _a4_ref(xb, wq, np.float32(0.25))
+    for _ in range(3):
+        yf, yi = _fused_a4(xb, wq, N, K, np.float32(0.25), workspace=ws)
+        np.testing.assert_array_equal(yi, acc)
+        np.testing.assert_array_equal(yf, ref)
+    assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("N,K", [(13824, 2560), (5120, 27648), (64, 33)])
+def test_w2a4_fused_equals_two_launch_path(N, K):
+    xb, W = synth.linear_case(1, N, K, seed=N * 3 + K)
+    wq, sw = oracle.ternarize_absmean(W)
+    wp = packed_on_device(wq)
+    x = _bf16_dev(xb.reshape(-1))
+    a = w2a8.linear_a4(x, wp, float(sw), N, K, fused=True)
+    b = w2a8.linear_a4(x, wp, float(sw), N, K, fused=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())

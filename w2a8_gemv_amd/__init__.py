@@ -24,7 +24,7 @@ __all__ = [
     "w2a8_gemv", "w2a8_gemv_noalloc", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
     "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "DEFAULT_GEMV_POLICY",
     "tune_gemm", "tune_gemm_ring",
-    "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
+    "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv", "w2a4_linear_gemv",
     "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
 ]
 
@@ -87,6 +87,8 @@ def lib():
         L.quant_act_int4.restype = I32
         L.w2a4_gemv.argtypes = [P, P, I64, I64, P, P, F32, P, P, I64, P]
         L.w2a4_gemv.restype = I32
+        L.w2a4_linear_gemv.argtypes = [P, P, I64, I64, F32, P, P, P, I64, P]
+        L.w2a4_linear_gemv.restype = I32
         L.w2a8_gemv_grouped.argtypes = [I32, P, P, I64, P, P, P, P, P, P, I64, P]
         L.w2a8_gemv_grouped.restype = I32
         L.w2a8_linear_gemv_grouped.argtypes = [I32, P, P, I64, P, P, P, P, P, I64, P]
@@ -398,9 +400,39 @@ def w2a4_gemv(w_packed, x_q4, N, K, y_i32=None, s_a=None, s_w=1.0, y_f32=None,
            "w2a4_gemv")
 
 
-def linear_a4(x_bf16, w_packed, s_w, N, K, stream=None):
-    """W2A4 linear layer for one token: quant_act_int4, then w2a4_gemv with the
-    fp32 epilogue (two launches, no host synchronisation) -> fp32 [1, N]."""
+def w2a4_linear_gemv(w_packed, x_bf16, N, K, s_w, y_f32, y_i32=None, workspace=None,
+                     stream=None):
+    """Raw C-ABI call: fused int4 quantize + W2A4 GEMV + fp32 epilogue for one token."""
+    _need(w_packed, "w_packed", torch.uint8, "cuda")
+    if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not x_bf16.is_cuda:
+        raise TypeError("x_bf16 must be a bfloat16 (or 16-bit bit pattern) CUDA tensor")
+    if not x_bf16.is_contiguous() or x_bf16.numel() != K:
+        raise ValueError("x_bf16 must be contiguous with K elements")
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("w_packed is smaller than packed_bytes(N, K)")
+    _need(y_f32, "y_f32", torch.float32, "cuda")
+    if y_f32.numel() != N:
+        raise ValueError("y_f32 must have N elements")
+    if y_i32 is not None:
+        _need(y_i32, "y_i32", torch.int32, "cuda")
+        if y_i32.numel() != N:
+            raise ValueError("y_i32 must have N elements")
+    ws = _ws(workspace_bytes(1, N, K), x_bf16.device, stream, workspace)
+    _check(lib().w2a4_linear_gemv(_ptr(w_packed), _ptr(x_bf16), N, K, ctypes.c_float(s_w),
+                                  _ptr(y_f32), _ptr(y_i32), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream_handle(stream)),
+           "w2a4_linear_gemv")
+
+
+def linear_a4(x_bf16, w_packed, s_w, N, K, stream=None, fused=True):
+    """W2A4 linear layer for one token -> fp32 [1, N].  fused=True:
+    w2a4_linear_gemv (one launch); otherwise quant_act_int4, then w2a4_gemv
+    with the fp32 epilogue (two launches, no host synchronisation).  Both
+    routes give bit-identical results."""
+    if fused:
+        y = torch.empty((1, N), dtype=torch.float32, device=x_bf16.device)
+        w2a4_linear_gemv(w_packed, x_bf16.reshape(-1), N, K, s_w, y.view(-1), stream=stream)
+        return y
     xq4, sa = quant_act_int4(x_bf16.reshape(1, -1), stream=stream)
     y = torch.empty((1, N), dtype=torch.float32, device=x_bf16.device)
     w2a4_gemv(w_packed, xq4, N, K, s_a=sa, s_w=s_w, y_f32=y.view(-1), stream=stream)

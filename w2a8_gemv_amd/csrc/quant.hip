@@ -151,26 +151,6 @@ __device__ __forceinline__ float row_absmax(const uint16_t *row, int K, bool vec
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// q = clamp(round_half_even(x * inv), -7, 7) as a two's complement nibble.
-__device__ __forceinline__ uint32_t q4(float x, float inv) {
-    float r = __builtin_rintf(x * inv);
-    r = fminf(fmaxf(r, -7.0f), 7.0f);
-    return uint32_t(int(r)) & 15u;
-}
-
-// Two 32-bit words of one 16-value chunk in the A4I layout: byte j of the
-// first word holds values j (low nibble) and 8 + j (high), byte j of the
-// second word values 4 + j and 12 + j.
-__device__ __forceinline__ void chunk_a4(const float (&v)[16], float inv, uint32_t &w0,
-                                         uint32_t &w1) {
-    w0 = w1 = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        w0 |= (q4(v[j], inv) | (q4(v[8 + j], inv) << 4)) << (8 * j);
-        w1 |= (q4(v[4 + j], inv) | (q4(v[12 + j], inv) << 4)) << (8 * j);
-    }
-}
-
 // One 256-thread workgroup per row; each thread writes 32-value granules
 // (16 bytes).  Values past K are written as zero nibbles.
 __global__ __launch_bounds__(256) void quant_a4_kernel(const uint16_t *xb, int M, int K,

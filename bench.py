@@ -776,6 +776,68 @@ def linear_extras(torch, w2a8, synth, lib, stream):
     return out
 
 
+def linear_large_extras(torch, w2a8, synth, lib, stream):
+    """The whole linear layer for one token on the two large matrices, cold:
+    quant_act_int8 + w2a8_gemv (two launches) against w2a8_linear_gemv, and
+    w2a4_linear_gemv (int4 activations), one launch each.  The fused outputs
+    are checked bit for bit against the two-launch path."""
+    import numpy as np
+    vp, F = ctypes.c_void_p, ctypes.c_float
+    sp = vp(stream.cuda_stream)
+    out = []
+    for n, k in ((5120, 27648), (55296, 5120)):
+        xb, W = synth.linear_case(1, n, k, synth.LINEAR_SEEDS[1])
+        wq, sw = w2a8.ternarize_absmean(torch.from_numpy(W))
+        del W
+        wp = w2a8.pack_ternary(wq).to(stream.device)
+        copies = rotation(torch, wp, wp.numel())
+        ptrs = [vp(c.data_ptr()) for c in copies]
+        xd = torch.from_numpy(xb.view(np.int16)).to(stream.device)
+        xq = torch.empty(k, dtype=torch.int8, device=stream.device)
+        sa = torch.empty(1, dtype=torch.float32, device=stream.device)
+        y2, yf, y4 = (torch.empty(n, dtype=torch.float32, device=stream.device) for _ in range(3))
+        ws = torch.zeros(max(256, w2a8.workspace_bytes(1, n, k)), dtype=torch.uint8,
+                         device=stream.device)
+
+        def two(j):
+            rc = lib.quant_act_int8(vp(xd.data_ptr()), 1, k, vp(xq.data_ptr()),
+                                    vp(sa.data_ptr()), sp)
+            if rc == 0:
+                rc = lib.w2a8_gemv(ptrs[j % len(ptrs)], vp(xq.data_ptr()), n, k, None,
+                                   vp(sa.data_ptr()), F(float(sw)), vp(y2.data_ptr()),
+                                   vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"two-launch layer failed with status {rc}")
+
+        def fused(j):
+            rc = lib.w2a8_linear_gemv(ptrs[j % len(ptrs)], vp(xd.data_ptr()), n, k,
+                                      F(float(sw)), vp(yf.data_ptr()), None,
+                                      vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a8_linear_gemv failed with status {rc}")
+
+        def fused4(j):
+            rc = lib.w2a4_linear_gemv(ptrs[j % len(ptrs)], vp(xd.data_ptr()), n, k,
+                                      F(float(sw)), vp(y4.data_ptr()), None,
+                                      vp(ws.data_ptr()), ws.numel(), sp)
+            if rc != 0:
+                raise RuntimeError(f"w2a4_linear_gemv failed with status {rc}")
+        reps = max(24, len(ptrs))
+        med = {}
+        for nm, fn in (("two_launch_us", two), ("fused_us", fused), ("fused_int4_us", fused4)):
+            t = graph_times(torch, fn, reps, stream)
+            med[nm] = round(sorted(t)[len(t) // 2], 3)
+        stream.synchronize()
+        if not torch.equal(y2, yf):
+            raise RuntimeError("w2a8_linear_gemv differs from quant_act_int8 + w2a8_gemv")
+        fbytes = 2 * k + n * k // 4 + 4 * n
+        out.append({"n": n, "k": k, **med, "rotation_copies": len(ptrs),
+                    "fused_GBps": round(fbytes / med["fused_us"] / 1e3, 1)})
+        del copies, ptrs, wp, xd, xq, sa, y2, yf, y4, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 # Decode projections of a 2560-wide layer that share one activation row:
 # query/key/value (2560 + 640 + 640 rows) and gate/up (2 x 6912 rows).
 GROUP_SETS = {"qkv": ([2560, 640, 640], 2560), "gate_up": ([6912, 6912], 2560)}
@@ -1345,6 +1407,7 @@ def main():
         out["detail"]["gemm"] = gemm_extras(torch, w2a8, synth, lib, stream, cus)
         out["detail"]["gemm_peak_int8_TOPS"] = PEAK_INT8_TOPS
         out["detail"]["linear_13824x2560"] = linear_extras(torch, w2a8, synth, lib, stream)
+        out["detail"]["linear_large"] = linear_large_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["grouped_decode"] = grouped_extras(torch, w2a8, synth, lib, stream)
         out["detail"]["w2a4"] = a4_extras(torch, w2a8, synth, lib, stream)
         if per and args.bf16_context:

@@ -14,7 +14,7 @@ import oracle
 import synth
 import w2a8_gemv_amd as w2a8
 
-from gpu_util import dev, to_dev
+from gpu_util import check_guard, dev, guarded, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -101,17 +101,22 @@ def test_full_linear_layer(M, fused):
 # ---------------------------------------------------------------------------
 def _fused_dev(xb, wq, N, K, sw):
     wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
-    yf = torch.full((N,), float("nan"), dtype=torch.float32, device=dev())
-    yi = torch.full((N,), -7, dtype=torch.int32, device=dev())
-    w2a8.w2a8_linear_gemv(wp, _bf16_dev(xb.reshape(-1)), N, K, float(sw), yf, y_i32=yi)
+    yf = guarded(N, torch.float32)
+    yi = guarded(N, torch.int32)
+    w2a8.w2a8_linear_gemv(wp, _bf16_dev(xb.reshape(-1)), N, K, float(sw), yf[:N], y_i32=yi[:N])
     torch.cuda.synchronize()
-    return yf.cpu().numpy(), yi.cpu().numpy()
+    check_guard(yf, N)
+    check_guard(yi, N)
+    return yf[:N].cpu().numpy(), yi[:N].cpu().numpy()
 
 
-# ragged K (K % 16 != 0, K < 16, K = 1), split strips (K = 27648, 10240),
-# several workgroup shapes
+# ragged K (K % 16 != 0, K < 16, K = 1, K % 8 != 0), split strips (K = 27648,
+# 10240), per-wave runs and shared k-ranges (one wave per strip: split strips
+# and many strips; 2600 x 6912 and 16448 x 3000 leave the last workgroup with
+# strips past N)
 FUSED_SHAPES = [(1000, 2560), (97, 100), (33, 7), (5, 1), (64, 15), (300, 16), (129, 129),
-                (2560, 6912), (3200, 10240), (5120, 27648), (40, 4000), (2, 130)]
+                (2560, 6912), (2600, 6912), (3200, 10240), (5120, 27648), (40, 4000), (2, 130),
+                (700, 8195), (13824, 2560), (55296, 5120), (16448, 3000), (20480, 3200)]
 
 
 @pytest.mark.parametrize("N,K", FUSED_SHAPES)
@@ -150,6 +155,38 @@ def test_fused_linear_gemv_forced_splits(policy):
             np.testing.assert_array_equal(yf, ref[0])
     finally:
         w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+# Runs longer than the fused kernel's LDS regions hold (32 tiles per wave):
+# more waves (unsplit long strips: 600 tiles), and more workgroups per strip
+# beyond 512 tiles (shared k-ranges: 1094 tiles over 2 or more workgroups).
+@pytest.mark.parametrize("policy,N,K", [((1, 32, 8, 256, 10 ** 6), 64, 76800),
+                                        ((1, 32, 8, 256, 10 ** 6), 40, 140000),
+                                        (None, 16448, 70000)])
+def test_fused_linear_gemv_long_runs(policy, N, K):
+    try:
+        if policy is not None:
+            w2a8.tune_gemv(*policy)
+        xb, _ = synth.linear_case(1, 1, K, seed=K)
+        _, wq = synth.gemv_case(N, K, seed=N)
+        yf, yi = _fused_dev(xb, wq, N, K, np.float32(0.02))
+        ref, acc = _linear_ref(xb, wq, np.float32(0.02))
+        np.testing.assert_array_equal(yi, acc[0])
+        np.testing.assert_array_equal(yf, ref[0])
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+
+
+@pytest.mark.parametrize("N,K", [(13824, 2560), (5120, 27648), (55296, 5120), (64, 33)])
+def test_fused_equals_two_launch_shapes(N, K):
+    xb, W = synth.linear_case(1, N, K, seed=N * 5 + K)
+    wq, sw = oracle.ternarize_absmean(W)
+    wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
+    x = _bf16_dev(xb)
+    a = w2a8.linear(x, wp, float(sw), N, K, fused=True)
+    b = w2a8.linear(x, wp, float(sw), N, K, fused=False)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
 def test_fused_equals_two_launch_path():

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "linear_ring.h"
 #include "w2a8_tuning.h"
 
 namespace w2a8 {
@@ -560,8 +561,26 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
     a.K = int(K);
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
-    gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
-    hipError_t e = launch_gemv_fused(a, static_cast<hipStream_t>(stream));
+    // Where the ring plan has one wave per strip (many strips, or long strips
+    // split over workgroups): the ring kernel over shared k-ranges; otherwise
+    // the workgroup kernel's fused variant.  Measured on MI355X (cold, graph
+    // of launches, us; ring / workgroup / quant_act_int8 + w2a8_gemv):
+    // 5120 x 27648 10.23 / 18.97 / 15.60; 55296 x 5120 13.46 / 19.03 / 14.96;
+    // 2560 x 6912 4.05 / 5.82 / 5.84; 3200 x 10240 5.58 / 7.20 / 7.84;
+    // 20480 x 3200 6.33 / 6.80 / 7.30.  With several waves per strip the
+    // workgroup kernel wins: 13824 x 2560 5.22 against 5.62 (ring, per-wave
+    // runs), 2560 x 2560 3.83 against 3.94.
+    hipError_t e;
+    int depth = 4;
+    gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
+    if (a.WK == 1) {
+        fused_ring_plan(&a, 0, kLinearSharedMaxRun);   // one wave per strip: shared k-ranges
+        a.unroll = depth;
+        e = launch_linear_ring(a, depth, static_cast<hipStream_t>(stream));
+    } else {
+        gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
+        e = launch_gemv_fused(a, static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 

@@ -4,6 +4,7 @@
 #include <algorithm>
 
 #include "a4.h"
+#include "linear_ring.h"
 
 namespace w2a8 {
 namespace {
@@ -15,53 +16,6 @@ bool shape_ok(int64_t N, int64_t K) {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Plan of the fused kernel, from the ring plan (launch fields WK, SG, RUN;
-// returns `shared`).
-//  * One wave per strip (many strips, or long strips split over
-//    workgroups): WS strips per workgroup share one quantized k-range, so
-//    the row's maximum and quantization are done once per WS strips.  WS = 8
-//    when the strips fill the workgroups (at most 1/32 of the waves idle)
-//    and, unsplit, there are at least 1536 strips; otherwise 4.  A split
-//    strip with fewer than 200 such workgroups takes twice the k-ranges.
-//    Measured on MI355X (cold, graph of launches, us; WS x k-range factor):
-//    2560 x 6912: 8x2 3.88, 8x1 3.97, 4x1 4.67; 5120 x 27648: 8x2 9.99,
-//    4x1 10.32, 8x1 11.56; 13824 x 6912: 8x2 6.73, 4x1 7.71;
-//    3200 x 10240 (100 strips): 4x1 5.38, 8x1 5.55, 8x2 5.83;
-//    55296 x 5120: 8 13.17, 4 13.78, 16 17.5; 20480 x 3200: 4 5.77,
-//    8 7.43, 2 7.77.  K-ranges hold at most kA4SharedMaxRun tiles.
-//  * Otherwise each wave quantizes its own run into its LDS region: runs
-//    capped at kA4FusedMaxRun tiles, with more waves first (up to 16) and
-//    then more workgroups per strip.
-// More workgroups per strip than the ring plan's only for split strips or
-// for strips longer than 16 * kA4FusedMaxRun tiles, which exceed every
-// k-range bound, so the workspace rule of the unfused GEMV still holds.
-bool fused_plan(GemvLaunch *a) {
-    const int64_t NS = a->NS, KT = a->KT;
-    if (a->WK == 1) {
-        int64_t SG = a->SG;
-        const bool fill8 = cdiv(NS, 8) * 8 - NS <= NS / 32;
-        const int64_t WS = std::min<int64_t>(NS, fill8 && (SG > 1 || NS >= 1536) ? 8 : 4);
-        if (SG > 1 && cdiv(NS, WS) * SG < 200) SG = std::min(KT, 2 * SG);
-        if (cdiv(KT, SG) > kA4SharedMaxRun) SG = cdiv(KT, kA4SharedMaxRun);
-        a->SG = int(SG);
-        a->WK = int(WS);
-        a->RUN = int(cdiv(KT, SG));
-        return true;
-    }
-    if (a->RUN <= kA4FusedMaxRun) return false;
-    int64_t SG = a->SG;
-    int64_t ktw = cdiv(KT, SG);
-    if (ktw > 16 * kA4FusedMaxRun) {
-        SG = cdiv(KT, 16 * kA4FusedMaxRun);
-        ktw = cdiv(KT, SG);
-    }
-    const int64_t WK = std::min<int64_t>(16, std::max<int64_t>(a->WK, cdiv(ktw, kA4FusedMaxRun)));
-    a->SG = int(SG);
-    a->WK = int(WK);
-    a->RUN = int(cdiv(ktw, WK));
-    return false;
-}
 
 }  // namespace
 }  // namespace w2a8
@@ -187,7 +141,7 @@ int w2a4_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
     a.NS = int(Np / kTileRows);
     int depth = 4;
     gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
-    const bool shared = fused_plan(&a);
+    const bool shared = fused_ring_plan(&a, kA4FusedMaxRun, kA4SharedMaxRun);
     a.unroll = depth;
     hipError_t e = launch_gemv_a4_fused(a, depth, shared, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;

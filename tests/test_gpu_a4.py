@@ -26,12 +26,15 @@ def _bf16_dev(bits: np.ndarray) -> torch.Tensor:
     return to_dev(bits.astype(np.uint16)).view(torch.bfloat16)
 
 
-# K % 16 == 0 up to 8192 takes the one-read kernel (an odd number of 16-value
+# K % 16 == 0 up to 32768 takes the one-read kernel (an odd number of 16-value
 # chunks leaves the last granule's second half to the lane after the last);
 # other K the two-pass kernel.
 @pytest.mark.parametrize("M,K", [(1, 1), (1, 7), (1, 15), (1, 16), (1, 31), (2, 33), (3, 100),
                                  (1, 2560), (4, 4000), (1, 27648), (17, 64), (3, 48),
-                                 (2, 8192), (5, 8176), (1, 8208), (128, 2560)])
+                                 (2, 8192), (5, 8176), (1, 8208), (128, 2560),
+                                 # 2 to 4 chunks per lane up to K = 32768 (odd chunk
+                                 # counts among them), then the two-pass kernel
+                                 (1, 16400), (2, 24576), (1, 32752), (3, 32768), (1, 32784)])
 def test_quant_int4_matches_oracle(M, K):
     xb, _ = synth.linear_case(M, 1, K, seed=3 * M + K)
     nbytes = w2a8.act4_bytes(M, K)

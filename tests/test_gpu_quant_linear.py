@@ -43,6 +43,25 @@ def test_quant_matches_oracle(M, K):
     np.testing.assert_array_equal(sa, osa)
 
 
+# Rows past 8192 values: 2 to 4 chunks of 8 per lane (K up to 32768), and K
+# just past that limit (the two-pass kernel); the output sits between guard
+# bands that must stay untouched.
+@pytest.mark.parametrize("M,K", [(1, 8200), (1, 16384), (2, 24576), (1, 27648), (3, 32768),
+                                 (1, 32776), (2, 10248)])
+def test_quant_long_rows_with_guards(M, K):
+    xb, _ = synth.linear_case(M, 1, K, seed=M * 11 + K)
+    buf = torch.full((M * K + 128,), -91, dtype=torch.int8, device=dev())
+    sab = torch.full((M + 16,), float("nan"), dtype=torch.float32, device=dev())
+    w2a8.quant_act_int8(_bf16_dev(xb), x_q=buf[64:64 + M * K], s_a=sab[:M])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    oq, osa = oracle.quant_act(xb)
+    np.testing.assert_array_equal(got[64:64 + M * K].reshape(M, K), oq)
+    assert (got[:64] == -91).all() and (got[64 + M * K:] == -91).all()
+    np.testing.assert_array_equal(sab[:M].cpu().numpy(), osa)
+    assert bool(torch.isnan(sab[M:]).all())
+
+
 def test_quant_worked_examples_and_zero_rows():
     rows = [[1.0, -0.5, 0.25, 0.0], [2.0, 1.0, -1.0, 0.5],
             [1.984375, 0.9765625, -0.9765625, 0.5078125], [0.0, 0.0, 0.0, 0.0],

@@ -247,3 +247,35 @@ def test_full_linear_reports_error_vs_unquantized():
     err = np.linalg.norm(y.cpu().numpy() - ref) / np.linalg.norm(ref)
     print(f"relative L2 error of the quantized layer vs fp64: {err:.4f}")
     assert np.isfinite(err) and err < 1.0
+
+
+@pytest.mark.parametrize("entry", ["w2a8_linear_gemv", "w2a4_linear_gemv"])
+def test_fused_layers_graph_replays_match_eager(entry):
+    """The fused layers on a split plan with shared k-ranges, captured in a
+    graph: every replay (with eager work between them) equals the eager call,
+    and the combining words are left zeroed."""
+    N, K = 5120, 27648
+    xb, _ = synth.linear_case(1, 1, K, seed=91)
+    _, wq = synth.gemv_case(N, K, seed=92, sparse=True)
+    wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
+    x = _bf16_dev(xb.reshape(-1))
+    fn = getattr(w2a8, entry)
+    ws = torch.zeros(w2a8.workspace_bytes(1, N, K), dtype=torch.uint8, device=dev())
+    s = torch.cuda.Stream()
+    eager = torch.empty(N, dtype=torch.float32, device=dev())
+    fn(wp, x, N, K, 0.03, eager, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    y = torch.empty(N, dtype=torch.float32, device=dev())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn(wp, x, N, K, 0.03, y, workspace=ws, stream=s)
+    for _ in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
+        other = torch.empty(N, dtype=torch.float32, device=dev())
+        fn(wp, x, N, K, 0.03, other, workspace=ws, stream=s)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+    assert int(ws.count_nonzero()) == 0

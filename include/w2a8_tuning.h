@@ -87,6 +87,20 @@ int w2a8_tune_gemm_ring(int waves_per_wg, int wgs_per_strip, int depth);
 int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg,
                    int *wgs_per_strip, int *depth);
 
+/* The automatic plan of the fused linear layer for one token
+ * (w2a8_linear_gemv with int4 = 0, w2a4_linear_gemv with int4 = 1) for
+ * (N, K) on a device with `cus` compute units under the current knobs.
+ * kernel: 1 the workgroup kernel's fused variant (int8 only), 3 the ring
+ * kernel over shared k-ranges (*waves_per_wg strips per workgroup, one wave
+ * each, quantizing one k-range of at most *run tiles into LDS), 4 the ring
+ * kernel with per-wave runs (int4 only: *waves_per_wg waves per strip, runs
+ * of at most *run tiles, each quantized into its own LDS region).
+ * *wgs_per_strip: k-ranges per strip (more than 1 only when
+ * w2a8_workspace_bytes(1, N, K) > 0).  *depth: ring depth, or the load batch
+ * of kernel 1.  Returns W2A8_OK, W2A8_ERR_NULL or W2A8_ERR_SHAPE. */
+int w2a8_linear_plan(int64_t N, int64_t K, int cus, int int4, int *kernel, int *waves_per_wg,
+                     int *wgs_per_strip, int *run, int *depth);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,11 +54,13 @@ def test_library_exports_every_declared_symbol():
     expected = {"w2a8_status_str", "w2a8_layout_version", "w2a8_packed_bytes",
                 "w2a8_workspace_bytes", "w2a8_ternarize_absmean", "pack_ternary",
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
-                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_tune_gemm", "w2a8_tune_gemv_force",
+                "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_linear_plan", "w2a8_tune_gemm",
+                "w2a8_tune_gemv_force",
                 "w2a8_tune_gemm_ring",
                 "w2a8_gemv_noalloc",
                 "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped",
-                "w2a4_act_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv"}
+                "w2a4_act_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
+                "w2a4_linear_gemv"}
     assert expected.issubset(set(names)), set(names) ^ expected
     L = ctypes.CDLL(w2a8.LIB_PATH)
     for n in names:
@@ -496,6 +498,49 @@ def test_tuning_knobs_validate():
         with pytest.raises(w2a8.W2A8Error):
             w2a8.tune_gemv_force(*bad)
     w2a8.tune_gemv_force(0)
+
+
+def test_linear_plan_properties():
+    """The fused layers' plans keep every LDS region, run and workgroup within
+    the kernels' bounds, split strips only where the workspace exists, and
+    pick the shared ring kernel exactly where the ring plan has one wave per
+    strip (int8)."""
+    pols = [w2a8.DEFAULT_GEMV_POLICY, (1, 32, 8, 256, 10 ** 6), (64, 1, 8, 256, 1),
+            (4, 4, 4, 3, 1), (16, 32, 2, 1, 1)]
+    try:
+        for pol in pols:
+            w2a8.tune_gemv(*pol)
+            for N in (1, 31, 2560, 2600, 16448, 55296, 400000):
+                for K in (1, 127, 2560, 6912, 27648, 70000, 140000, 1048448):
+                    ws = w2a8.workspace_bytes(1, N, K)
+                    kt, ns = -(-K // 128), -(-N // 32)
+                    for cus in (1, 80, 256, 304):
+                        for int4 in (False, True):
+                            kern, wk, sg, run, d = w2a8.linear_plan(N, K, cus, int4)
+                            assert 1 <= wk <= 16 and 1 <= sg <= kt
+                            assert sg == 1 or ws > 0, (pol, N, K, cus, int4)
+                            ktw = -(-kt // sg)
+                            if kern == 3:                 # shared k-ranges
+                                assert wk <= ns and run == ktw and d in (2, 4, 6, 8, 12)
+                                assert run * (64 if int4 else 128) <= 64 * 1024
+                            elif kern == 4:               # per-wave runs (int4)
+                                assert int4 and run <= 64 and run >= -(-ktw // wk)
+                                assert wk * run * 64 <= 64 * 1024 and d in (2, 4, 6, 8, 12)
+                            else:                         # workgroup kernel (int8)
+                                assert kern == 1 and not int4
+                            if not int4 and K % 16 == 0:
+                                ring_wk = w2a8.gemv_plan(N, K, cus)[1]
+                                assert (kern == 3) == (ring_wk == 1), (pol, N, K, cus)
+    finally:
+        w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
+    # the measured choices on a 256-CU device
+    assert w2a8.linear_plan(5120, 27648, 256)[:4] == (3, 8, 12, 18)
+    assert w2a8.linear_plan(55296, 5120, 256)[:4] == (3, 8, 1, 40)
+    assert w2a8.linear_plan(20480, 3200, 256)[:4] == (3, 4, 1, 25)
+    assert w2a8.linear_plan(13824, 2560, 256)[0] == 1
+    assert w2a8.linear_plan(13824, 2560, 256, int4=True)[:4] == (4, 8, 1, 3)
+    with pytest.raises(w2a8.W2A8Error):
+        w2a8.linear_plan(0, 2560, 256)
 
 
 def test_gemv_plan_properties():

@@ -22,7 +22,7 @@ __all__ = [
     "W2A8Error", "lib", "packed_bytes", "workspace_bytes", "layout_version",
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemv_noalloc", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
-    "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "DEFAULT_GEMV_POLICY",
+    "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "linear_plan", "DEFAULT_GEMV_POLICY",
     "tune_gemm", "tune_gemm_ring",
     "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv", "w2a4_linear_gemv",
     "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
@@ -96,6 +96,8 @@ def lib():
         L.w2a8_tune_gemv.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv.restype = I32
         L.w2a8_gemv_plan.argtypes = [I64, I64, I32, P, P, P, P]
+        L.w2a8_linear_plan.argtypes = [I64, I64, I32, I32, P, P, P, P, P]
+        L.w2a8_linear_plan.restype = I32
         L.w2a8_tune_gemv_force.argtypes = [I32, I32, I32, I32, I32]
         L.w2a8_tune_gemv_force.restype = I32
         L.w2a8_tune_gemm.argtypes = [I32]
@@ -583,6 +585,18 @@ def tune_gemm(kernel: int):
 def tune_gemm_ring(waves_per_wg: int = 0, wgs_per_strip: int = 0, depth: int = 0):
     """Forced plan of the short-batch MFMA ring kernel (all 0: automatic)."""
     _check(lib().w2a8_tune_gemm_ring(waves_per_wg, wgs_per_strip, depth), "w2a8_tune_gemm_ring")
+
+
+def linear_plan(N: int, K: int, cus: int, int4: bool = False):
+    """Automatic launch plan of the fused linear layer (w2a8_linear_gemv, or
+    w2a4_linear_gemv with int4=True): (kernel, waves per workgroup,
+    workgroups per strip, run, depth); kernel 1 is the workgroup kernel's
+    fused variant, 3 the ring kernel over shared k-ranges, 4 the ring kernel
+    with per-wave runs."""
+    v = [ctypes.c_int(0) for _ in range(5)]
+    _check(lib().w2a8_linear_plan(N, K, cus, int(bool(int4)), *[ctypes.byref(x) for x in v]),
+           "w2a8_linear_plan")
+    return tuple(x.value for x in v)
 
 
 def gemv_plan(N: int, K: int, cus: int):

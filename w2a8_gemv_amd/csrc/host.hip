@@ -570,17 +570,12 @@ int w2a8_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
     // 20480 x 3200 6.33 / 6.80 / 7.30.  With several waves per strip the
     // workgroup kernel wins: 13824 x 2560 5.22 against 5.62 (ring, per-wave
     // runs), 2560 x 2560 3.83 against 3.94.
-    hipError_t e;
     int depth = 4;
-    gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
-    if (a.WK == 1) {
-        fused_ring_plan(&a, 0, kLinearSharedMaxRun);   // one wave per strip: shared k-ranges
-        a.unroll = depth;
-        e = launch_linear_ring(a, depth, static_cast<hipStream_t>(stream));
-    } else {
-        gemv_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &a.unroll);
-        e = launch_gemv_fused(a, static_cast<hipStream_t>(stream));
-    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e =
+        linear_layer_plan(pol, a.NS, a.KT, dev.cus, false, &a, &depth) == kLinearShared
+            ? launch_linear_ring(a, depth, hs)
+            : launch_gemv_fused(a, hs);
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 
@@ -889,6 +884,20 @@ int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg
         *kernel = 1;
         gemv_plan(pol, NS, KT, cus, waves_per_wg, wgs_per_strip, &run, depth);
     }
+    return W2A8_OK;
+}
+
+int w2a8_linear_plan(int64_t N, int64_t K, int cus, int int4, int *kernel, int *waves_per_wg,
+                     int *wgs_per_strip, int *run, int *depth) {
+    if (!kernel || !waves_per_wg || !wgs_per_strip || !run || !depth) return W2A8_ERR_NULL;
+    if (!nk_ok(N, K) || cus < 1) return W2A8_ERR_SHAPE;
+    GemvLaunch a;
+    *kernel = linear_layer_plan(gemv_policy(), round_up(N, kTileRows) / kTileRows,
+                                round_up(K, kTileK) / kTileK, cus, int4 != 0, &a, depth);
+    *waves_per_wg = a.WK;
+    *wgs_per_strip = a.SG;
+    *run = a.RUN;
+    if (*kernel == kLinearWorkgroup) *depth = a.unroll;
     return W2A8_OK;
 }
 

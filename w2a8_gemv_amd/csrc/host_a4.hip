@@ -140,9 +140,7 @@ int w2a4_linear_gemv(const void *w_packed, const uint16_t *x_bf16, int64_t N, in
     a.KT = int((K + kTileK - 1) / kTileK);
     a.NS = int(Np / kTileRows);
     int depth = 4;
-    gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
-    const bool shared = fused_ring_plan(&a, kA4FusedMaxRun, kA4SharedMaxRun);
-    a.unroll = depth;
+    const bool shared = linear_layer_plan(pol, a.NS, a.KT, dev.cus, true, &a, &depth) == kLinearShared;
     hipError_t e = launch_gemv_a4_fused(a, depth, shared, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }

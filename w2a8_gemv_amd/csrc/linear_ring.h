@@ -28,6 +28,20 @@ namespace w2a8 {
 // k-range bound: the workspace rule of the unfused GEMV still holds.
 bool fused_ring_plan(GemvLaunch *a, int max_run, int max_shared_run);
 
+// Kernels of the fused linear layers (values of w2a8_linear_plan's `kernel`).
+enum LinearKernel {
+    kLinearWorkgroup = 1,   // int8: the workgroup kernel's fused variant (gemv.hip)
+    kLinearShared = 3,      // ring kernel over shared k-ranges (WK strips per workgroup)
+    kLinearPerWave = 4,     // int4: ring kernel, each wave's run in its own LDS region
+};
+// The fused layer's launch plan for NS strips of KT tiles: fills a's WK, SG,
+// RUN and unroll and returns the kernel.  Int8: the shared ring kernel where
+// the ring plan has one wave per strip, else the workgroup kernel (gemv_plan).
+// Int4: fused_ring_plan with kA4FusedMaxRun / kA4SharedMaxRun.  *depth: the
+// ring depth (ring kernels).
+LinearKernel linear_layer_plan(const GemvPolicy &pol, int64_t NS, int64_t KT, int cus, bool int4,
+                               GemvLaunch *a, int *depth);
+
 // Int8 fused linear GEMV over shared k-ranges (a plan for which
 // fused_ring_plan returned true; a.xb: the bf16 row; a.y_f32 required; a.x,
 // a.sa unused; any K).  LDS: a.RUN * 128 bytes, a.RUN <= kLinearSharedMaxRun;

@@ -30,6 +30,7 @@
 // quantizing its own run as the W2A4 kernel does for plans with several
 // waves per strip, measured slower here than the workgroup kernel's fused
 // variant: 5.62 against 5.22 us at 13824 x 2560.)
+#include "a4.h"
 #include "device.h"
 #include "linear_ring.h"
 
@@ -255,6 +256,26 @@ bool fused_ring_plan(GemvLaunch *a, int max_run, int max_shared_run) {
     a->WK = int(WK);
     a->RUN = int(cdiv(ktw, WK));
     return false;
+}
+
+LinearKernel linear_layer_plan(const GemvPolicy &pol, int64_t NS, int64_t KT, int cus, bool int4,
+                               GemvLaunch *a, int *depth) {
+    a->NS = int(NS);
+    a->KT = int(KT);
+    *depth = 4;
+    gemv_ring_plan(pol, NS, KT, cus, &a->WK, &a->SG, &a->RUN, depth);
+    a->unroll = *depth;
+    if (int4) return fused_ring_plan(a, kA4FusedMaxRun, kA4SharedMaxRun) ? kLinearShared
+                                                                           : kLinearPerWave;
+    // One wave per strip: shared k-ranges (always the shared plan then).
+    // Otherwise the workgroup kernel, which measured faster than the ring
+    // with per-wave runs on those plans.
+    if (a->WK == 1) {
+        fused_ring_plan(a, 0, kLinearSharedMaxRun);
+        return kLinearShared;
+    }
+    gemv_plan(pol, NS, KT, cus, &a->WK, &a->SG, &a->RUN, &a->unroll);
+    return kLinearWorkgroup;
 }
 
 hipError_t launch_linear_ring(const GemvLaunch &la, int depth, hipStream_t stream) {

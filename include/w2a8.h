@@ -157,7 +157,8 @@ int unpack_ternary(const void *packed, int64_t packed_bytes, int64_t N,
 /* Per-token absmax quantization of bf16 activations to int8.
  * [TEST] (introduction): the kernels consume 8-bit activations; the pages
  * give no quantizer formula.  Per row m:
- *   a = max_k |x[m][k]|;  inv = 127 / a  (fp32 division);
+ *   a = max_k |x[m][k]|;  inv = min(127 / a, FLT_MAX)  (fp32 division; the cap
+ *   only acts when a < 127 / FLT_MAX, where the quotient overflows);
  *   x_q[m][k] = clamp(round_half_even(x[m][k] * inv), -127, 127);
  *   s_a[m] = a / 127  (fp32 division).   A zero row gives 0 and s_a = 0.
  * x_bf16: device, [M][K] bf16 bit patterns (uint16), 16-byte aligned.
@@ -287,7 +288,8 @@ int64_t w2a4_act_bytes(int64_t M, int64_t K);
 int pack_act_int4(const int8_t *q, int64_t M, int64_t K, uint8_t *out, int64_t out_bytes);
 
 /* Per-token absmax int4 quantization of bf16 activations (device).  Per row m:
- *   a = max_k |x[m][k]|;  inv = 7 / a  (fp32 division);
+ *   a = max_k |x[m][k]|;  inv = min(7 / a, FLT_MAX)  (fp32 division; the cap
+ *   only acts when a < 7 / FLT_MAX);
  *   q[m][k] = clamp(round_half_even(x[m][k] * inv), -7, 7);
  *   s_a[m] = a / 7  (fp32 division).   A zero row gives 0 and s_a = 0.
  * x_bf16: device, [M][K] bf16 bit patterns, 16-byte aligned.  x_q4: device,

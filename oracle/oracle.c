@@ -26,6 +26,7 @@
  * by the not-gpu tests (closed forms, invariants, brute force, worked
  * examples derived by hand from the definitions).
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -107,11 +108,14 @@ void oracle_ternarize_absmean(const float *W, int64_t N, int64_t K,
  * [TEST] (page intro): the kernels take 8-bit activations; no page gives the
  * quantizer.  Reading: per token (row m)
  *   a     = max_k |x[m][k]|             (bf16 -> fp32 is exact)
- *   inv   = 127 / a                     (fp32 division)
+ *   inv   = 127 / a                     (fp32 division), capped at FLT_MAX
  *   q     = clamp(rne(x * inv), -127, 127)   (fp32 multiply, then round)
  *   sa[m] = a / 127                     (fp32 division, not 1/inv)
- * A row of zeros gives q = 0 and sa = 0.  NaN / Inf inputs are outside the
- * contract.
+ * A row of zeros gives q = 0 and sa = 0.  The cap only matters for rows whose
+ * maximum is below 127 / FLT_MAX (about 3.7e-37, subnormal-scale bf16): there
+ * 127 / a overflows to infinity and 0 * inf would make the row's zeros NaN;
+ * capped, zeros stay 0 and every code stays finite.  NaN / Inf inputs are
+ * outside the contract.
  */
 static float bf16_to_f32(uint16_t b)
 {
@@ -137,6 +141,7 @@ void oracle_quant_act(const uint16_t *xb, int64_t M, int64_t K, int8_t *xq,
             continue;
         }
         volatile float inv = 127.0f / a;
+        if (inv > FLT_MAX) inv = FLT_MAX;
         for (int64_t k = 0; k < K; ++k) {
             volatile float p = bf16_to_f32(row[k]) * inv;
             float r = nearbyintf(p);
@@ -254,7 +259,8 @@ int oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *w)
  * lower-precision activations and gives no formula.
  * Reading: the O3 quantizer with 4-bit signed codes, 7 levels each side:
  *   a = max_k |x[m][k]|
- *   inv = 7 / a                         (fp32 division)
+ *   inv = 7 / a                         (fp32 division), capped at FLT_MAX
+ *                                       as in O3 (a below 7 / FLT_MAX)
  *   q[m][k] = clamp(round_half_even(x[m][k] * inv), -7, 7)
  *   sa[m] = a / 7                       (fp32 division, not 1/inv)
  * A row of zeros gives q = 0 and sa = 0.  The product with ternary weights is
@@ -276,6 +282,7 @@ void oracle_quant_act_a4(const uint16_t *xb, int64_t M, int64_t K, int8_t *xq,
             continue;
         }
         volatile float inv = 7.0f / a;
+        if (inv > FLT_MAX) inv = FLT_MAX;
         for (int64_t k = 0; k < K; ++k) {
             volatile float p = bf16_to_f32(row[k]) * inv;
             float r = nearbyintf(p);

@@ -279,3 +279,56 @@ def test_fused_layers_graph_replays_match_eager(entry):
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
     assert int(ws.count_nonzero()) == 0
+
+
+def _tiny_rows(K, seed):
+    """Rows whose maximum is below 127 / FLT_MAX (subnormal-scale bf16): the
+    quantizers' reciprocal overflows and is capped, zeros must stay zero."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((3, K)) * 2.0 ** -130).astype(np.float32)
+    x[0, :4] = [2.0 ** -126, 0.0, -2.0 ** -127, 2.0 ** -128][:K]
+    x[1, ::7] = 0.0
+    x[2] = 0.0
+    x[2, K // 2] = -2.0 ** -133                  # the least bf16 subnormal, alone
+    return synth.fp32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("K", [4, 100, 2560, 27648])
+def test_quantizers_tiny_rows(K):
+    xb = _tiny_rows(K, seed=K)
+    q, sa = _quant_dev(xb)
+    oq, osa = oracle.quant_act(xb)
+    np.testing.assert_array_equal(q, oq)
+    np.testing.assert_array_equal(sa, osa)
+    assert np.all(q[xb == 0] == 0)
+    xq4, sa4 = w2a8.quant_act_int4(_bf16_dev(xb))
+    torch.cuda.synchronize()
+    q4, osa4 = oracle.quant_act_a4(xb)
+    np.testing.assert_array_equal(xq4.cpu().numpy(), oracle.pack_act4(q4))
+    np.testing.assert_array_equal(sa4.cpu().numpy(), osa4)
+
+
+@pytest.mark.parametrize("N,K", [(300, 100), (2560, 2560), (55296, 5120), (5120, 27648)])
+def test_fused_layers_tiny_rows(N, K):
+    """Both fused layers (workgroup and ring kernels) on rows of subnormal
+    scale, bit-identical to the oracle chain (subnormal scales and outputs
+    included)."""
+    xb = _tiny_rows(K, seed=N + K)
+    _, wq = synth.gemv_case(N, K, seed=N, sparse=True)
+    wp = w2a8.pack_ternary(torch.from_numpy(wq)).to(dev())
+    sw = np.float32(0.75)
+    for m in range(xb.shape[0]):
+        row = xb[m:m + 1]
+        yf = torch.empty(N, dtype=torch.float32, device=dev())
+        yi = torch.empty(N, dtype=torch.int32, device=dev())
+        w2a8.w2a8_linear_gemv(wp, _bf16_dev(row.reshape(-1)), N, K, float(sw), yf, y_i32=yi)
+        ref, acc = _linear_ref(row, wq, sw)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(yi.cpu().numpy(), acc[0])
+        np.testing.assert_array_equal(yf.cpu().numpy(), ref[0])
+        w2a8.w2a4_linear_gemv(wp, _bf16_dev(row.reshape(-1)), N, K, float(sw), yf, y_i32=yi)
+        q4, sa4 = oracle.quant_act_a4(row)
+        acc4 = oracle.gemm_i32(q4, wq)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(yi.cpu().numpy(), acc4[0])
+        np.testing.assert_array_equal(yf.cpu().numpy(), oracle.epilogue(acc4, sa4, sw)[0])

@@ -118,7 +118,8 @@ def test_ternarize_mutants_fail(mut):
 
 
 # --------------------------- O3 mutants ------------------------------------
-def _quant_generic(xb, amax_fn, round_fn, qmax=127, lo=-127, per_row=True, divide=False):
+def _quant_generic(xb, amax_fn, round_fn, qmax=127, lo=-127, per_row=True, divide=False,
+                   cap=True):
     xf = synth.bf16_bits_to_fp32(np.atleast_2d(xb)).astype(np.float32)
     M, K = xf.shape
     q = np.zeros((M, K), np.int8)
@@ -128,11 +129,15 @@ def _quant_generic(xb, amax_fn, round_fn, qmax=127, lo=-127, per_row=True, divid
         a = np.float32(amax_fn(xf[m])) if per_row else a_all
         if a == 0:
             continue
-        inv = np.float32(qmax) / a
+        with np.errstate(over="ignore", invalid="ignore"):
+            inv = np.float32(qmax) / a
+        if cap:
+            inv = min(inv, np.finfo(np.float32).max)
         sa[m] = a / np.float32(qmax)
         # divide: x / sa (the rounded scale) instead of x * inv (its rounded reciprocal)
-        v = (xf[m] / sa[m]) if divide else (xf[m] * inv)
-        q[m] = np.clip(round_fn(v), lo, 127).astype(np.int8)
+        with np.errstate(over="ignore", invalid="ignore"):
+            v = (xf[m] / sa[m]) if divide else (xf[m] * inv)
+            q[m] = np.clip(round_fn(v), lo, 127).astype(np.int8)
     return q, sa
 
 
@@ -161,8 +166,13 @@ def _q_divide_by_scale(xb):
     return _quant_generic(xb, lambda r: np.abs(r).max(), np.rint, divide=True)
 
 
+def _q_no_cap(xb):
+    # 127/a left to overflow: tiny rows quantize to +-127 and their zeros to 0*inf
+    return _quant_generic(xb, lambda r: np.abs(r).max(), np.rint, cap=False)
+
+
 @pytest.mark.parametrize("mut", [_q_trunc, _q_no_abs, _q_per_tensor, _q_scale_128,
-                                 _q_half_away, _q_divide_by_scale])
+                                 _q_half_away, _q_divide_by_scale, _q_no_cap])
 def test_quant_mutants_fail(mut):
     assert _fails(quant_pins, mut)
 
@@ -248,7 +258,7 @@ def test_pack_mutant_collision_fails():
 
 # --------------------------- O5 mutants ------------------------------------
 def _q4_generic(xb, qmax=7, lo=-7, hi=7, round_fn=np.rint, amax_fn=lambda r: np.abs(r).max(),
-                per_row=True):
+                per_row=True, cap=True):
     xf = synth.bf16_bits_to_fp32(np.atleast_2d(xb)).astype(np.float32)
     M, K = xf.shape
     q = np.zeros((M, K), np.int8)
@@ -258,8 +268,11 @@ def _q4_generic(xb, qmax=7, lo=-7, hi=7, round_fn=np.rint, amax_fn=lambda r: np.
         a = np.float32(amax_fn(xf[m])) if per_row else a_all
         if a == 0:
             continue
-        inv = np.float32(qmax) / a
-        q[m] = np.clip(round_fn(xf[m] * inv), lo, hi).astype(np.int8)
+        with np.errstate(over="ignore", invalid="ignore"):
+            inv = np.float32(qmax) / a
+            if cap:
+                inv = min(inv, np.finfo(np.float32).max)
+            q[m] = np.clip(round_fn(xf[m] * inv), lo, hi).astype(np.int8)
         sa[m] = a / np.float32(qmax)
     return q, sa
 
@@ -272,7 +285,9 @@ def _q4_generic(xb, qmax=7, lo=-7, hi=7, round_fn=np.rint, amax_fn=lambda r: np.
     lambda xb: _q4_generic(xb, per_row=False),
     lambda xb: _q4_generic(xb, round_fn=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)),
     lambda xb: oracle.quant_act(xb),
-], ids=["trunc", "scale8", "scale8_clamp7", "no_abs", "per_tensor", "half_away", "int8"])
+    lambda xb: _q4_generic(xb, cap=False),
+], ids=["trunc", "scale8", "scale8_clamp7", "no_abs", "per_tensor", "half_away", "int8",
+        "no_cap"])
 def test_quant_a4_mutants_fail(mut):
     assert _fails(quant_a4_pins, mut)
 

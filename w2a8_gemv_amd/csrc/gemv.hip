@@ -284,7 +284,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch a, const GemvGroups t
         }
         // The quantizer's scale and reciprocal; a zero row quantizes to 0.
         sa = amax / 127.0f;
-        const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+        const float inv = amax == 0.0f ? 0.0f : fminf(127.0f / amax, __FLT_MAX__);
 #pragma unroll
         for (int j = 0; j < kXChunks; ++j) {
             const int c = lane + 64 * j;

@@ -144,7 +144,7 @@ __device__ __forceinline__ void a4_body(const GemvLaunch &a) {
             amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         }
         // The quantizer's reciprocal and scale; a zero row quantizes to 0.
-        const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+        const float inv = amax == 0.0f ? 0.0f : fminf(7.0f / amax, __FLT_MAX__);
         sa = amax / 7.0f;
         v2u *region = reinterpret_cast<v2u *>(MS ? smem : smem + wv * (a.RUN * 64));
         for (int c = qfirst; c < 8 * n; c += qstride) {

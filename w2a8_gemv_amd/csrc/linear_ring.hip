@@ -19,7 +19,8 @@
 //    so those L2 hits do not wait behind the weights in the in-order load
 //    counter;
 //  * after the ring is issued: the rest of the maximum share, DPP within
-//    waves, one barrier across them, inv = 127/amax and sa = amax/127;
+//    waves, one barrier across them, inv = min(127/amax, FLT_MAX) and
+//    sa = amax/127;
 //  * quantization into LDS, 16 values (one 16-byte chunk) per step, values
 //    past K as zeros (so any K works: the pad codes meet zero activations);
 //  * the stream then reads each tile's chunk from LDS.
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(1024) void linear_ring_kernel(GemvLaunch a) {
         amax = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     }
     // The quantizer's reciprocal and scale; a zero row quantizes to 0.
-    const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+    const float inv = amax == 0.0f ? 0.0f : fminf(127.0f / amax, __FLT_MAX__);
     const float sa = amax / 127.0f;
 
     // 3. Quantize the k-range into LDS.

@@ -2,7 +2,7 @@
 //
 // The pages fix 8-bit activations ("如何编译 BitNet W2A8 CUDA 内核并用 test.py
 // 运行 GEMV 加速测试？", introduction) but give no quantizer.  Per row m:
-//   a = max|x|;  inv = 127/a;  q = clamp(round_half_even(x*inv), -127, 127);
+//   a = max|x|;  inv = min(127/a, FLT_MAX);  q = clamp(round_half_even(x*inv), -127, 127);
 //   s_a = a/127;  a zero row gives q = 0, s_a = 0.
 // Every step is a single correctly rounded fp32 operation (the division is
 // IEEE, the product is not contracted, v_rndne_f32 rounds half to even), so
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *xb, int M, i
         if (tid == 0) sa[m] = 0.0f;
         return;
     }
-    const float inv = 127.0f / amax;
+    const float inv = fminf(127.0f / amax, __FLT_MAX__);
     if (vec) {
         const v4u *r8 = reinterpret_cast<const v4u *>(row);
         v2u *o8 = reinterpret_cast<v2u *>(out);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(1024) void quant_rows_kernel(const uint16_t *xb, in
             amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(v[i][j])), fabsf(hi_bf16(v[i][j]))));
     __shared__ __attribute__((aligned(16))) float red[16];
     amax = block_absmax(amax, red);
-    const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;   // a zero row quantizes to 0
+    const float inv = amax == 0.0f ? 0.0f : fminf(127.0f / amax, __FLT_MAX__);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = tid + i * bd;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void quant_a4_kernel(const uint16_t *xb, int M
     v4u *out = reinterpret_cast<v4u *>(xq4 + int64_t(m) * G * 16);
     const bool vec = (K & 7) == 0;
     const float amax = row_absmax(row, K, vec);
-    const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+    const float inv = amax == 0.0f ? 0.0f : fminf(7.0f / amax, __FLT_MAX__);
     for (int g = tid; g < G; g += 256) {
         uint32_t w[4];
 #pragma unroll
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(1024) void quant_a4_rows_kernel(const uint16_t *xb,
         }
     __shared__ __attribute__((aligned(16))) float red[16];
     amax = block_absmax(amax, red);
-    const float inv = amax == 0.0f ? 0.0f : 7.0f / amax;
+    const float inv = amax == 0.0f ? 0.0f : fminf(7.0f / amax, __FLT_MAX__);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = tid + i * bd;

@@ -557,7 +557,7 @@ def test_gemv_plan_properties():
                         assert kern == (2 if K % 16 == 0 else 1)
                         if kern == 2:
                             kt = -(-K // 128)
-                            assert 1 <= sg <= kt and 1 <= wk <= 16 and u in (4, 6, 8)
+                            assert 1 <= sg <= kt and 1 <= wk <= 16 and u in (4, 6, 8, 12)
                             if sg > 1:
                                 assert kt >= pol[4] and wk == 1
                             if -(-N // 32) >= 2 * cus:
@@ -582,7 +582,7 @@ def test_gemv_default_plans_of_the_measured_shapes():
     depth) on a 256-CU device for the shapes the rules were measured on.
 
     Ring kernel (K a multiple of 16): one wave per whole strip from two
-    strips per CU up; single-wave workgroups with the k-range split to about
+    strips per CU up, the ring deeper the fewer strips per CU; single-wave workgroups with the k-range split to about
     3.75 waves per CU for strips of 48 tiles or more; 8-wave workgroups
     otherwise.  Batch kernel (ragged K; the same tile counts as the workload
     shapes, K one less): twice the waves with half-length runs in unsplit
@@ -596,6 +596,12 @@ def test_gemv_default_plans_of_the_measured_shapes():
             (55296, 5120): (1, 1, 4), (6912, 5120): (8, 1, 6), (5120, 3456): (8, 1, 4)}
     for (N, K), plan in ring.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
+    # one wave per strip: ring depth by strips per CU (12 below 2.5, 8 up to 4,
+    # 6 up to 5.5, then 4), from the depth sweep on many-strip shapes
+    for N, d in ((16384, 12), (18432, 12), (20480, 8), (24576, 8), (27648, 8), (32768, 8), (41472, 6),
+                 (55296, 4), (73728, 4)):
+        for K in (2560, 5120):
+            assert tuple(w2a8.gemv_plan(N, K, 256)) == (2, 1, 1, d), (N, K)
     batch = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
              (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),
              (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 10, 4),

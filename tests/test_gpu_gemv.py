@@ -133,6 +133,16 @@ def test_gemv_sweep_shapes_full(idx):
     np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
 
 
+# One wave per strip with every automatic ring depth (12 below 2.5 strips per
+# CU, 8 up to 4, 6 up to 5.5, then 4 on a 256-CU device), ragged N and a K
+# that is not a multiple of the depth's tile groups.
+@pytest.mark.parametrize("N,K", [(16400, 2560), (20000, 1040), (26000, 1552), (41472, 1024),
+                                 (57000, 656)])
+def test_gemv_many_strip_depths_full(N, K):
+    x, w, wp, xd = _case(N, K, seed=N % 1000 + K)
+    np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), oracle.gemm_i32(x, w))
+
+
 def test_gemv_small_config_full():
     x, w, wp, xd = _case(2560, 2560, synth.SEED_SMALL)
     np.testing.assert_array_equal(gemv_dev(wp, xd, 2560, 2560), oracle.gemm_i32(x, w))

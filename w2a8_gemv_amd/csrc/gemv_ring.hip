@@ -165,7 +165,16 @@ __global__ __launch_bounds__(1024) void gemv_ring_grouped_kernel(GemvLaunch a, G
 // its own ring (loads in flight / memory latency), so the plan aims for
 // roughly a thousand or more evenly loaded waves:
 //  * at least two strips per CU: one single-wave workgroup per whole strip
-//    (no combine at all), ring depth 4 for strips of 32 tiles or more, else 8;
+//    (no combine at all), with about 24-32 KiB in flight per CU: ring depth
+//    12 below 2.5 strips per CU, 8 up to 4, 6 up to 5.5, else 4.  Measured
+//    (cold, forced depths 4/6/8/12, us): 16384 x 5120 (2 per CU) 8.96 /
+//    8.05 / 7.49 / 6.94; 20480 x 5120 10.14 / 8.63 / 7.44 / 7.28; 27648 x
+//    5120 (3.4) 10.86 / 8.64 / 8.19 / 8.94; 32768 x 5120 10.75 / 9.25 /
+//    9.00 / 9.31; 41472 x 5120 (5.1) 12.07 / 11.81 / 12.21 / 13.05;
+//    55296 x 5120 (6.75) 13.63 / 14.11 / 13.97 / 14.88; the same order at
+//    K = 2560 to 6912 and up to 9 strips per CU.  At exactly 2.5 (20480 x
+//    3200, a sweep shape) depths 8 and 12 tie graph-timed (5.70 / 5.66) and
+//    12 was slower under the kernel trace (5.92 against 5.67), so it keeps 8;
 //  * long strips (KT >= split_min_tiles): single-wave workgroups with the
 //    k-range split so that the grid has about 3.75 waves per CU, combined
 //    with one atomic per row; depth 8 for runs of 24 tiles or more, else 4;
@@ -180,7 +189,10 @@ void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *w
     int64_t WK = 8, SG = 1, D = KT >= 40 ? 6 : 4;
     if (NS >= 2 * int64_t(cus)) {
         WK = 1;
-        D = KT >= 32 ? 4 : 8;
+        // strips per CU q = NS / cus: depth 12 for q < 2.5, 8 for q <= 4,
+        // 6 for q <= 5.5, else 4
+        D = 2 * NS < 5 * int64_t(cus) ? 12 : NS <= 4 * int64_t(cus) ? 8
+            : 2 * NS <= 11 * int64_t(cus) ? 6 : 4;
     } else if (KT >= p.split_min_tiles && KT >= 2) {
         WK = 1;
         SG = std::max<int64_t>(2, std::min<int64_t>(KT / 4, (int64_t(cus) * 15 / 4 + NS / 2) / NS));

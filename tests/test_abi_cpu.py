@@ -582,9 +582,9 @@ def test_gemv_default_plans_of_the_measured_shapes():
     depth) on a 256-CU device for the shapes the rules were measured on.
 
     Ring kernel (K a multiple of 16): one wave per whole strip from two
-    strips per CU up, the ring deeper the fewer strips per CU; single-wave workgroups with the k-range split to about
-    3.75 waves per CU for strips of 48 tiles or more; 8-wave workgroups
-    otherwise.  Batch kernel (ragged K; the same tile counts as the workload
+    strips per CU up, the ring deeper the fewer strips per CU; single-wave
+    workgroups with the k-range split to at most 4 waves per CU for strips
+    of 48 tiles or more; 8-wave workgroups otherwise.  Batch kernel (ragged K; the same tile counts as the workload
     shapes, K one less): twice the waves with half-length runs in unsplit
     strips while there are no more strips than CUs, 4-wave workgroups above
     that, and a split over workgroups for strips of 48 k-tiles or more, into
@@ -592,7 +592,7 @@ def test_gemv_default_plans_of_the_measured_shapes():
     assert w2a8.DEFAULT_GEMV_POLICY == (4, 6, 8, 256, 48)
     ring = {(2560, 2560): (8, 1, 4), (3840, 2560): (8, 1, 4), (3200, 3200): (8, 1, 4),
             (4800, 3200): (8, 1, 4), (13824, 2560): (8, 1, 4), (20480, 3200): (1, 1, 8),
-            (2560, 6912): (1, 12, 4), (3200, 10240): (1, 10, 4), (5120, 27648): (1, 6, 8),
+            (2560, 6912): (1, 12, 4), (3200, 10240): (1, 10, 8), (5120, 27648): (1, 6, 8),
             (55296, 5120): (1, 1, 4), (6912, 5120): (8, 1, 6), (5120, 3456): (8, 1, 4)}
     for (N, K), plan in ring.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
@@ -602,6 +602,12 @@ def test_gemv_default_plans_of_the_measured_shapes():
                  (55296, 4), (73728, 4)):
         for K in (2560, 5120):
             assert tuple(w2a8.gemv_plan(N, K, 256)) == (2, 1, 1, d), (N, K)
+    # long strips below two strips per CU: floor(4 cus / NS) k-ranges (at most
+    # 4 waves on every CU), depth 8 unless the runs are at most 5 tiles
+    for (N, K), plan in {(12288, 14336): (1, 2, 8), (8192, 6912): (1, 4, 8),
+                         (6144, 10240): (1, 5, 8), (4096, 27648): (1, 8, 8),
+                         (2048, 6912): (1, 13, 4), (2048, 27648): (1, 16, 8)}.items():
+        assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
     batch = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
              (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),
              (20480, 3200): (4, 1, 4), (2560, 6912): (1, 9, 4), (3200, 10240): (1, 10, 4),

@@ -176,8 +176,15 @@ __global__ __launch_bounds__(1024) void gemv_ring_grouped_kernel(GemvLaunch a, G
 //    3200, a sweep shape) depths 8 and 12 tie graph-timed (5.70 / 5.66) and
 //    12 was slower under the kernel trace (5.92 against 5.67), so it keeps 8;
 //  * long strips (KT >= split_min_tiles): single-wave workgroups with the
-//    k-range split so that the grid has about 3.75 waves per CU, combined
-//    with one atomic per row; depth 8 for runs of 24 tiles or more, else 4;
+//    k-range split into SG = floor(4 cus / NS) ranges (at least 2, runs of
+//    at least 4 tiles), so the grid has at most 4 waves on every CU,
+//    combined with one atomic per row; depth 8, or 4 for runs of at most 5
+//    tiles.  Measured (cold, forced plans, us; old rule: about 3.75 waves
+//    per CU rounded, depth 8 only for runs of 24 tiles or more): 12288 x
+//    14336 (384 strips) 11.73 with 3 ranges against 10.21 with 2 (4.5 waves
+//    on half the CUs, 3 on every CU); 6144 x 10240 6.24 at depth 4 against
+//    5.31 at 8; 8192 x 6912 5.97 against 5.21; 2048 x 27648 6.01 against
+//    5.14; 2560 x 6912 (runs of 5) 3.56 at 4 against 3.58 at 8;
 //  * otherwise: 8-wave workgroups over whole strips, depth 4 (6 for strips of
 //    40 tiles or more).
 // Measured on MI355X (cold, per-launch): within 2% of the best of a sweep of
@@ -195,9 +202,9 @@ void gemv_ring_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *w
             : 2 * NS <= 11 * int64_t(cus) ? 6 : 4;
     } else if (KT >= p.split_min_tiles && KT >= 2) {
         WK = 1;
-        SG = std::max<int64_t>(2, std::min<int64_t>(KT / 4, (int64_t(cus) * 15 / 4 + NS / 2) / NS));
+        SG = std::max<int64_t>(2, std::min<int64_t>(KT / 4, 4 * int64_t(cus) / NS));
         SG = std::min(SG, KT);
-        D = ceil_div(KT, SG) >= 24 ? 8 : 4;
+        D = ceil_div(KT, SG) <= 5 ? 4 : 8;
     }
     WK = std::min(WK, ceil_div(KT, SG));
     *wk = int(WK);

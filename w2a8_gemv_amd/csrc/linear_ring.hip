@@ -266,13 +266,23 @@ LinearKernel linear_layer_plan(const GemvPolicy &pol, int64_t NS, int64_t KT, in
     *depth = 4;
     gemv_ring_plan(pol, NS, KT, cus, &a->WK, &a->SG, &a->RUN, depth);
     a->unroll = *depth;
-    if (int4) return fused_ring_plan(a, kA4FusedMaxRun, kA4SharedMaxRun) ? kLinearShared
-                                                                           : kLinearPerWave;
+    // Shared k-ranges of fewer than 12 tiles keep depth 4 whatever the ring
+    // GEMV's plan: depth 8 there measured slower (int8, us: 3200 x 10240,
+    // runs of 8: 5.87 against 5.58; 2560 x 27648, runs of 9: 8.10 against
+    // 7.43; int4 7.48 against 7.23).
+    if (int4) {
+        if (!fused_ring_plan(a, kA4FusedMaxRun, kA4SharedMaxRun)) return kLinearPerWave;
+        if (a->RUN < 12) *depth = 4;
+        a->unroll = *depth;
+        return kLinearShared;
+    }
     // One wave per strip: shared k-ranges (always the shared plan then).
     // Otherwise the workgroup kernel, which measured faster than the ring
     // with per-wave runs on those plans.
     if (a->WK == 1) {
         fused_ring_plan(a, 0, kLinearSharedMaxRun);
+        if (a->RUN < 12) *depth = 4;
+        a->unroll = *depth;
         return kLinearShared;
     }
     gemv_plan(pol, NS, KT, cus, &a->WK, &a->SG, &a->RUN, &a->unroll);

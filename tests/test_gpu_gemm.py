@@ -198,7 +198,10 @@ def test_gemm_ring_kernel(M, N, K):
 AUTO_SHORT = [(4, 32800, 256), (8, 20000, 3200), (8, 6900, 5120), (9, 3100, 10000),
               (12, 2500, 6900), (16, 5000, 16400), (12, 24570, 384), (12, 24500, 384),
               (16, 24600, 640), (16, 24530, 640), (20, 3000, 24576), (32, 8160, 24600),
-              (24, 8200, 24600), (20, 3000, 24448)]
+              (24, 8200, 24600), (20, 3000, 24448),
+              # two waves per strip from three strips per CU, one from six;
+              # depth 4 on strips of 32 tiles or more
+              (8, 27648, 1040), (6, 55296, 528), (8, 8192, 8192), (5, 16400, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", AUTO_SHORT)

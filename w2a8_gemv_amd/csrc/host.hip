@@ -166,13 +166,18 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
 // Short-batch MFMA ring kernel plan (measured on MI355X, cold weights, M = 8
 // unless noted; best of sweeps of WK 1..16, SG 1..8, depth 2..8 per shape,
 // pipelined kernel in brackets where measured):
-//  * at least four strips per CU: one wave per strip, depth 4
+//  * at least six strips per CU: one wave per strip, depth 4
 //    (55296 x 5120: 15.9 us [16.5]);
+//  * three to six strips per CU: two waves per strip, depth 4 (32768 x
+//    4096: 9.49 against 10.96 with one wave; 27648 x 5120: 10.20 against
+//    10.48 with four waves of depth 2);
 //  * K under 40 tiles, or at least 3/4 of a strip per CU: 4 waves per strip,
-//    no split, depth 2 (4 with fewer strips than CUs) (13824 x 2560:
-//    5.06 us [6.16], M = 4 5.04; 20480 x 3200: 6.44, where one wave per
-//    strip took 7.90; 6912 x 5120: 5.14, where 3 workgroups per strip took
-//    6.04; 2560 x 2560: 3.89; 5120 x 3456: 4.39);
+//    no split, depth 2 for strips of fewer than 32 tiles on at least one
+//    strip per CU, else 4 (13824 x 2560: 5.06 us [6.16], M = 4 5.04;
+//    20480 x 3200: 6.44, where one wave per strip took 7.90; 6912 x 5120:
+//    5.14, where 3 workgroups per strip took 6.04; 2560 x 2560: 3.89;
+//    5120 x 3456: 4.39; depth 4 against 2: 8192 x 8192 6.89 against 8.08,
+//    8192 x 14336 9.12 against 13.13, 16384 x 8192 9.91 against 10.37);
 //  * K of 64 to 127 tiles: 4 waves and 4 workgroups per strip, depth 2
 //    (3200 x 10240: 5.77 against 6.29 with 3 workgroups of depth 4);
 //  * otherwise 4 waves and 3 workgroups per strip, depth 4 (2 from 128
@@ -181,10 +186,12 @@ void gemv_plan(const GemvPolicy &p, int64_t NS, int64_t KT, int cus, int *wk, in
 void gemm_ring_plan(int64_t NS, int64_t KT, int64_t M, int cus, int64_t lds, int *wk, int *sg,
                     int *depth) {
     int64_t WK = 4, SG = 1, D = 4;
-    if (NS >= 4 * int64_t(cus)) {
+    if (NS >= 6 * int64_t(cus)) {
         WK = 1;
+    } else if (NS >= 3 * int64_t(cus)) {
+        WK = 2;
     } else if (KT < 40 || 4 * NS >= 3 * int64_t(cus)) {
-        D = NS >= cus ? 2 : 4;
+        D = NS >= cus && KT < 32 ? 2 : 4;
     } else if (KT >= 64 && KT < 128) {
         SG = 4;
         D = 2;

@@ -68,6 +68,13 @@ int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int de
  * Returns W2A8_OK or W2A8_ERR_VALUE. */
 int w2a8_tune_gemm(int kernel);
 
+/* Measurement knob: force configuration `config` (0..9) of the pipelined
+ * MFMA GEMM's table (workgroup rows, waves, strips per wave, ring stages and
+ * wave groups over K) wherever w2a8_gemm takes the pipelined kernel; -1
+ * restores the automatic choice.  Every configuration computes every shape
+ * exactly; only speed differs.  Returns W2A8_OK or W2A8_ERR_VALUE. */
+int w2a8_tune_gemm_pipe(int config);
+
 /* Forced plan of the short-batch MFMA ring kernel, wherever w2a8_gemm takes
  * it: `waves_per_wg` (1..16) waves per workgroup splitting a 32-row strip's
  * k-range, `wgs_per_strip` (1..4096; at most the strip's k-tiles are used)

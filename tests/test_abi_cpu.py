@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol():
                 "unpack_ternary", "quant_act_int8", "w2a8_gemv", "w2a8_gemm",
                 "w2a8_tune_gemv", "w2a8_gemv_plan", "w2a8_linear_plan", "w2a8_tune_gemm",
                 "w2a8_tune_gemv_force",
-                "w2a8_tune_gemm_ring",
+                "w2a8_tune_gemm_ring", "w2a8_tune_gemm_pipe",
                 "w2a8_gemv_noalloc",
                 "w2a8_linear_gemv", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped",
                 "w2a4_act_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv",
@@ -494,6 +494,11 @@ def test_tuning_knobs_validate():
             w2a8.tune_gemm_ring(*bad)
     for ok in [(1, 1, 2), (16, 4096, 8), (0, 0, 0)]:
         w2a8.tune_gemm_ring(*ok)
+    for bad in (-2, 10):
+        with pytest.raises(w2a8.W2A8Error):
+            w2a8.tune_gemm_pipe(bad)
+    for ok in (0, 9, -1):
+        w2a8.tune_gemm_pipe(ok)
     for bad in [(3, 1, 1, 4, 1), (2, 4, 1, 4, 0), (1, 4, 1, 8, 1), (2, 4, 1, 3, 1), (8, 1, 1, 4, 1)]:
         with pytest.raises(w2a8.W2A8Error):
             w2a8.tune_gemv_force(*bad)

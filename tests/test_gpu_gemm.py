@@ -89,6 +89,21 @@ def test_gemm_forced_kernel(kernel, M, N, K):
     np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
 
 
+@pytest.mark.parametrize("cfg", range(10))
+@pytest.mark.parametrize("M,N,K", [(100, 700, 1040), (17, 3000, 5248), (460, 520, 272)])
+def test_gemm_every_pipelined_configuration(cfg, M, N, K):
+    """Each configuration of the pipelined kernel's table forced on ragged M,
+    N and K (the automatic choice picks them by shape)."""
+    w2a8.tune_gemm(1)
+    w2a8.tune_gemm_pipe(cfg)
+    try:
+        x, w = synth.gemm_case(M, N, K, seed=cfg + M + N)
+        y = _gemm_dev(packed_on_device(w), to_dev(x), M, N, K)
+        np.testing.assert_array_equal(y, oracle.gemm_i32(x, w))
+    finally:
+        w2a8.tune_gemm_pipe(-1)
+
+
 @pytest.mark.parametrize("M,N,K", [(150, 700, 1024), (200, 3000, 5120), (10, 300, 2432),
                                    (13, 2600, 1040), (50, 400, 5120), (100, 1500, 2608),
                                    (129, 2600, 5120)],

@@ -23,7 +23,7 @@ __all__ = [
     "ternarize_absmean", "pack_ternary", "unpack_ternary", "quant_act_int8",
     "w2a8_gemv", "w2a8_gemv_noalloc", "w2a8_gemm", "gemv", "gemm", "linear", "Workspace",
     "w2a8_linear_gemv", "tune_gemv", "tune_gemv_force", "gemv_plan", "linear_plan", "DEFAULT_GEMV_POLICY",
-    "tune_gemm", "tune_gemm_ring",
+    "tune_gemm", "tune_gemm_ring", "tune_gemm_pipe",
     "act4_bytes", "pack_act_int4", "quant_act_int4", "w2a4_gemv", "w2a4_linear_gemv",
     "linear_a4", "w2a8_gemv_grouped", "w2a8_linear_gemv_grouped", "linear_grouped",
 ]
@@ -102,6 +102,8 @@ def lib():
         L.w2a8_tune_gemv_force.restype = I32
         L.w2a8_tune_gemm.argtypes = [I32]
         L.w2a8_tune_gemm.restype = I32
+        L.w2a8_tune_gemm_pipe.argtypes = [I32]
+        L.w2a8_tune_gemm_pipe.restype = I32
         L.w2a8_tune_gemm_ring.argtypes = [I32, I32, I32]
         L.w2a8_tune_gemm_ring.restype = I32
         L.w2a8_gemv_plan.restype = I32
@@ -580,6 +582,11 @@ def tune_gemm(kernel: int):
     """Batched-product kernel: 0 automatic, 1 pipelined whenever K allows, 2 general,
     3 few-row whenever M <= 8, 4 short-batch MFMA ring whenever M <= 32 and K allows."""
     _check(lib().w2a8_tune_gemm(kernel), "w2a8_tune_gemm")
+
+
+def tune_gemm_pipe(config: int = -1):
+    """Forced configuration (0..9) of the pipelined MFMA GEMM (-1: automatic)."""
+    _check(lib().w2a8_tune_gemm_pipe(config), "w2a8_tune_gemm_pipe")
 
 
 def tune_gemm_ring(waves_per_wg: int = 0, wgs_per_strip: int = 0, depth: int = 0):

@@ -30,6 +30,7 @@
 //  * Split-K (only when M*N is small): int32 partials are added atomically
 //    into the workspace; the last workgroup of a tile (arrival counter)
 //    takes the totals, resets them and applies the epilogue.
+#include "knobs.h"
 #include "device.h"
 
 namespace w2a8 {
@@ -578,11 +579,19 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         //    went from 22.4 to 12.6 us, 13824 x 2560 at M = 8 from 9.3 to
         //    7.3 us); 16-row tiles for M <= 16, whose activation tile is
         //    half as large (55296 x 5120 at M = 8: 15.2 against 16.9 us);
+        //    For M > 32 that holds up to 2 such workgroups per CU (a sweep of
+        //    every configuration off the workload shapes: 4096 x 4096 at
+        //    M = 512 14.9 against 19.2 us with 64-row tiles, 8192 x 8192 at
+        //    M = 256 26.2 against 33.3, 16384 x 4096 at M = 128 15.4
+        //    against 19.4);
         //  * otherwise 32 or 64 rows per workgroup by M, and a 128 x 256
         //    workgroup tile (8 waves, each decoded weight block used by 8
-        //    activation blocks) for M > 448 over at least 256 strips
-        //    (24.7 against 29.9 us at M = 512, 13824 x 2560; at M = 448 the
-        //    64-row tile is still ahead, 23.5 against 24.5 us);
+        //    activation blocks) for M > 128 over more than 4 such 32-row
+        //    workgroups per CU (24.7 against 29.9 us at M = 512,
+        //    13824 x 2560; 31.4 against 41.9 at M = 256, 28672 x 4096; at
+        //    4 per CU the 64-row tile is still ahead: 8192 x 8192 at
+        //    M = 512 40.7 against 49.9, 16384 x 4096 at M = 256 23.3
+        //    against 29.1);
         //  * K of 20 tiles or more over few strips: workgroups of one strip
         //    with 8 wave groups and 16-row tiles while that grid is at most
         //    one workgroup per CU (2560 x 6912 at M = 8: 6.0 against 8.2 us,
@@ -606,16 +615,18 @@ GemmShape gemm_shape(int64_t M, int64_t N, int64_t K, int cus, bool can_split) {
         const bool narrow16 = narrow && ceil_div(M, 16) * n2 <= cus;
         const bool narrow32 = narrow && ceil_div(M, 32) * n2 <= cus;
         int pipe;
-        if (one16)
+        if (gemm_pipe_force() >= 0)
+            pipe = gemm_pipe_force();
+        else if (one16)
             pipe = 9;
         else if (narrow16)
             pipe = 8;
         else if (narrow32)
             pipe = 7;
-        else if (KT >= 8 && g32 <= int64_t(cus) * 7 / 4)
+        else if (KT >= 8 && (g32 <= int64_t(cus) * 7 / 4 || (M > 32 && g32 <= 2 * int64_t(cus))))
             pipe = ((KT >= 40 && g32 <= cus) ? 4 : 3) + (M <= 16 ? 2 : 0);
         else
-            pipe = M <= 32 ? 0 : (M > 448 && NS >= 256) ? 2 : 1;
+            pipe = M <= 32 ? 0 : (M > 128 && g32 > 4 * int64_t(cus)) ? 2 : 1;
         const PipeCfg &c = kPipeCfg[pipe];
         const int64_t mblk = ceil_div(M, c.BM), nblk = ceil_div(NS, int64_t(c.WN) * c.SPW);
         const int mode = gemm_kernel_mode();

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "knobs.h"
 #include "linear_ring.h"
 #include "w2a8_tuning.h"
 
@@ -76,6 +77,9 @@ bool forced_plan(const GemvPolicy &p, int64_t KT, GemvLaunch *a) {
 }
 }  // namespace
 
+std::atomic<int> g_pipe_force{-1};
+int gemm_pipe_force() { return g_pipe_force.load(std::memory_order_relaxed); }
+void set_gemm_pipe_force(int cfg) { g_pipe_force.store(cfg, std::memory_order_relaxed); }
 int gemm_kernel_mode() { return g_gemm_mode.load(std::memory_order_relaxed); }
 void set_gemm_kernel_mode(int mode) { g_gemm_mode.store(mode, std::memory_order_relaxed); }
 
@@ -924,6 +928,12 @@ int w2a8_tune_gemm_ring(int waves_per_wg, int wgs_per_strip, int depth) {
 int w2a8_tune_gemm(int kernel) {
     if (kernel < 0 || kernel > 4) return W2A8_ERR_VALUE;
     set_gemm_kernel_mode(kernel);
+    return W2A8_OK;
+}
+
+int w2a8_tune_gemm_pipe(int config) {
+    if (config < -1 || config >= kGemmPipeConfigs) return W2A8_ERR_VALUE;
+    set_gemm_pipe_force(config);
     return W2A8_OK;
 }
 

@@ -52,8 +52,9 @@ PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, 5.0 POPS
 ROTATE_BYTES = 700e6          # > 256 MB Infinity Cache + 8 x 4 MB L2, with margin
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_traffic.json")
 COLDNESS_FILE = os.path.join(ROOT, "profiles", "gemv_sweep_coldness.json")
-# Sources that decide what the GEMV kernel reads and writes: the ring kernel
-# and its launch plan (one file), and the shared helpers and launch struct.
+# Sources that decide what the GEMV kernels read and write: the ring and
+# row-slice kernels and their launch plans (one file), and the shared helpers
+# and launch struct.
 GEMV_SRCS = [os.path.join(ROOT, "w2a8_gemv_amd", "csrc", f)
              for f in ("gemv_ring.hip", "common.h", "device.h")]
 
@@ -130,10 +131,29 @@ def parse_args():
 CALIB_BYTES = 256 << 20
 
 
+# The plain GEMV's kernels, by the plan's kernel number (w2a8_gemv_plan).
+GEMV_KERNELS = {2: "gemv_ring_kernel", 3: "gemv_slice_kernel"}
+
+
+def gemv_dispatch_key(w2a8, n, k, cus):
+    """(kernel with its depth, threads in the grid, threads per workgroup) of
+    the plain GEMV's dispatch for (n, k): distinct for every sweep shape's plan
+    (the grid alone is not)."""
+    kern, wk, sg, d = w2a8.gemv_plan(n, k, cus)
+    return (f"{GEMV_KERNELS[kern]}<{d}>", (-(-n // 32)) * sg * 64 * wk, 64 * wk)
+
+
+def _gemv_row_key(r):
+    """The same key for a counter row of a GEMV dispatch, else None."""
+    name = _short_kernel_name(r["Kernel_Name"])
+    if not any(name.startswith(g + "<") for g in GEMV_KERNELS.values()):
+        return None
+    return (name, int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+
+
 def _ring_dispatches(path, counters):
-    """Per (grid threads, workgroup threads) of the ring GEMV dispatches: the
-    mean of each counter; and the largest copy dispatch's values (the
-    256 MiB calibration copy)."""
+    """Per gemv_dispatch_key of the GEMV dispatches: the mean of each counter;
+    and the largest copy dispatch's values (the 256 MiB calibration copy)."""
     import csv
     per, copy = {}, {}
     rows = list(csv.DictReader(open(path)))
@@ -141,8 +161,8 @@ def _ring_dispatches(path, counters):
         name, c, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
         if c not in counters:
             continue
-        if "gemv_ring_kernel" in name:
-            key = (int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+        key = _gemv_row_key(r)
+        if key is not None:
             per.setdefault(key, {}).setdefault(c, []).append(v)
         elif "copyBuffer" in name:
             copy[c] = max(copy.get(c, 0.0), v)
@@ -175,8 +195,7 @@ def write_coldness_summary(cold_csv, warm_csv, cus=256):
         runs[mode] = (per, CALIB_BYTES / copy["TCC_EA0_RDREQ_DRAM_sum"])
         out["bytes_per_request_" + mode] = round(runs[mode][1], 2)
     for n, k in synth.SWEEP_SHAPES:
-        _, wk, sg, _ = w2a8.gemv_plan(n, k, cus)
-        key = ((-(-n // 32)) * sg * 64 * wk, 64 * wk)
+        key = gemv_dispatch_key(w2a8, n, k, cus)
         packed = -(-n // 32) * 32 * (-(-k // 128)) * 128 // 4
         row = {"n": n, "k": k, "packed_bytes": packed}
         for mode, (per, bpr) in runs.items():
@@ -224,10 +243,8 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
         factor = CALIB_BYTES / (max(copies) * 1024.0)
         per = {}
         for r in rows:
-            if "gemv_ring_kernel" in r["Kernel_Name"]:
-                # (threads in the grid, threads per workgroup): distinct for
-                # every sweep shape's plan (grid size alone is not)
-                key = (int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            key = _gemv_row_key(r)
+            if key is not None:
                 per.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         return factor, per
 
@@ -235,8 +252,7 @@ def write_traffic_summary(fetch_csv, write_csv, cus=256):
     wf, write = load(write_csv)
     shapes = []
     for n, k in synth.SWEEP_SHAPES:
-        _, wk, sg, _ = w2a8.gemv_plan(n, k, cus)
-        key = ((-(-n // 32)) * sg * 64 * wk, 64 * wk)
+        key = gemv_dispatch_key(w2a8, n, k, cus)
         f = sum(fetch[key]) / len(fetch[key]) * ff
         w = sum(write[key]) / len(write[key]) * wf
         shapes.append({"n": n, "k": k, "algorithmic_bytes": algo_bytes(n, k),
@@ -1347,7 +1363,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "kernel": "w2a8::gemv_ring_kernel (all launches of the timed region)",
+            "kernel": "w2a8::gemv_ring_kernel and w2a8::gemv_slice_kernel (all launches "
+                      "of the timed region)",
             "avg_launch_us": round(dev_us / len(shapes), 3),
             "step_device_us": round(dev_us, 3),
         },

@@ -42,10 +42,14 @@ int w2a8_tune_gemv(int wg_per_cu, int tiles_per_wave, int unroll, int krange_til
  * weights when `direct_x` is 1 (K a multiple of 16; not with batch 8) instead
  * of staging the wave's run in LDS.  kernel 2: the ring kernel (K a multiple
  * of 16) with `depth` (2, 4, 6, 8 or 12) tiles in flight per wave; it always
- * loads activations next to the weights, so `direct_x` must be 1.
+ * loads activations next to the weights, so `direct_x` must be 1.  kernel 3:
+ * the row-slice kernel (K a multiple of 16): 8 single-wave workgroups per
+ * strip, each owning 4 of the 32 rows of every tile, with `depth` (2, 4, 6
+ * or 8) steps of 8 tiles in flight; it never splits the k-range, so
+ * `waves_per_wg` must be 1, `wgs_per_strip` 8 and `direct_x` 1.
  * w2a8_gemv returns W2A8_ERR_VALUE for a forced batch plan whose runs exceed
- * 32 tiles per wave, or a forced ring plan on K not a multiple of 16.
- * w2a8_workspace_bytes(1, N, K) counts a forced split.  Returns W2A8_OK or
+ * 32 tiles per wave, or a forced ring or row-slice plan on K not a multiple
+ * of 16.  w2a8_workspace_bytes(1, N, K) counts a forced split.  Returns W2A8_OK or
  * W2A8_ERR_VALUE. */
 int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int depth,
                          int direct_x);
@@ -85,12 +89,14 @@ int w2a8_tune_gemm_pipe(int config);
 int w2a8_tune_gemm_ring(int waves_per_wg, int wgs_per_strip, int depth);
 
 /* The automatic plan w2a8_gemv would use for (N, K) on a device with `cus`
- * compute units under the current knobs: the kernel (2: the ring kernel, for
- * K a multiple of 16; 1: the batch kernel, for other K), waves per workgroup,
- * workgroups per 32-row strip (more than 1 only when
- * w2a8_workspace_bytes(1, N, K) > 0) and depth (ring: tiles in flight per
- * wave; batch: load batch).  Returns W2A8_OK, W2A8_ERR_NULL or
- * W2A8_ERR_SHAPE. */
+ * compute units under the current knobs: the kernel (3: the row-slice kernel,
+ * for K a multiple of 16 on matrices of few strips and at most 96 k-tiles;
+ * 2: the ring kernel, for the other K multiples of 16; 1: the batch kernel,
+ * for other K), waves per workgroup, workgroups per 32-row strip (kernel 3:
+ * always 8 row slices, no split; kernels 1 and 2: k-ranges, more than 1 only
+ * when w2a8_workspace_bytes(1, N, K) > 0) and depth (ring: tiles in flight
+ * per wave; row-slice: steps of 8 tiles in flight; batch: load batch).
+ * Returns W2A8_OK, W2A8_ERR_NULL or W2A8_ERR_SHAPE. */
 int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg,
                    int *wgs_per_strip, int *depth);
 

@@ -413,7 +413,9 @@ def test_workspace_rule_matches_the_plans():
             for N in (1, 2560, 55296):
                 for K in (1, 128, 385, 2560, 6016, 6017, 27648, 40000):
                     ws = w2a8.workspace_bytes(1, N, K)
-                    splits = [w2a8.gemv_plan(N, K, cus)[2] > 1 for cus in (1, 80, 256, 304)]
+                    # (kernel 3's 8 workgroups per strip are row slices, not k-ranges)
+                    splits = [p[2] > 1 and p[0] != 3
+                              for p in (w2a8.gemv_plan(N, K, cus) for cus in (1, 80, 256, 304))]
                     if ws == 0:
                         assert not any(splits), (pol, N, K)
                     kt = -(-K // 128)
@@ -499,9 +501,12 @@ def test_tuning_knobs_validate():
             w2a8.tune_gemm_pipe(bad)
     for ok in (0, 9, -1):
         w2a8.tune_gemm_pipe(ok)
-    for bad in [(3, 1, 1, 4, 1), (2, 4, 1, 4, 0), (1, 4, 1, 8, 1), (2, 4, 1, 3, 1), (8, 1, 1, 4, 1)]:
+    for bad in [(3, 1, 1, 4, 1), (2, 4, 1, 4, 0), (1, 4, 1, 8, 1), (2, 4, 1, 3, 1), (8, 1, 1, 4, 1),
+                (3, 1, 8, 12, 1), (3, 2, 8, 4, 1), (3, 1, 8, 4, 0), (4, 1, 8, 4, 1)]:
         with pytest.raises(w2a8.W2A8Error):
             w2a8.tune_gemv_force(*bad)
+    w2a8.tune_gemv_force(3, 1, 8, 6, 1)
+    assert w2a8.workspace_bytes(1, 2560, 2560) == 0      # the row-slice kernel never splits
     w2a8.tune_gemv_force(0)
 
 
@@ -533,9 +538,10 @@ def test_linear_plan_properties():
                                 assert wk * run * 64 <= 64 * 1024 and d in (2, 4, 6, 8, 12)
                             else:                         # workgroup kernel (int8)
                                 assert kern == 1 and not int4
-                            if not int4 and K % 16 == 0:
-                                ring_wk = w2a8.gemv_plan(N, K, cus)[1]
-                                assert (kern == 3) == (ring_wk == 1), (pol, N, K, cus)
+                            gp = w2a8.gemv_plan(N, K, cus)
+                            if not int4 and gp[0] == 2:
+                                # the ring plan's shape, where the plain GEMV takes it
+                                assert (kern == 3) == (gp[1] == 1), (pol, N, K, cus)
     finally:
         w2a8.tune_gemv(*w2a8.DEFAULT_GEMV_POLICY)
     # the measured choices on a 256-CU device
@@ -559,7 +565,13 @@ def test_gemv_plan_properties():
                 for K in (1, 127, 128, 2560, 27648, 100000, 1048448):
                     for cus in (1, 80, 256):
                         kern, wk, sg, u = w2a8.gemv_plan(N, K, cus)
-                        assert kern == (2 if K % 16 == 0 else 1)
+                        assert kern in ((2, 3) if K % 16 == 0 else (1,))
+                        if kern == 3:
+                            # 8 row slices per strip, at most 3.75 waves per CU
+                            kt = -(-K // 128)
+                            assert (wk, sg) == (1, 8) and u in (4, 6)
+                            assert 32 * -(-N // 32) <= 15 * cus and kt <= 96
+                            continue
                         if kern == 2:
                             kt = -(-K // 128)
                             assert 1 <= sg <= kt and 1 <= wk <= 16 and u in (4, 6, 8, 12)
@@ -595,12 +607,21 @@ def test_gemv_default_plans_of_the_measured_shapes():
     that, and a split over workgroups for strips of 48 k-tiles or more, into
     equal k-ranges where one of the two smaller counts gives them."""
     assert w2a8.DEFAULT_GEMV_POLICY == (4, 6, 8, 256, 48)
-    ring = {(2560, 2560): (8, 1, 4), (3840, 2560): (8, 1, 4), (3200, 3200): (8, 1, 4),
-            (4800, 3200): (8, 1, 4), (13824, 2560): (8, 1, 4), (20480, 3200): (1, 1, 8),
-            (2560, 6912): (1, 12, 4), (3200, 10240): (1, 10, 8), (5120, 27648): (1, 6, 8),
-            (55296, 5120): (1, 1, 4), (6912, 5120): (8, 1, 6), (5120, 3456): (8, 1, 4)}
+    ring = {(4800, 3200): (8, 1, 4), (13824, 2560): (8, 1, 4), (20480, 3200): (1, 1, 8),
+            (5120, 27648): (1, 6, 8), (55296, 5120): (1, 1, 4), (6912, 5120): (8, 1, 6),
+            (5120, 3456): (8, 1, 4)}
     for (N, K), plan in ring.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
+    # Row-slice kernel: at most 120 strips (3.75 single-wave workgroups per CU)
+    # with strips of at most 64 tiles, or 96 from 64 strips; depth 4 up to 40
+    # tiles, else 6
+    slices = {(2560, 2560): 4, (3840, 2560): 4, (3200, 3200): 4, (2560, 6912): 6,
+              (3200, 10240): 6, (512, 4096): 4, (2048, 6912): 6, (2048, 10240): 6,
+              (3840, 10240): 6, (32, 16): 4}
+    for (N, K), d in slices.items():
+        assert tuple(w2a8.gemv_plan(N, K, 256)) == (3, 1, 8, d), (N, K)
+    for N, K in ((1536, 10240), (512, 14336), (3872, 2560), (2560, 12416)):
+        assert w2a8.gemv_plan(N, K, 256)[0] == 2, (N, K)
     # one wave per strip: ring depth by strips per CU (12 below 2.5, 8 up to 4,
     # 6 up to 5.5, then 4), from the depth sweep on many-strip shapes
     for N, d in ((16384, 12), (18432, 12), (20480, 8), (24576, 8), (27648, 8), (32768, 8), (41472, 6),
@@ -611,7 +632,7 @@ def test_gemv_default_plans_of_the_measured_shapes():
     # 4 waves on every CU), depth 8 unless the runs are at most 5 tiles
     for (N, K), plan in {(12288, 14336): (1, 2, 8), (8192, 6912): (1, 4, 8),
                          (6144, 10240): (1, 5, 8), (4096, 27648): (1, 8, 8),
-                         (2048, 6912): (1, 13, 4), (2048, 27648): (1, 16, 8)}.items():
+                         (1024, 14336): (1, 28, 4), (2048, 27648): (1, 16, 8)}.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
     batch = {(2560, 2560): (8, 1, 2), (3840, 2560): (8, 1, 2), (3200, 3200): (8, 1, 2),
              (4800, 3200): (8, 1, 2), (1024, 1024): (4, 1, 2), (13824, 2560): (4, 1, 4),

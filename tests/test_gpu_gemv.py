@@ -70,7 +70,7 @@ def test_gemv_forced_splits(policy, N, K):
 FORCED = [(2, 1, 1, 2, 1), (2, 1, 1, 12, 1), (2, 4, 1, 4, 1), (2, 3, 2, 6, 1), (2, 8, 3, 8, 1),
           (2, 16, 1, 12, 1), (2, 2, 5, 8, 1), (2, 4, 1, 8, 1), (2, 3, 4, 12, 1), (2, 6, 2, 6, 1),
           (2, 16, 8, 4, 1), (1, 4, 1, 4, 1), (1, 2, 3, 2, 1), (1, 1, 1, 2, 0), (1, 8, 2, 8, 0),
-          (1, 3, 4, 4, 0)]
+          (1, 3, 4, 4, 0), (3, 1, 8, 2, 1), (3, 1, 8, 4, 1), (3, 1, 8, 6, 1), (3, 1, 8, 8, 1)]
 
 
 @pytest.mark.parametrize("force", FORCED, ids=[".".join(map(str, f)) for f in FORCED])
@@ -82,8 +82,8 @@ def test_gemv_forced_plans(force, N, K):
     sg = min(force[2], kt)
     if force[0] == 1 and -(-(-(-kt // sg)) // min(force[1], -(-kt // sg))) > 32:
         pytest.skip("run longer than the batch kernel stages")
-    if force[0] == 2 and K % 16:
-        pytest.skip("the ring kernel needs K a multiple of 16")
+    if force[0] in (2, 3) and K % 16:
+        pytest.skip("the ring and row-slice kernels need K a multiple of 16")
     w2a8.tune_gemv_force(*force)
     try:
         x, w, wp, xd = _case(N, K, seed=11 + N + 3 * K)
@@ -101,7 +101,8 @@ def test_gemv_forced_plans(force, N, K):
 
 @pytest.mark.parametrize("idx", range(len(synth.LARGE_SHAPES)))
 @pytest.mark.parametrize("force", [(2, 6, 1, 12, 1), (2, 2, 2, 8, 1), (2, 1, 1, 12, 1),
-                                   (2, 1, 6, 8, 1), (2, 4, 3, 4, 1), (2, 1, 12, 2, 1)])
+                                   (2, 1, 6, 8, 1), (2, 4, 3, 4, 1), (2, 1, 12, 2, 1),
+                                   (3, 1, 8, 4, 1), (3, 1, 8, 8, 1)])
 def test_gemv_forced_ring_large_shapes(force, idx):
     N, K = synth.LARGE_SHAPES[idx]
     w2a8.tune_gemv_force(*force)
@@ -233,7 +234,7 @@ def test_gemv_f32_only_output():
 
 
 def test_gemv_repeat_deterministic_and_workspace_reset():
-    N, K = 2560, 6912
+    N, K = 4800, 6912
     w2a8.tune_gemv(8, 4, 4, 256, 1)   # strips split over workgroups: exercises the atomics
     assert w2a8.gemv_plan(N, K, torch.cuda.get_device_properties(0).multi_processor_count)[2] > 1
     x, w, wp, xd = _case(N, K, seed=31)

@@ -573,7 +573,8 @@ def tune_gemv(wg_per_cu: int, tiles_per_wave: int, unroll: int, krange_tiles: in
 
 def tune_gemv_force(kernel: int, waves_per_wg: int = 1, wgs_per_strip: int = 1, depth: int = 2,
                     direct_x: int = 0):
-    """Force a GEMV plan (kernel 1: batch kernel, 2: ring kernel; 0: automatic)."""
+    """Force a GEMV plan (kernel 1: batch kernel, 2: ring kernel, 3: row-slice
+    kernel with waves_per_wg 1 and wgs_per_strip 8; 0: automatic)."""
     _check(lib().w2a8_tune_gemv_force(kernel, waves_per_wg, wgs_per_strip, depth, direct_x),
            "w2a8_tune_gemv_force")
 

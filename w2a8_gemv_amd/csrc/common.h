@@ -41,7 +41,9 @@ struct GemvPolicy {
     // Forced plan for measurement sweeps (force_kernel 0: automatic plan).
     // 1: batch kernel with force_wk waves, force_sg workgroups per strip and
     // load batch force_depth, direct activation loads when force_dx; 2: ring
-    // kernel with depth force_depth (activations always loaded directly).
+    // kernel with depth force_depth (activations always loaded directly); 3:
+    // row-slice kernel with depth force_depth (force_wk 1, force_sg 8: its
+    // 8 slice workgroups per strip, never a k-split).
     int force_kernel = 0, force_wk = 0, force_sg = 0, force_depth = 0, force_dx = 0;
 };
 // A consistent copy of the current knobs (taken under a lock: every call
@@ -52,7 +54,8 @@ void set_gemv_policy(const GemvPolicy &p);
 // workgroups (and so needs the workspace).  Depends on K alone, not on the
 // device.
 inline bool gemv_may_split(int64_t KT, const GemvPolicy &p) {
-    return KT >= p.split_min_tiles || KT > p.krange_tiles || (p.force_kernel && p.force_sg > 1);
+    return KT >= p.split_min_tiles || KT > p.krange_tiles ||
+           (p.force_kernel && p.force_kernel != 3 && p.force_sg > 1);
 }
 
 // GEMV launch arguments (passed to the kernel by value).
@@ -169,6 +172,12 @@ hipError_t launch_gemv(const GemvLaunch &a, hipStream_t stream);
 // Ring-pipelined GEMV (gemv_ring.hip): K a multiple of 16, WK <= 16 waves
 // per workgroup, depth 2, 4, 6, 8 or 12 tiles in flight per wave.
 hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, hipStream_t stream);
+// Row-slice GEMV (gemv_ring.hip): K a multiple of 16, 8 single-wave
+// workgroups per strip (each 4 rows of every tile), no split, no workspace;
+// depth 2, 4, 6 or 8 steps of 8 tiles in flight per wave.  The plan returns
+// true (with the depth) for the shapes it serves by default.
+bool gemv_slice_plan(int64_t NS, int64_t KT, int cus, int *depth);
+hipError_t launch_gemv_slice(const GemvLaunch &a, int depth, hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
                         hipStream_t stream);

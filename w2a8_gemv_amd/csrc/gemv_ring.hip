@@ -157,6 +157,79 @@ __global__ __launch_bounds__(1024) void gemv_ring_grouped_kernel(GemvLaunch a, G
     ring_body<D, true>(a, t);
 }
 
+// Row-slice variant for matrices with few strips: kSlices single-wave
+// workgroups share a strip, workgroup (s, sl) owning the 4 rows of row group
+// sl in every tile of strip s.  A step reads the 128-byte slice of 8
+// consecutive tiles (lane l: tile l/8 of the step, k-chunk l%8), so a strip
+// is read by 8 waves spread over the device without splitting its k-range:
+// no combining words and no atomics.  Each lane holds 4 rows x 16 k of one
+// tile; a row's value is the sum over the whole wave.
+constexpr int kSlices = 8;
+
+template <int D>
+__global__ __launch_bounds__(64) void gemv_slice_kernel(GemvLaunch a) {
+    const int lane = threadIdx.x;
+    const int s = int(blockIdx.x) / kSlices, sl = int(blockIdx.x) % kSlices;
+    const int u = lane >> 3, kg = lane & 7;     // tile of the step, k-chunk
+    const int off = sl * 8 + kg;                // 16-byte slot within a tile
+    const int nst = (a.KT + kSlices - 1) / kSlices;
+    const int last = a.KT - 1;
+    const v4u *sbase = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords);
+    const v4u *xp = reinterpret_cast<const v4u *>(a.x);
+    const int xlast = (a.K >> 4) - 1;           // last 16-byte chunk (K % 16 == 0)
+
+    // 1. Fill the ring: steps 0 .. D-1 (tiles clamped to the strip's last).
+    v4u r[D], xq[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const int t = min(j * kSlices + u, last);
+        r[j] = __builtin_nontemporal_load(sbase + t * (kTileBytes / 16) + off);
+        xq[j] = xp[min(t * (kTileK / 16) + kg, xlast)];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 2. Stream: every step but the last is whole and inside K (the strip's
+    //    last tile is in the last step).
+    RingAcc acc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc.a1[q] = acc.a4[q] = acc.a16[q] = 0;
+    int sxl = 0;
+    int i = 0;
+    for (; i + D < nst; i += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            sxl = xsum16(xq[j], sxl);
+            ring_mac(r[j], xq[j], acc);
+            const int t = min((i + D + j) * kSlices + u, last);
+            r[j] = __builtin_nontemporal_load(sbase + t * (kTileBytes / 16) + off);
+            xq[j] = xp[min(t * (kTileK / 16) + kg, xlast)];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        if (i + j < nst) {
+            // lanes past the strip's last tile, and chunks at or past K, count as zero
+            const int t = (i + j) * kSlices + u;
+            const bool in = t <= last && t * kTileK + 16 * kg < a.K;
+            const v4u xv = in ? xq[j] : v4u{0u, 0u, 0u, 0u};
+            sxl = xsum16(xv, sxl);
+            ring_mac(r[j], xv, acc);
+        }
+    }
+
+    // 3. Reduce over the wave: sum_k w*x = sum_k c*x - sum_k x per row.
+    const int sx = wave_sum(sxl);
+    int rr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rr[q] = wave_sum(acc.a1[q] + (acc.a4[q] >> 2) + (acc.a16[q] >> 4));
+    if (lane >= 4) return;
+    const int v = (lane == 0 ? rr[0] : lane == 1 ? rr[1] : lane == 2 ? rr[2] : rr[3]) - sx;
+    const int row = s * kTileRows + sl * 4 + lane;
+    const float sa = a.y_f32 ? a.sa[0] : 0.0f;
+    if (row < a.N) store_proj(Proj{a.wp, a.y_i32, a.y_f32, a.sw, a.N, s}, sa, row, v);
+}
+
 }  // namespace
 
 // Ring-kernel plan (K a multiple of 16): plain reads of this device reach
@@ -248,6 +321,40 @@ hipError_t launch_ring(const GemvLaunch &la, const GemvGroups *t, int depth, hip
 
 hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, hipStream_t stream) {
     return launch_ring<false>(a, nullptr, depth, stream);
+}
+
+// Row-slice plan: the slice kernel serves matrices of at most 3.75
+// single-wave workgroups per CU (8 per strip) whose strips are short enough
+// for 8 waves each: KT <= 64, or KT <= 96 from one quarter strip per CU.
+// Depth 4 for strips of at most 40 tiles (5 steps), else 6.  Measured (cold,
+// graph-timed; 256 CUs; time against the ring plan's): better on every shape
+// of N = 512..3840 x K = 2560..8192 (0.88-0.99, ties at N = 3840 x K <=
+// 4096), e.g. 2560 x 2560 2.74 against 2.84 us, 2560 x 6912 3.44 against
+// 3.56; at K = 10240 from N = 2048 (3200 x 10240 4.01 against 4.25, 3840 x
+// 10240 0.91) but not below (1536 x 10240 1.01, 512 x 10240 1.03); from
+// 4800 x 3200 (150 strips) on slower (3.40 against 3.17), and at 35-71 MB
+// far slower (5120 x 27648 9.4 against 8.3, 55296 x 5120 14.5 against 12.8:
+// a strip's 8 slices are read in 128-byte pieces by 8 waves).
+bool gemv_slice_plan(int64_t NS, int64_t KT, int cus, int *depth) {
+    if (32 * NS > 15 * int64_t(cus)) return false;
+    if (KT > 96 || (KT > 64 && 4 * NS < int64_t(cus))) return false;
+    *depth = KT <= 40 ? 4 : 6;
+    return true;
+}
+
+hipError_t launch_gemv_slice(const GemvLaunch &a, int depth, hipStream_t stream) {
+    if ((a.K & 15) != 0 || int64_t(a.NS) * kSlices > INT32_MAX) return hipErrorInvalidValue;
+    GemvLaunch la = a;
+    void *args[] = {&la};
+    const void *fn;
+    switch (depth) {
+    case 2: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<4>); break;
+    case 6: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<6>); break;
+    case 8: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<8>); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, dim3(unsigned(a.NS) * kSlices), dim3(64), args, 0, stream);
 }
 
 hipError_t launch_gemv_ring_grouped(const GemvLaunch &a, const GemvGroups &t, int depth,

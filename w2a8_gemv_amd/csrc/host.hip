@@ -459,7 +459,20 @@ int gemv_enqueue(const GemvPolicy &pol, const DeviceInfo &dev, const void *w_pac
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(Np / kTileRows);
     hipError_t e;
-    if (forced_plan(pol, a.KT, &a)) {
+    int depth = 4;
+    if (pol.force_kernel == 3) {
+        if ((K & 15) != 0) return W2A8_ERR_VALUE;
+        a.WK = a.SG = 1;
+        a.RUN = a.KT;
+        a.unroll = pol.force_depth;
+        e = launch_gemv_slice(a, pol.force_depth, static_cast<hipStream_t>(stream));
+    } else if (!pol.force_kernel && (K & 15) == 0 && gemv_slice_plan(a.NS, a.KT, dev.cus, &depth)) {
+        // few strips, short k-range: 8 row-slice waves per strip, no split
+        a.WK = a.SG = 1;
+        a.RUN = a.KT;
+        a.unroll = depth;
+        e = launch_gemv_slice(a, depth, static_cast<hipStream_t>(stream));
+    } else if (forced_plan(pol, a.KT, &a)) {
         const hipStream_t st = static_cast<hipStream_t>(stream);
         if (pol.force_kernel == 1) {
             if (a.RUN > 32) return W2A8_ERR_VALUE;
@@ -470,7 +483,6 @@ int gemv_enqueue(const GemvPolicy &pol, const DeviceInfo &dev, const void *w_pac
             e = launch_gemv_ring(a, pol.force_depth, st);
         }
     } else if ((K & 15) == 0) {
-        int depth = 4;
         gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
         a.unroll = depth;
         e = launch_gemv_ring(a, depth, static_cast<hipStream_t>(stream));
@@ -864,12 +876,14 @@ int w2a8_tune_gemv_force(int kernel, int waves_per_wg, int wgs_per_strip, int de
         set_gemv_policy(p);
         return W2A8_OK;
     }
-    if (kernel < 0 || kernel > 2 || waves_per_wg < 1 || waves_per_wg > 16 || wgs_per_strip < 1 ||
+    if (kernel < 0 || kernel > 3 || waves_per_wg < 1 || waves_per_wg > 16 || wgs_per_strip < 1 ||
         wgs_per_strip > 4096 || (direct_x != 0 && direct_x != 1))
         return W2A8_ERR_VALUE;
     const bool ok = kernel == 1 ? (depth == 2 || depth == 4 || depth == 8) && !(direct_x && depth == 8)
-                                : (depth == 2 || depth == 4 || depth == 6 || depth == 8 ||
-                                   depth == 12) && direct_x == 1;
+                    : kernel == 2 ? (depth == 2 || depth == 4 || depth == 6 || depth == 8 ||
+                                     depth == 12) && direct_x == 1
+                                  : (depth == 2 || depth == 4 || depth == 6 || depth == 8) &&
+                                        direct_x == 1 && waves_per_wg == 1 && wgs_per_strip == 8;
     if (!ok) return W2A8_ERR_VALUE;
     p.force_kernel = kernel;
     p.force_wk = waves_per_wg;
@@ -888,7 +902,11 @@ int w2a8_gemv_plan(int64_t N, int64_t K, int cus, int *kernel, int *waves_per_wg
     const int64_t KT = round_up(K, kTileK) / kTileK;
     int run = 0;
     const GemvPolicy pol = gemv_policy();
-    if (K % 16 == 0) {
+    if (K % 16 == 0 && gemv_slice_plan(NS, KT, cus, depth)) {
+        *kernel = 3;
+        *waves_per_wg = 1;
+        *wgs_per_strip = 8;
+    } else if (K % 16 == 0) {
         *kernel = 2;
         gemv_ring_plan(pol, NS, KT, cus, waves_per_wg, wgs_per_strip, &run, depth);
     } else {

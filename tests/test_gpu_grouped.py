@@ -28,6 +28,8 @@ GROUPS = [
     ([31, 33, 1, 64], 129),
     ([100, 7, 300], 1000),
     ([1, 2, 3, 31, 32, 33, 63, 65], 15),
+    ([31, 33, 1, 64, 97], 2000),     # row-slice kernel: ragged rows, a ragged last tile
+    ([200, 33], 8192),               # row-slice kernel at depth 6
     ([5120], 27648),
     ([96, 40, 200], 27648),
     ([250, 1, 77, 129, 64, 32, 500, 3], 4000),

@@ -50,6 +50,10 @@ hipError_t launch_quant_a4(const uint16_t *xb, int M, int K, uint8_t *xq4, float
 // A4I row; any K); same plan (gemv_ring_plan), layout, reduction and
 // workspace.  depth: 2, 4, 6, 8 or 12 tiles in flight per wave.
 hipError_t launch_gemv_a4(const GemvLaunch &a, int depth, hipStream_t stream);
+// Its row-slice form (the int8 row-slice kernel's work split: 8 single-wave
+// workgroups per strip, each 4 rows of every tile; no split, no workspace),
+// for the shapes gemv_slice_plan takes.  depth: 2, 4, 6 or 8 steps of 8 tiles.
+hipError_t launch_gemv_a4_slice(const GemvLaunch &a, int depth, hipStream_t stream);
 // The same kernel fused with the int4 quantizer (a.xb points at the bf16 row,
 // a.x and a.sa unused): every workgroup takes the row maximum and quantizes
 // the part of the row its waves consume into LDS.

@@ -178,6 +178,9 @@ hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, hipStream_t stream);
 // true (with the depth) for the shapes it serves by default.
 bool gemv_slice_plan(int64_t NS, int64_t KT, int cus, int *depth);
 hipError_t launch_gemv_slice(const GemvLaunch &a, int depth, hipStream_t stream);
+// The row-slice kernel over several projections (strips numbered across them).
+hipError_t launch_gemv_slice_grouped(const GemvLaunch &a, const GemvGroups &t, int depth,
+                                     hipStream_t stream);
 
 hipError_t launch_quant(const uint16_t *xb, int M, int K, int8_t *xq, float *sa,
                         hipStream_t stream);

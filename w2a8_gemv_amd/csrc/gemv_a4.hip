@@ -258,6 +258,72 @@ __global__ __launch_bounds__(1024) void gemv_a4_kernel(GemvLaunch a) {
     a4_body<D, false, false>(a);
 }
 
+// Row-slice form for matrices of few strips, as the int8 row-slice kernel
+// (gemv_ring.hip): workgroup (s, sl) owns row group sl (4 rows) of every tile
+// of strip s; a step reads the 128-byte slice of 8 consecutive tiles (lane l:
+// tile l/8 of the step, chunk l%8) and its 8-byte activation chunks.  No
+// split: a row's value is the sum over the whole wave.
+template <int D>
+__global__ __launch_bounds__(64) void gemv_a4_slice_kernel(GemvLaunch a) {
+    const int lane = threadIdx.x;
+    const int s = int(blockIdx.x) / 8, sl = int(blockIdx.x) % 8;
+    const int u = lane >> 3, kg = lane & 7;
+    const int off = sl * 8 + kg;
+    const int nst = (a.KT + 7) / 8;
+    const int last = a.KT - 1;
+    const v4u *sbase = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords);
+    const v2u *xp = reinterpret_cast<const v2u *>(a.x);
+    const int xlast = (a.K + kA4Granule - 1) / kA4Granule * 2 - 1;   // 2 chunks per granule
+
+    v4u r[D];
+    v2u xq[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const int t = min(j * 8 + u, last);
+        r[j] = __builtin_nontemporal_load(sbase + t * (kTileBytes / 16) + off);
+        xq[j] = xp[min(t * 8 + kg, xlast)];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Every step but the last holds tiles before the strip's last one, whose
+    // chunks all lie inside the padded row.
+    int acc[4] = {0, 0, 0, 0};
+    int sxl = 0;
+    int i = 0;
+    for (; i + D < nst; i += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            sxl = dot8(xq[j][0], 0x11111111u, dot8(xq[j][1], 0x11111111u, sxl));
+            mac_a4(r[j], xq[j], acc);
+            const int t = min((i + D + j) * 8 + u, last);
+            r[j] = __builtin_nontemporal_load(sbase + t * (kTileBytes / 16) + off);
+            xq[j] = xp[min(t * 8 + kg, xlast)];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        if (i + j < nst) {
+            // lanes past the strip's last tile, and chunks past the padded row, count as zero
+            const int t = (i + j) * 8 + u;
+            const bool in = t <= last && t * 8 + kg <= xlast;
+            const v2u xv = in ? xq[j] : v2u{0u, 0u};
+            sxl = dot8(xv[0], 0x11111111u, dot8(xv[1], 0x11111111u, sxl));
+            mac_a4(r[j], xv, acc);
+        }
+    }
+    const int sx = wave_sum(sxl);
+    int rr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rr[q] = wave_sum(acc[q]);
+    if (lane >= 4) return;
+    const int v = (lane == 0 ? rr[0] : lane == 1 ? rr[1] : lane == 2 ? rr[2] : rr[3]) - sx;
+    const int row = s * kTileRows + sl * 4 + lane;
+    if (row < a.N) {
+        if (a.y_i32) a.y_i32[row] = v;
+        if (a.y_f32) a.y_f32[row] = (float(v) * a.sa[0]) * a.sw;
+    }
+}
+
 template <int D, bool MS>
 __global__ __launch_bounds__(1024) void gemv_a4_fused_kernel(GemvLaunch a) {
     a4_body<D, true, MS>(a);
@@ -308,6 +374,21 @@ hipError_t launch_gemv_a4(const GemvLaunch &a, int depth, hipStream_t stream) {
 
 hipError_t launch_gemv_a4_fused(const GemvLaunch &a, int depth, bool shared, hipStream_t stream) {
     return launch_a4<true>(a, depth, shared, stream);
+}
+
+hipError_t launch_gemv_a4_slice(const GemvLaunch &la, int depth, hipStream_t stream) {
+    if (int64_t(la.NS) * 8 > INT32_MAX) return hipErrorInvalidValue;
+    GemvLaunch a = la;
+    void *args[] = {&a};
+    const void *fn;
+    switch (depth) {
+    case 2: fn = reinterpret_cast<const void *>(&gemv_a4_slice_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&gemv_a4_slice_kernel<4>); break;
+    case 6: fn = reinterpret_cast<const void *>(&gemv_a4_slice_kernel<6>); break;
+    case 8: fn = reinterpret_cast<const void *>(&gemv_a4_slice_kernel<8>); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, dim3(unsigned(a.NS) * 8), dim3(64), args, 0, stream);
 }
 
 }  // namespace w2a8

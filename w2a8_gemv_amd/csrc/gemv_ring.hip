@@ -163,18 +163,20 @@ __global__ __launch_bounds__(1024) void gemv_ring_grouped_kernel(GemvLaunch a, G
 // consecutive tiles (lane l: tile l/8 of the step, k-chunk l%8), so a strip
 // is read by 8 waves spread over the device without splitting its k-range:
 // no combining words and no atomics.  Each lane holds 4 rows x 16 k of one
-// tile; a row's value is the sum over the whole wave.
+// tile; a row's value is the sum over the whole wave.  GROUPED: strips are
+// numbered across the projections, as in the grouped ring kernel.
 constexpr int kSlices = 8;
 
-template <int D>
-__global__ __launch_bounds__(64) void gemv_slice_kernel(GemvLaunch a) {
+template <int D, bool GROUPED>
+__device__ __forceinline__ void slice_body(const GemvLaunch &a, const GemvGroups &tab) {
     const int lane = threadIdx.x;
     const int s = int(blockIdx.x) / kSlices, sl = int(blockIdx.x) % kSlices;
+    const Proj pj = select_proj<GROUPED>(a, tab, s);
     const int u = lane >> 3, kg = lane & 7;     // tile of the step, k-chunk
     const int off = sl * 8 + kg;                // 16-byte slot within a tile
     const int nst = (a.KT + kSlices - 1) / kSlices;
     const int last = a.KT - 1;
-    const v4u *sbase = reinterpret_cast<const v4u *>(a.wp + int64_t(s) * a.KT * kTileWords);
+    const v4u *sbase = reinterpret_cast<const v4u *>(pj.wp + int64_t(pj.s) * a.KT * kTileWords);
     const v4u *xp = reinterpret_cast<const v4u *>(a.x);
     const int xlast = (a.K >> 4) - 1;           // last 16-byte chunk (K % 16 == 0)
 
@@ -225,9 +227,19 @@ __global__ __launch_bounds__(64) void gemv_slice_kernel(GemvLaunch a) {
     for (int q = 0; q < 4; ++q) rr[q] = wave_sum(acc.a1[q] + (acc.a4[q] >> 2) + (acc.a16[q] >> 4));
     if (lane >= 4) return;
     const int v = (lane == 0 ? rr[0] : lane == 1 ? rr[1] : lane == 2 ? rr[2] : rr[3]) - sx;
-    const int row = s * kTileRows + sl * 4 + lane;
-    const float sa = a.y_f32 ? a.sa[0] : 0.0f;
-    if (row < a.N) store_proj(Proj{a.wp, a.y_i32, a.y_f32, a.sw, a.N, s}, sa, row, v);
+    const int row = pj.s * kTileRows + sl * 4 + lane;
+    const float sa = pj.y_f32 ? a.sa[0] : 0.0f;
+    if (row < pj.N) store_proj(pj, sa, row, v);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void gemv_slice_kernel(GemvLaunch a) {
+    slice_body<D, false>(a, GemvGroups{});
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void gemv_slice_grouped_kernel(GemvLaunch a, GemvGroups t) {
+    slice_body<D, true>(a, t);
 }
 
 }  // namespace
@@ -342,19 +354,38 @@ bool gemv_slice_plan(int64_t NS, int64_t KT, int cus, int *depth) {
     return true;
 }
 
-hipError_t launch_gemv_slice(const GemvLaunch &a, int depth, hipStream_t stream) {
-    if ((a.K & 15) != 0 || int64_t(a.NS) * kSlices > INT32_MAX) return hipErrorInvalidValue;
-    GemvLaunch la = a;
-    void *args[] = {&la};
+namespace {
+
+template <bool GROUPED>
+hipError_t launch_slice(const GemvLaunch &la, const GemvGroups *t, int depth, hipStream_t stream) {
+    if ((la.K & 15) != 0 || int64_t(la.NS) * kSlices > INT32_MAX) return hipErrorInvalidValue;
+    GemvLaunch a = la;
+    GemvGroups tt = t ? *t : GemvGroups{};
+    void *args[] = {&a, &tt};
     const void *fn;
+#define W2A8_SLICE(DD)                                                                     \
+    fn = GROUPED ? reinterpret_cast<const void *>(&gemv_slice_grouped_kernel<DD>)          \
+                 : reinterpret_cast<const void *>(&gemv_slice_kernel<DD>)
     switch (depth) {
-    case 2: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<4>); break;
-    case 6: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<6>); break;
-    case 8: fn = reinterpret_cast<const void *>(&gemv_slice_kernel<8>); break;
+    case 2: W2A8_SLICE(2); break;
+    case 4: W2A8_SLICE(4); break;
+    case 6: W2A8_SLICE(6); break;
+    case 8: W2A8_SLICE(8); break;
     default: return hipErrorInvalidValue;
     }
+#undef W2A8_SLICE
     return hipLaunchKernel(fn, dim3(unsigned(a.NS) * kSlices), dim3(64), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_slice(const GemvLaunch &a, int depth, hipStream_t stream) {
+    return launch_slice<false>(a, nullptr, depth, stream);
+}
+
+hipError_t launch_gemv_slice_grouped(const GemvLaunch &a, const GemvGroups &t, int depth,
+                                     hipStream_t stream) {
+    return launch_slice<true>(a, &t, depth, stream);
 }
 
 hipError_t launch_gemv_ring_grouped(const GemvLaunch &a, const GemvGroups &t, int depth,

@@ -673,11 +673,17 @@ int grouped_launch(const GemvPolicy &pol, const GemvGroups &t, int64_t ns, int64
     a.KT = int(round_up(K, kTileK) / kTileK);
     a.NS = int(ns);
     // One plan for the whole launch, as for a matrix of all the strips: the
-    // ring kernel for int8 rows with K a multiple of 16, else the workgroup
-    // kernel (which also quantizes a bf16 row in every workgroup).
+    // row-slice or ring kernel for int8 rows with K a multiple of 16 (the
+    // plain GEMV's rule), else the workgroup kernel (which also quantizes a
+    // bf16 row in every workgroup).
     hipError_t e;
-    if (!xb && (K & 15) == 0) {
-        int depth = 4;
+    int depth = 4;
+    if (!xb && (K & 15) == 0 && gemv_slice_plan(a.NS, a.KT, dev.cus, &depth)) {
+        a.WK = a.SG = 1;
+        a.RUN = a.KT;
+        a.unroll = depth;
+        e = launch_gemv_slice_grouped(a, t, depth, static_cast<hipStream_t>(stream));
+    } else if (!xb && (K & 15) == 0) {
         gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
         a.unroll = depth;
         e = launch_gemv_ring_grouped(a, t, depth, static_cast<hipStream_t>(stream));

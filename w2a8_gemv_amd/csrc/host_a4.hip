@@ -100,10 +100,20 @@ int w2a4_gemv(const void *w_packed, const uint8_t *x_q4, int64_t N, int64_t K, i
     a.K = int(K);
     a.KT = int((K + kTileK - 1) / kTileK);
     a.NS = int(Np / kTileRows);
+    // The int8 GEMV's kernel choice: the row-slice form on matrices of few,
+    // short strips, else the ring kernel's plan.
     int depth = 4;
-    gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
-    a.unroll = depth;
-    hipError_t e = launch_gemv_a4(a, depth, static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (gemv_slice_plan(a.NS, a.KT, dev.cus, &depth)) {
+        a.WK = a.SG = 1;
+        a.RUN = a.KT;
+        a.unroll = depth;
+        e = launch_gemv_a4_slice(a, depth, static_cast<hipStream_t>(stream));
+    } else {
+        gemv_ring_plan(pol, a.NS, a.KT, dev.cus, &a.WK, &a.SG, &a.RUN, &depth);
+        a.unroll = depth;
+        e = launch_gemv_a4(a, depth, static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? W2A8_OK : W2A8_ERR_LAUNCH;
 }
 

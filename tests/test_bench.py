@@ -115,3 +115,24 @@ def test_gemm_counter_summary(tmp_path):
     assert r["lds_per_mfma"] == 0.5 and r["salu_per_mfma"] == 2.0
     # 16000 busy cycles over 1024 SIMDs x 8 us x 2.4 GHz
     assert abs(r["mfma_busy"] - round(16000 / (1024 * 8 * 2400), 4)) < 1e-12
+
+
+def test_gemv_dispatch_keys_are_distinct_per_sweep_shape():
+    """The counter summaries match GEMV dispatches to sweep shapes by kernel
+    with its depth, grid and workgroup size: every sweep shape's key must be
+    its own, and a counter row of that dispatch must map back to it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    import w2a8_gemv_amd as w2a8
+    keys = [bench.gemv_dispatch_key(w2a8, n, k, 256) for n, k in synth.SWEEP_SHAPES]
+    assert len(set(keys)) == len(keys)
+    for (n, k), key in zip(synth.SWEEP_SHAPES, keys):
+        kern = w2a8.gemv_plan(n, k, 256)[0]
+        assert key[0].startswith(bench.GEMV_KERNELS[kern] + "<")
+        row = {"Kernel_Name": f"void w2a8::(anonymous namespace)::{key[0]}(w2a8::GemvLaunch)",
+               "Grid_Size": str(key[1]), "Workgroup_Size": str(key[2])}
+        assert bench._gemv_row_key(row) == key
+    assert bench._gemv_row_key({"Kernel_Name": "void w2a8::(anonymous namespace)::"
+                                "gemv_ring_grouped_kernel<4>(w2a8::GemvLaunch, w2a8::GemvGroups)",
+                                "Grid_Size": "1", "Workgroup_Size": "64"}) is None

@@ -43,17 +43,23 @@ def _with_workspace(wp, xd, N, K, sa, sw):
     return yi.cpu().numpy(), yf.cpu().numpy()
 
 
-# (N, K, seed): first call, then a smaller one.  K >= 48 tiles: the default
-# plans split strips over workgroups (the path that uses the scratch).
-CASES = [((3000, 10240, 61), (700, 6912, 62)),
-         ((5120, 27648, 63), (96, 8192, 64)),
-         ((40000, 7000, 65), (33, 6144, 66))]
+# (N, K, seed): first call, then a smaller one.  Every shape's default plan
+# splits strips over workgroups (the path that uses the scratch): the ring
+# kernel on strips of more than 96 tiles, the batch kernel for K not a
+# multiple of 16 (40000 x 7000).  The row-slice kernel, which shorter strips
+# on few rows get, never splits and so never touches the scratch.
+CASES = [((3000, 13824, 61), (700, 12800, 62)),
+         ((5120, 27648, 63), (96, 13312, 64)),
+         ((40000, 7000, 65), (33, 12416, 66))]
 
 
-@pytest.mark.parametrize("first,second", CASES, ids=["3000x10240", "5120x27648", "40000x7000"])
+@pytest.mark.parametrize("first,second", CASES, ids=["3000x13824", "5120x27648", "40000x7000"])
 def test_noalloc_matches_gemv_twice(first, second):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     for N, K, seed in (first, second):
         assert w2a8.workspace_bytes(1, N, K) > 0
+        kern, _, sg, _ = w2a8.gemv_plan(N, K, cus)
+        assert kern in (1, 2) and sg > 1, (N, K)      # the plan combines through the scratch
         x, w = synth.gemv_case(N, K, seed)
         wp, xd = packed_on_device(w), to_dev(x)
         sa = to_dev(np.array([0.0137], np.float32))
@@ -65,7 +71,9 @@ def test_noalloc_matches_gemv_twice(first, second):
 
 
 def test_noalloc_unsplit_and_ragged():
-    # no split (no scratch used) and a ragged K (the batch kernel)
+    # 2560 x 2560: the row-slice kernel (no scratch used); 300 x 1000: a short
+    # ragged K (batch kernel, unsplit); 64 x 7001: a long ragged K (batch
+    # kernel, split through the scratch)
     for N, K, seed in ((2560, 2560, 67), (300, 1000, 68), (64, 7001, 69)):
         x, w = synth.gemv_case(N, K, seed)
         wp, xd = packed_on_device(w), to_dev(x)

@@ -567,10 +567,11 @@ def test_gemv_plan_properties():
                         kern, wk, sg, u = w2a8.gemv_plan(N, K, cus)
                         assert kern in ((2, 3) if K % 16 == 0 else (1,))
                         if kern == 3:
-                            # 8 row slices per strip, at most 3.75 waves per CU
-                            kt = -(-K // 128)
+                            # 8 row slices per strip: at most 4 waves per CU, or
+                            # up to 8 on strips of 48-64 tiles
+                            kt, ns = -(-K // 128), -(-N // 32)
                             assert (wk, sg) == (1, 8) and u in (4, 6)
-                            assert 32 * -(-N // 32) <= 15 * cus and kt <= 96
+                            assert kt <= 96 and (2 * ns <= cus or (ns <= cus and 48 <= kt <= 64))
                             continue
                         if kern == 2:
                             kt = -(-K // 128)
@@ -612,15 +613,18 @@ def test_gemv_default_plans_of_the_measured_shapes():
             (5120, 3456): (8, 1, 4)}
     for (N, K), plan in ring.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)
-    # Row-slice kernel: at most 120 strips (3.75 single-wave workgroups per CU)
-    # with strips of at most 64 tiles, or 96 from 64 strips; depth 4 up to 40
-    # tiles, else 6
+    # Row-slice kernel: at most 128 strips (4 single-wave workgroups per CU)
+    # with strips of at most 64 tiles, or 96 from 64 strips, depth 6 above 40
+    # tiles; and up to 256 strips of 48-64 tiles (where the ring plan would
+    # split them), depth 4
     slices = {(2560, 2560): 4, (3840, 2560): 4, (3200, 3200): 4, (2560, 6912): 6,
               (3200, 10240): 6, (512, 4096): 4, (2048, 6912): 6, (2048, 10240): 6,
-              (3840, 10240): 6, (32, 16): 4}
+              (3840, 10240): 6, (32, 16): 4, (4096, 4096): 4, (4096, 11008): 6,
+              (4800, 6912): 4, (8192, 6144): 4, (8192, 8192): 4, (8192, 6912): 4}
     for (N, K), d in slices.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (3, 1, 8, d), (N, K)
-    for N, K in ((1536, 10240), (512, 14336), (3872, 2560), (2560, 12416)):
+    for N, K in ((1536, 10240), (512, 14336), (4128, 2560), (2560, 12416), (10240, 6144),
+                 (5120, 10240), (8224, 6144), (6912, 5120)):
         assert w2a8.gemv_plan(N, K, 256)[0] == 2, (N, K)
     # one wave per strip: ring depth by strips per CU (12 below 2.5, 8 up to 4,
     # 6 up to 5.5, then 4), from the depth sweep on many-strip shapes
@@ -630,7 +634,7 @@ def test_gemv_default_plans_of_the_measured_shapes():
             assert tuple(w2a8.gemv_plan(N, K, 256)) == (2, 1, 1, d), (N, K)
     # long strips below two strips per CU: floor(4 cus / NS) k-ranges (at most
     # 4 waves on every CU), depth 8 unless the runs are at most 5 tiles
-    for (N, K), plan in {(12288, 14336): (1, 2, 8), (8192, 6912): (1, 4, 8),
+    for (N, K), plan in {(12288, 14336): (1, 2, 8), (12288, 6912): (1, 2, 8),
                          (6144, 10240): (1, 5, 8), (4096, 27648): (1, 8, 8),
                          (1024, 14336): (1, 28, 4), (2048, 27648): (1, 16, 8)}.items():
         assert tuple(w2a8.gemv_plan(N, K, 256)) == (2,) + plan, (N, K)

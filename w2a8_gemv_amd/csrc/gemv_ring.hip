@@ -335,22 +335,32 @@ hipError_t launch_gemv_ring(const GemvLaunch &a, int depth, hipStream_t stream) 
     return launch_ring<false>(a, nullptr, depth, stream);
 }
 
-// Row-slice plan: the slice kernel serves matrices of at most 3.75
-// single-wave workgroups per CU (8 per strip) whose strips are short enough
-// for 8 waves each: KT <= 64, or KT <= 96 from one quarter strip per CU.
-// Depth 4 for strips of at most 40 tiles (5 steps), else 6.  Measured (cold,
-// graph-timed; 256 CUs; time against the ring plan's): better on every shape
-// of N = 512..3840 x K = 2560..8192 (0.88-0.99, ties at N = 3840 x K <=
-// 4096), e.g. 2560 x 2560 2.74 against 2.84 us, 2560 x 6912 3.44 against
-// 3.56; at K = 10240 from N = 2048 (3200 x 10240 4.01 against 4.25, 3840 x
-// 10240 0.91) but not below (1536 x 10240 1.01, 512 x 10240 1.03); from
-// 4800 x 3200 (150 strips) on slower (3.40 against 3.17), and at 35-71 MB
-// far slower (5120 x 27648 9.4 against 8.3, 55296 x 5120 14.5 against 12.8:
-// a strip's 8 slices are read in 128-byte pieces by 8 waves).
+// Row-slice plan: the slice kernel serves matrices of small packed size
+// where the ring plan would leave CUs idle or split strips.  Measured (cold,
+// graph-timed, 256 CUs; time against the ring plan's):
+//  * at most 4 single-wave workgroups per CU (NS <= CUs/2), strips of at
+//    most 64 tiles, or 96 from NS >= CUs/4: better on every shape of N =
+//    512..4096 x K = 2560..8192 (0.87-0.99, ties at N = 3840 x K <= 4096),
+//    e.g. 2560 x 2560 2.74 against 2.84 us, 2560 x 6912 3.44 against 3.56,
+//    4096 x 4096 3.07 against 3.22; at K = 10240-12288 from N = 2048 (3200 x
+//    10240 4.01 against 4.25, 3840 x 12288 4.47 against 4.85) but not below
+//    (1536 x 10240 1.01, 512 x 10240 1.03); at K = 14336 it loses below 64
+//    strips (1.06-1.08); from 136 strips at K < 6144 it loses (4352 x 3200
+//    1.02, 4800 x 3200 3.26 against 3.16, 6912 x 5120 1.03);
+//  * up to 8 per CU (NS <= CUs) where the ring plan splits strips of 48-64
+//    tiles over workgroups: 0.89-0.94 (4800 x 6912 4.02 against 4.48, 8192 x
+//    8192 5.26 against 5.64), but from 80 tiles, and from 320 strips, even or
+//    slower (8192 x 10240 1.01, 10240 x 8192 1.03, 12288 x 12288 1.08);
+//  * at 35-71 MB far slower (5120 x 27648 9.4 against 8.3, 55296 x 5120 14.5
+//    against 12.8): a strip's 8 slices are read in 128-byte pieces by 8 waves.
+// Depth 4, except 6 for strips of more than 40 tiles on at most 4 workgroups
+// per CU.
 bool gemv_slice_plan(int64_t NS, int64_t KT, int cus, int *depth) {
-    if (32 * NS > 15 * int64_t(cus)) return false;
-    if (KT > 96 || (KT > 64 && 4 * NS < int64_t(cus))) return false;
-    *depth = KT <= 40 ? 4 : 6;
+    const int64_t c = cus;
+    const bool take = 2 * NS <= c ? KT <= 64 || (KT <= 96 && 4 * NS >= c)
+                                  : NS <= c && KT >= 48 && KT <= 64;
+    if (!take) return false;
+    *depth = KT > 40 && 2 * NS <= c ? 6 : 4;
     return true;
 }
 

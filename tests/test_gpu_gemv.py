@@ -277,3 +277,20 @@ def test_gemv_graph_replays_match_eager():
         np.testing.assert_array_equal(y.cpu().numpy(), ref)
         # eager work between replays
         np.testing.assert_array_equal(gemv_dev(wp, xd, N, K), ref)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (4096, 11008), (11008, 4096), (8192, 8192),
+                                 (4800, 6912)])
+def test_gemv_automatic_plan_on_projection_shapes(N, K):
+    """Common projection shapes on both sides of the row-slice rule (the
+    automatic plan, whichever kernel it picks), every output against the
+    oracle, int32 and fp32."""
+    x, w, wp, xd = _case(N, K, seed=N + 3 * K)
+    ref = oracle.gemm_i32(x, w)
+    ws = torch.zeros(max(1, w2a8.workspace_bytes(1, N, K)), dtype=torch.uint8, device=dev())
+    np.testing.assert_array_equal(gemv_dev(wp, xd, N, K, workspace=ws), ref)
+    sa = np.array([0.0119], np.float32)
+    yi, yf = gemv_dev(wp, xd, N, K, sa=to_dev(sa), sw=0.027, want_f32=True, workspace=ws)
+    np.testing.assert_array_equal(yi, ref)
+    np.testing.assert_array_equal(yf, oracle.epilogue(ref, sa, np.float32(0.027)))
+    assert int(ws.count_nonzero()) == 0

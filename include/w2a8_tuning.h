@@ -90,7 +90,9 @@ int w2a8_tune_gemm_ring(int waves_per_wg, int wgs_per_strip, int depth);
 
 /* The automatic plan w2a8_gemv would use for (N, K) on a device with `cus`
  * compute units under the current knobs: the kernel (3: the row-slice kernel,
- * for K a multiple of 16 on matrices of few strips and at most 96 k-tiles;
+ * for K a multiple of 16 on matrices of small packed size: at most cus/2
+ * strips of at most 64 k-tiles, or 96 from cus/4 strips, or at most cus
+ * strips of 48 to 64 k-tiles;
  * 2: the ring kernel, for the other K multiples of 16; 1: the batch kernel,
  * for other K), waves per workgroup, workgroups per 32-row strip (kernel 3:
  * always 8 row slices, no split; kernels 1 and 2: k-ranges, more than 1 only
